@@ -1,0 +1,30 @@
+"""Reader for the hand-worked fixtures under tests/golden/."""
+
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def read_blocks(name="mxfp4_blocks.txt"):
+    blocks = {}
+    extra = {}
+    cur = None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rest = line.partition(" ")
+            if key == "block":
+                cur = blocks.setdefault(rest, {})
+            elif key == "in":
+                cur["in"] = np.array([float(v) for v in rest.split()], dtype=np.float64)
+            elif key == "scale":
+                cur["scale"] = int(rest, 16)
+            elif key == "codes":
+                cur["codes"] = np.array([int(v, 16) for v in rest.split()], dtype=np.uint8)
+            else:
+                extra[key] = rest
+    return blocks, extra
