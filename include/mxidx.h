@@ -1,0 +1,198 @@
+/*
+ * mxidx.h -- C ABI of the MXFP4 paged indexer-cache library for MI355X (gfx950).
+ *
+ * The library implements the hot path of a DSA lightning indexer whose K cache
+ * is stored in MXFP4:
+ *
+ *   idx_quantize        rows of 128 values -> MXFP4 rows (the FP4 query)
+ *   idx_insert          K rows -> MXFP4 -> paged cache through a slot mapping
+ *   idx_gather          paged cache -> contiguous MXFP4 K (prefill)
+ *   idx_logits_prefill  logit[t,s] = sum_h w[t,h] * max(0, q[t,h] . k[s]), dense K
+ *   idx_logits_paged    the same score, K read through a block table (decode)
+ *   idx_topk            per-row top-k column indices over [ks, ke)
+ *
+ * Sources: P1 = "[Kernel] MXFP4 indexer cache for GLM-5.2 / DSA (glm_moe_dsa)"
+ * (vLLM pull request 48558); P2 = "Enable SM86 MXFP4 sparse-indexer cache"
+ * (Whamp/vllm pull request 14); P3 = API page
+ * "vllm.models.glm5next.nvidia.sparse_indexer".  MXFP4 itself is the OCP
+ * Microscaling Formats (MX) v1.0 format: E2M1 elements, E8M0 block scales.
+ *
+ * MXFP4 row (P1 "Changes", "Benefit": 68 bytes per token per head):
+ *   128 values = 4 blocks of 32.  64 code bytes: element 2j in the low nibble
+ *   of byte j, element 2j+1 in the high nibble; nibble = sign<<3 | code, code
+ *   c in 0..7 has magnitude {0,0.5,1,1.5,2,3,4,6}[c].  4 scale bytes: byte b
+ *   is E_b + 127 for block b, the value of an element being
+ *   (-1)^s * grid[c] * 2^E_b.
+ *   Encode rule: E_b = the smallest integer with amax_b <= 6 * 2^E_b
+ *   (amax_b = 0 gives -127; clamped to [-127, 127]); each element is
+ *   x * 2^-E_b rounded to the nearest grid value, ties to the even code; the
+ *   sign bit is the input's sign bit (so -0.0 encodes as 0x8).
+ *
+ * Paged cache (P1 live-validation comment: block-split value/scale layout):
+ *   num_pages pages of page_size * 68 bytes.  Within a page, the page_size
+ *   code rows (64 B each) come first in token order, then the page_size scale
+ *   rows (4 B each).  Slot s = page * page_size + offset.
+ *
+ * Conventions for every call:
+ *   - All array pointers are DEVICE pointers allocated and owned by the
+ *     caller.  The library never allocates, frees or synchronizes; every call
+ *     only enqueues work on `stream` (0 = the null stream) and returns.
+ *   - Shapes are row-major; "stride" arguments count elements of the array's
+ *     own type.
+ *   - Arguments that the host can check (null pointers with non-zero sizes,
+ *     unsupported sizes, misaligned pointers or strides) return IDX_ERR_ARG
+ *     before any device work.  Zero-sized work returns IDX_OK and enqueues
+ *     nothing.
+ *   - Device-side preconditions (slots, block-table entries and ks/ke within
+ *     range, finite inputs) are not checked on the host.  Kernels skip slots
+ *     and page ids outside the cache instead of touching memory out of range,
+ *     and clamp ke to the row width.
+ *   - The first call on a device checks that it is a gfx950 device
+ *     (fail-closed gate, as P2 "Summary" asks of its kernels); on other
+ *     devices every call returns IDX_ERR_UNSUPPORTED_ARCH.
+ *   - No exception crosses this boundary; launch failures return IDX_ERR_LAUNCH.
+ *   - Calls are thread-safe; calls on one stream execute in order.
+ */
+#ifndef MXIDX_H
+#define MXIDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_ERR_ARG = 1,               /* invalid argument (checked on the host) */
+  IDX_ERR_NO_DEVICE = 2,         /* no HIP device / device index out of range */
+  IDX_ERR_UNSUPPORTED_ARCH = 3,  /* device is not gfx950 */
+  IDX_ERR_LAUNCH = 4             /* kernel launch failed */
+} idx_status;
+
+typedef enum { IDX_BF16 = 0, IDX_F32 = 1 } idx_dtype;
+
+#define IDX_HEAD_DIM 128
+#define IDX_BLOCK 32
+#define IDX_ROW_CODE_BYTES 64
+#define IDX_ROW_SCALE_BYTES 4
+#define IDX_ROW_BYTES 68
+#define IDX_PAGE_SIZE 64
+#define IDX_MAX_HEADS 128
+#define IDX_TOPK_MAX 2048
+
+/* Version of this ABI (major * 100 + minor). */
+int idx_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* idx_strerror(int status);
+
+/* Run the architecture gate for `device` now (it otherwise runs on the first
+ * call that enqueues work on that device).  Returns IDX_OK on gfx950,
+ * IDX_ERR_UNSUPPORTED_ARCH on another GPU, IDX_ERR_NO_DEVICE when `device`
+ * does not exist. */
+int idx_init(int device);
+
+/* idx_quantize -- MXFP4-encode `rows` rows of 128 values into contiguous output
+ * (the FP4 query of P1 "Changes"/"Notes" and P2 "Summary"; P3 "forward_cuda"
+ * takes FP4 q as a (values, scales) pair).
+ *   x:        [rows, row_stride] of bf16 (dtype IDX_BF16) or fp32 (IDX_F32);
+ *             the first 128 elements of each row are encoded.  16-byte aligned;
+ *             row_stride >= 128 and a multiple of 8 (bf16) or 4 (fp32).
+ *   values:   [rows, 64] uint8 out (code bytes).
+ *   scales:   [rows, 4] uint8 out (scale bytes).
+ * Bytes are bit-exact to the encode rule above. */
+int idx_quantize(const void* x, int dtype, int64_t rows, int64_t row_stride,
+                 uint8_t* values, uint8_t* scales, hipStream_t stream);
+
+/* idx_insert -- quantize K rows and scatter them into the paged cache
+ * (the indexer K quant-and-cache kernel of P1 "Changes"; slot -1 = no write,
+ * P3 "_kpool_compress_insert").
+ *   k:            [num_tokens, k_row_stride] bf16 or fp32, as for idx_quantize.
+ *   slot_mapping: [num_tokens] int64; token i goes to slot_mapping[i];
+ *                 negative slots (and slots >= num_pages*page_size) write
+ *                 nothing.  Non-negative slots must be distinct.
+ *   cache:        [num_pages, page_size * 68] uint8, updated in place; only the
+ *                 68 bytes of each written slot change.
+ *   page_size:    must be 64. */
+int idx_insert(const void* k, int dtype, int64_t num_tokens, int64_t k_row_stride,
+               const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
+               int page_size, hipStream_t stream);
+
+/* idx_gather -- paged cache -> contiguous MXFP4 K (the cp_gather that P1's
+ * live-validation comment names as sharing the cache layout).
+ *   block_table:    [batch, bt_row_stride] int32 page ids.
+ *   seq_lens:       [batch] int32; token j < seq_lens[b] of sequence b is read
+ *                   from page block_table[b, j / page_size], offset j % page_size.
+ *   cu_seq_offsets: [batch] int64; that token lands in output row
+ *                   cu_seq_offsets[b] + j (rows >= total_tokens are skipped).
+ *   max_seq_len:    host-side upper bound of seq_lens (sizes the grid; tokens
+ *                   beyond it are not gathered).
+ *   k_values:       [total_tokens, 64] uint8 out;  k_scales: [total_tokens, 4] uint8 out.
+ *   Output rows that no token maps to are left untouched. */
+int idx_gather(const uint8_t* cache, int64_t num_pages, int page_size,
+               const int32_t* block_table, int64_t bt_row_stride,
+               const int32_t* seq_lens, const int64_t* cu_seq_offsets, int batch,
+               int64_t max_seq_len, int64_t total_tokens,
+               uint8_t* k_values, uint8_t* k_scales, hipStream_t stream);
+
+/* idx_logits_prefill -- dense indexer logits (mqa_logits, P3
+ * "SparseAttnIndexerKpool"; the prefill MQA-logits kernel of P2 "Summary"):
+ *   logits[t, s] = sum_h weights[t,h] * max(0, sum_i qhat[t,h,i] * khat[s,i])
+ * for ks[t] <= s < ke[t] (ke clamped to S), qhat/khat the exact MXFP4 values.
+ *   q_values [T, H, 64], q_scales [T, H, 4]  (idx_quantize output);
+ *   k_values [S, 64],    k_scales [S, 4]     (idx_gather output);
+ *   weights  [T, H] fp32;  ks, ke [T] int32 (ks NULL means all zero);
+ *   logits   [T, logits_row_stride] fp32 out, logits_row_stride >= S.
+ *   clean != 0: columns outside [ks, ke) of [0, S) are set to -inf;
+ *   clean == 0: they are left untouched.
+ * H must be a multiple of 16 in [16, 128].  Accumulation is fp32 (exact
+ * products, fp32 sums over the 4 blocks and the heads). */
+int idx_logits_prefill(const uint8_t* q_values, const uint8_t* q_scales,
+                       const uint8_t* k_values, const uint8_t* k_scales,
+                       const float* weights, const int32_t* ks, const int32_t* ke,
+                       int64_t T, int H, int64_t S,
+                       float* logits, int64_t logits_row_stride, int clean,
+                       hipStream_t stream);
+
+/* idx_logits_paged -- decode logits read through the block table
+ * (paged_mqa_logits, P3 "SparseAttnIndexerKpool"; the paged-decode MQA-logits
+ * kernel of P2 "Summary").  Row r = b*next_n + i (the i-th of the last next_n
+ * tokens of sequence b, context length L_b = context_lens[b]) scores columns
+ * s < L_b - next_n + i + 1, reading token s from page
+ * block_table[b, s / page_size].
+ *   q_values [B*next_n, H, 64], q_scales [B*next_n, H, 4], weights [B*next_n, H];
+ *   cache [num_pages, page_size*68]; block_table [B, bt_row_stride] int32;
+ *   context_lens [B] int32, each <= max_context_len;
+ *   logits [B*next_n, logits_row_stride] fp32 out, logits_row_stride >= max_context_len.
+ *   clean != 0: columns of [0, max_context_len) that a row does not score
+ *   are set to -inf; clean == 0: they are left untouched.
+ * page_size must be 64; H a multiple of 16 in [16, 128]; next_n in [1, 16]. */
+int idx_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
+                     const float* weights, const uint8_t* cache, int64_t num_pages,
+                     int page_size, const int32_t* block_table, int64_t bt_row_stride,
+                     const int32_t* context_lens, int B, int next_n, int H,
+                     int64_t max_context_len, float* logits, int64_t logits_row_stride,
+                     int clean, hipStream_t stream);
+
+/* idx_topk -- per-row top-k column indices (top_k_per_row, P3
+ * "SparseAttnIndexerKpool"; exact sets as tested in P2 "Validation").
+ *   logits [rows, logits_row_stride] fp32 (finite in [ks, ke));
+ *   ks [rows] int32 or NULL (= 0); ke [rows] int32;
+ *   out_idx [rows, k] int32 out: the columns of the min(k, ke-ks) largest values
+ *   in [ks, ke), ranked by value then by lower column (-0.0 == +0.0); the
+ *   remaining slots hold -1.  The set is exact; the order of the returned
+ *   columns is deterministic but not part of the contract.
+ *   1 <= k <= 2048; columns are absolute indices into the row. */
+int idx_topk(const float* logits, int64_t rows, int64_t logits_row_stride,
+             const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
+             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXIDX_H */

@@ -1,0 +1,303 @@
+"""MXFP4 paged indexer cache for MI355X (gfx950): Python binding of libmxidx.so.
+
+Thin ctypes layer over the C ABI in ``include/mxidx.h``: it checks tensor
+dtypes/devices/shapes, allocates outputs with torch when the caller passes
+none, and hands raw device pointers and the current HIP stream to the
+library.  Every step of the path runs in the HIP kernels; there is no CPU or
+PyTorch fallback, and a missing library raises ``MxidxError``.
+
+Build the library with ``python -m mxfp4_paged_cache_quant_amd.build``.
+"""
+
+import ctypes
+import os
+
+__all__ = [
+    "MxidxError", "lib", "lib_path", "version", "init",
+    "quantize", "insert", "gather", "logits_prefill", "logits_paged", "topk",
+    "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
+]
+
+HEAD_DIM = 128
+CODE_BYTES = 64
+SCALE_BYTES = 4
+ROW_BYTES = 68
+PAGE_SIZE = 64
+TOPK_MAX = 2048
+MAX_HEADS = 128
+
+IDX_BF16, IDX_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libmxidx.so")
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+# name -> (restype, argtypes); must match include/mxidx.h
+EXPORTS = {
+    "idx_version": (_int, []),
+    "idx_strerror": (ctypes.c_char_p, [_int]),
+    "idx_init": (_int, [_int]),
+    "idx_quantize": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "idx_insert": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int, _c_void_p]),
+    "idx_gather": (_int, [_c_void_p, _i64, _int, _c_void_p, _i64, _c_void_p, _c_void_p, _int, _i64,
+                          _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "idx_logits_prefill": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _i64, _int, _i64, _c_void_p, _i64, _int, _c_void_p]),
+    "idx_logits_paged": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _int, _c_void_p,
+                                _i64, _c_void_p, _int, _int, _int, _i64, _c_void_p, _i64, _int,
+                                _c_void_p]),
+    "idx_topk": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p]),
+}
+
+
+class MxidxError(RuntimeError):
+    def __init__(self, what, status=None):
+        self.status = status
+        super().__init__(what)
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded ctypes library (raises MxidxError when it is not built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(lib_path):
+            raise MxidxError(f"{lib_path} is not built: run python -m mxfp4_paged_cache_quant_amd.build")
+        handle = ctypes.CDLL(lib_path)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def _check(status, call):
+    if status != 0:
+        msg = lib().idx_strerror(status).decode()
+        raise MxidxError(f"{call}: {msg} (status {status})", status)
+
+
+def version():
+    return lib().idx_version()
+
+
+def init(device=0):
+    _check(lib().idx_init(device), "idx_init")
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers (torch supplies device memory and the stream only)
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtype=None):
+    if not t.is_cuda:
+        raise MxidxError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise MxidxError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _rows_view(x, name):
+    """[..., 128] tensor with unit inner stride -> (rows, row_stride, dtype code)."""
+    torch = _torch()
+    _dev(x, name)
+    if x.shape[-1] != HEAD_DIM or x.stride(-1) != 1:
+        raise MxidxError(f"{name} must be [..., 128] with a contiguous last dim")
+    if x.dtype == torch.bfloat16:
+        code = IDX_BF16
+    elif x.dtype == torch.float32:
+        code = IDX_F32
+    else:
+        raise MxidxError(f"{name} must be bfloat16 or float32")
+    rows = x.numel() // HEAD_DIM
+    if x.dim() == 1:
+        stride = HEAD_DIM
+    else:
+        x2 = x.reshape(-1, HEAD_DIM) if x.dim() > 2 else x
+        if x2.data_ptr() != x.data_ptr():
+            raise MxidxError(f"{name} rows must be addressable with one row stride")
+        stride = x2.stride(0) if rows > 1 else HEAD_DIM
+    return rows, stride, code
+
+
+def quantize(x, values=None, scales=None, stream=None):
+    """MXFP4-encode rows of 128 values: returns (values u8 [..., 64], scales u8 [..., 4])."""
+    torch = _torch()
+    rows, stride, code = _rows_view(x, "x")
+    lead = tuple(x.shape[:-1])
+    if values is None:
+        values = torch.empty(lead + (CODE_BYTES,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (SCALE_BYTES,), dtype=torch.uint8, device=x.device)
+    _dev(values, "values", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    if values.numel() != rows * CODE_BYTES or scales.numel() != rows * SCALE_BYTES or \
+            not values.is_contiguous() or not scales.is_contiguous():
+        raise MxidxError("values/scales must be contiguous [rows, 64] / [rows, 4]")
+    _check(lib().idx_quantize(_ptr(x), code, rows, stride, _ptr(values), _ptr(scales), _stream(stream)),
+           "idx_quantize")
+    return values, scales
+
+
+def insert(k, slot_mapping, cache, stream=None):
+    """Quantize K rows [N, 128] and scatter them into ``cache`` [num_pages, 64*68] (in place)."""
+    torch = _torch()
+    rows, stride, code = _rows_view(k, "k")
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(cache, "cache", torch.uint8)
+    if slot_mapping.numel() != rows or not slot_mapping.is_contiguous():
+        raise MxidxError("slot_mapping must be a contiguous int64 [N]")
+    if not cache.is_contiguous() or cache.numel() % (PAGE_SIZE * ROW_BYTES) != 0:
+        raise MxidxError("cache must be a contiguous uint8 [num_pages, 64*68]")
+    num_pages = cache.numel() // (PAGE_SIZE * ROW_BYTES)
+    _check(lib().idx_insert(_ptr(k), code, rows, stride, _ptr(slot_mapping), _ptr(cache), num_pages,
+                            PAGE_SIZE, _stream(stream)), "idx_insert")
+    return cache
+
+
+def gather(cache, block_table, seq_lens, cu_seq_offsets, max_seq_len, total_tokens,
+           k_values=None, k_scales=None, stream=None):
+    """Paged cache -> contiguous (k_values u8 [total, 64], k_scales u8 [total, 4])."""
+    torch = _torch()
+    _dev(cache, "cache", torch.uint8)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(cu_seq_offsets, "cu_seq_offsets", torch.int64)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise MxidxError("block_table must be [batch, pages] with unit inner stride")
+    batch = block_table.shape[0]
+    if seq_lens.numel() != batch or cu_seq_offsets.numel() != batch:
+        raise MxidxError("seq_lens / cu_seq_offsets must have one entry per sequence")
+    if block_table.shape[1] * PAGE_SIZE < max_seq_len or not cache.is_contiguous():
+        raise MxidxError("block_table has fewer pages than max_seq_len needs")
+    if k_values is None:
+        k_values = torch.zeros((total_tokens, CODE_BYTES), dtype=torch.uint8, device=cache.device)
+    if k_scales is None:
+        k_scales = torch.zeros((total_tokens, SCALE_BYTES), dtype=torch.uint8, device=cache.device)
+    for name, t, cols in (("k_values", k_values, CODE_BYTES), ("k_scales", k_scales, SCALE_BYTES)):
+        _dev(t, name, torch.uint8)
+        if not t.is_contiguous() or t.numel() < total_tokens * cols:
+            raise MxidxError(f"{name} must be a contiguous uint8 [total_tokens, {cols}]")
+    num_pages = cache.numel() // (PAGE_SIZE * ROW_BYTES)
+    _check(lib().idx_gather(_ptr(cache), num_pages, PAGE_SIZE, _ptr(block_table), block_table.stride(0),
+                            _ptr(seq_lens), _ptr(cu_seq_offsets), batch, int(max_seq_len),
+                            int(total_tokens), _ptr(k_values), _ptr(k_scales), _stream(stream)),
+           "idx_gather")
+    return k_values, k_scales
+
+
+def logits_prefill(q_values, q_scales, k_values, k_scales, weights, ks, ke, logits=None,
+                   clean=True, stream=None):
+    """Dense logits [T, S] (fp32) for rows t over columns [ks[t], ke[t])."""
+    torch = _torch()
+    T, H = q_values.shape[0], q_values.shape[1]
+    S = k_values.shape[0]
+    for name, t, dt in (("q_values", q_values, torch.uint8), ("q_scales", q_scales, torch.uint8),
+                        ("k_values", k_values, torch.uint8), ("k_scales", k_scales, torch.uint8),
+                        ("weights", weights, torch.float32), ("ke", ke, torch.int32)):
+        _dev(t, name, dt)
+        if not t.is_contiguous():
+            raise MxidxError(f"{name} must be contiguous")
+    if ks is not None:
+        _dev(ks, "ks", torch.int32)
+    if tuple(q_values.shape) != (T, H, CODE_BYTES) or tuple(q_scales.shape) != (T, H, SCALE_BYTES) \
+            or tuple(k_values.shape) != (S, CODE_BYTES) or tuple(k_scales.shape) != (S, SCALE_BYTES) \
+            or tuple(weights.shape) != (T, H):
+        raise MxidxError("shape mismatch among q/k/weights")
+    if ke.numel() != T or (ks is not None and (ks.numel() != T or not ks.is_contiguous())):
+        raise MxidxError("ks / ke must hold one entry per query row")
+    if logits is None:
+        fill = float("-inf") if clean else 0.0
+        logits = torch.full((T, S), fill, dtype=torch.float32, device=q_values.device)
+    _dev(logits, "logits", torch.float32)
+    if logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] < T or logits.shape[1] < S:
+        raise MxidxError("logits must be [>=T, >=S] with contiguous rows")
+    _check(lib().idx_logits_prefill(_ptr(q_values), _ptr(q_scales), _ptr(k_values), _ptr(k_scales),
+                                    _ptr(weights), _ptr(ks), _ptr(ke), T, H, S, _ptr(logits),
+                                    logits.stride(0), 1 if clean else 0, _stream(stream)),
+           "idx_logits_prefill")
+    return logits
+
+
+def logits_paged(q_values, q_scales, weights, cache, block_table, context_lens, next_n,
+                 max_context_len, logits=None, clean=True, stream=None):
+    """Decode logits [B*next_n, max_context_len] (fp32) read through the block table."""
+    torch = _torch()
+    R, H = q_values.shape[0], q_values.shape[1]
+    B = context_lens.numel()
+    for name, t, dt in (("q_values", q_values, torch.uint8), ("q_scales", q_scales, torch.uint8),
+                        ("weights", weights, torch.float32), ("cache", cache, torch.uint8),
+                        ("block_table", block_table, torch.int32),
+                        ("context_lens", context_lens, torch.int32)):
+        _dev(t, name, dt)
+    if R != B * next_n:
+        raise MxidxError("q rows must be batch * next_n")
+    for name, t in (("q_values", q_values), ("q_scales", q_scales), ("weights", weights),
+                    ("cache", cache), ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise MxidxError(f"{name} must be contiguous")
+    if tuple(q_values.shape) != (R, H, CODE_BYTES) or tuple(q_scales.shape) != (R, H, SCALE_BYTES) \
+            or tuple(weights.shape) != (R, H):
+        raise MxidxError("shape mismatch among q/weights")
+    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.shape[0] != B:
+        raise MxidxError("block_table must be [batch, pages] with unit inner stride")
+    if block_table.shape[1] * PAGE_SIZE < max_context_len:
+        raise MxidxError("block_table has fewer pages than max_context_len needs")
+    if logits is None:
+        fill = float("-inf") if clean else 0.0
+        logits = torch.full((R, max_context_len), fill, dtype=torch.float32, device=q_values.device)
+    _dev(logits, "logits", torch.float32)
+    if logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] < R or \
+            logits.shape[1] < max_context_len:
+        raise MxidxError("logits must be [>=rows, >=max_context_len] with contiguous rows")
+    num_pages = cache.numel() // (PAGE_SIZE * ROW_BYTES)
+    _check(lib().idx_logits_paged(_ptr(q_values), _ptr(q_scales), _ptr(weights), _ptr(cache), num_pages,
+                                  PAGE_SIZE, _ptr(block_table), block_table.stride(0),
+                                  _ptr(context_lens), B, next_n, H, int(max_context_len),
+                                  _ptr(logits), logits.stride(0), 1 if clean else 0, _stream(stream)),
+           "idx_logits_paged")
+    return logits
+
+
+def topk(logits, ks, ke, k, out=None, stream=None):
+    """Per-row top-k column indices (int32 [rows, k], -1 padded)."""
+    torch = _torch()
+    _dev(logits, "logits", torch.float32)
+    _dev(ke, "ke", torch.int32)
+    if ks is not None:
+        _dev(ks, "ks", torch.int32)
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise MxidxError("logits must be 2-D with contiguous rows")
+    rows = logits.shape[0]
+    if ke.numel() != rows or not ke.is_contiguous() or \
+            (ks is not None and (ks.numel() != rows or not ks.is_contiguous())):
+        raise MxidxError("ks / ke must hold one entry per row")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    _dev(out, "out", torch.int32)
+    if not out.is_contiguous() or tuple(out.shape) != (rows, k):
+        raise MxidxError("out must be a contiguous int32 [rows, k]")
+    _check(lib().idx_topk(_ptr(logits), rows, logits.stride(0), _ptr(ks), _ptr(ke), k, _ptr(out),
+                          _stream(stream)), "idx_topk")
+    return out

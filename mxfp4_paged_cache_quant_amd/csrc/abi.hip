@@ -1,0 +1,179 @@
+// C ABI of the MXFP4 indexer-cache library (declared in include/mxidx.h):
+// host-side argument validation, the fail-closed gfx950 gate, and dispatch to
+// the kernel launchers.  No allocation, no synchronization, no exceptions.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "mxidx.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// 0 = not checked yet, 1 = gfx950, 2 = another architecture
+std::atomic<int> g_gate[kMaxDevices];
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int gate_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return IDX_ERR_NO_DEVICE;
+  const int st = g_gate[dev].load(std::memory_order_acquire);
+  if (st == 1) return IDX_OK;
+  if (st == 2) return IDX_ERR_UNSUPPORTED_ARCH;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return IDX_ERR_NO_DEVICE;
+  const char* arch = prop.gcnArchName;
+  // Test hook: pretend the device reports another architecture.
+  if (const char* forced = std::getenv("MXIDX_FORCE_ARCH")) arch = forced;
+  const bool ok = std::strncmp(arch, "gfx950", 6) == 0 && (arch[6] == '\0' || arch[6] == ':');
+  g_gate[dev].store(ok ? 1 : 2, std::memory_order_release);
+  return ok ? IDX_OK : IDX_ERR_UNSUPPORTED_ARCH;
+}
+
+int gate_current() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return IDX_ERR_NO_DEVICE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return IDX_ERR_NO_DEVICE;
+  return gate_device(dev);
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? IDX_OK : IDX_ERR_LAUNCH; }
+
+bool heads_ok(int H) { return H >= 16 && H <= IDX_MAX_HEADS && H % 16 == 0; }
+
+int check_rows_input(const void* x, int dtype, int64_t rows, int64_t row_stride) {
+  if (rows < 0) return IDX_ERR_ARG;
+  if (dtype != IDX_BF16 && dtype != IDX_F32) return IDX_ERR_ARG;
+  if (rows == 0) return IDX_OK;
+  if (!x || !aligned(x, 16)) return IDX_ERR_ARG;
+  if (row_stride < IDX_HEAD_DIM) return IDX_ERR_ARG;
+  if (row_stride % (dtype == IDX_BF16 ? 8 : 4) != 0) return IDX_ERR_ARG;
+  return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int idx_version(void) { return 100; }
+
+const char* idx_strerror(int status) {
+  switch (status) {
+    case IDX_OK: return "ok";
+    case IDX_ERR_ARG: return "invalid argument";
+    case IDX_ERR_NO_DEVICE: return "no HIP device";
+    case IDX_ERR_UNSUPPORTED_ARCH: return "device is not gfx950 (MI355X)";
+    case IDX_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int idx_init(int device) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || device < 0 || device >= count)
+    return IDX_ERR_NO_DEVICE;
+  return gate_device(device);
+}
+
+int idx_quantize(const void* x, int dtype, int64_t rows, int64_t row_stride, uint8_t* values,
+                 uint8_t* scales, hipStream_t stream) {
+  int st = check_rows_input(x, dtype, rows, row_stride);
+  if (st != IDX_OK) return st;
+  if (rows == 0) return IDX_OK;
+  if (!values || !scales || !aligned(values, 4)) return IDX_ERR_ARG;
+  if ((st = gate_current()) != IDX_OK) return st;
+  return launched(mxidx::launch_quantize(x, dtype == IDX_F32, rows, row_stride, values, scales, stream));
+}
+
+int idx_insert(const void* k, int dtype, int64_t num_tokens, int64_t k_row_stride,
+               const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages, int page_size,
+               hipStream_t stream) {
+  int st = check_rows_input(k, dtype, num_tokens, k_row_stride);
+  if (st != IDX_OK) return st;
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0) return IDX_ERR_ARG;
+  if (num_tokens == 0) return IDX_OK;
+  if (!slot_mapping || !aligned(slot_mapping, 8)) return IDX_ERR_ARG;
+  if (num_pages > 0 && (!cache || !aligned(cache, 4))) return IDX_ERR_ARG;
+  if ((st = gate_current()) != IDX_OK) return st;
+  return launched(mxidx::launch_insert(k, dtype == IDX_F32, num_tokens, k_row_stride, slot_mapping,
+                                       cache, num_pages, stream));
+}
+
+int idx_gather(const uint8_t* cache, int64_t num_pages, int page_size, const int32_t* block_table,
+               int64_t bt_row_stride, const int32_t* seq_lens, const int64_t* cu_seq_offsets,
+               int batch, int64_t max_seq_len, int64_t total_tokens, uint8_t* k_values,
+               uint8_t* k_scales, hipStream_t stream) {
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0 || batch < 0 || batch > 65535 ||
+      max_seq_len < 0 || total_tokens < 0)
+    return IDX_ERR_ARG;
+  if (batch == 0 || max_seq_len == 0 || total_tokens == 0 || num_pages == 0) return IDX_OK;
+  const int64_t pages_per_seq = (max_seq_len + IDX_PAGE_SIZE - 1) / IDX_PAGE_SIZE;
+  if (bt_row_stride < pages_per_seq) return IDX_ERR_ARG;
+  if (!cache || !aligned(cache, 16) || !block_table || !seq_lens || !cu_seq_offsets ||
+      !aligned(cu_seq_offsets, 8) || !k_values || !aligned(k_values, 16) || !k_scales ||
+      !aligned(k_scales, 4))
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_gather(cache, num_pages, block_table, bt_row_stride, seq_lens,
+                                       cu_seq_offsets, batch, max_seq_len, total_tokens, k_values,
+                                       k_scales, stream));
+}
+
+int idx_logits_prefill(const uint8_t* q_values, const uint8_t* q_scales, const uint8_t* k_values,
+                       const uint8_t* k_scales, const float* weights, const int32_t* ks,
+                       const int32_t* ke, int64_t T, int H, int64_t S, float* logits,
+                       int64_t logits_row_stride, int clean, hipStream_t stream) {
+  if (T < 0 || S < 0 || !heads_ok(H)) return IDX_ERR_ARG;
+  if (T == 0 || S == 0) return IDX_OK;
+  if (logits_row_stride < S) return IDX_ERR_ARG;
+  if (!q_values || !aligned(q_values, 16) || !q_scales || !k_values || !aligned(k_values, 16) ||
+      !k_scales || !aligned(k_scales, 4) || !weights || !aligned(weights, 16) || !ke || !logits ||
+      !aligned(logits, 4))
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_logits_prefill(q_values, q_scales, k_values, k_scales, weights, ks,
+                                               ke, T, H, S, logits, logits_row_stride, clean,
+                                               stream));
+}
+
+int idx_logits_paged(const uint8_t* q_values, const uint8_t* q_scales, const float* weights,
+                     const uint8_t* cache, int64_t num_pages, int page_size,
+                     const int32_t* block_table, int64_t bt_row_stride,
+                     const int32_t* context_lens, int B, int next_n, int H,
+                     int64_t max_context_len, float* logits, int64_t logits_row_stride, int clean,
+                     hipStream_t stream) {
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0 || B < 0 || B > 65535 || next_n < 1 ||
+      next_n > 16 || !heads_ok(H) || max_context_len < 0)
+    return IDX_ERR_ARG;
+  if (B == 0 || max_context_len == 0) return IDX_OK;
+  const int64_t pages_per_seq = (max_context_len + IDX_PAGE_SIZE - 1) / IDX_PAGE_SIZE;
+  if (bt_row_stride < pages_per_seq || logits_row_stride < max_context_len) return IDX_ERR_ARG;
+  if (!q_values || !aligned(q_values, 16) || !q_scales || !weights || !aligned(weights, 16) ||
+      !cache || !aligned(cache, 16) || !block_table || !context_lens || !logits ||
+      !aligned(logits, 4))
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_logits_paged(q_values, q_scales, weights, cache, num_pages,
+                                             block_table, bt_row_stride, context_lens, B, next_n,
+                                             H, max_context_len, logits, logits_row_stride, clean,
+                                             stream));
+}
+
+int idx_topk(const float* logits, int64_t rows, int64_t logits_row_stride, const int32_t* ks,
+             const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {
+  if (rows < 0 || k < 1 || k > IDX_TOPK_MAX || logits_row_stride < 0 ||
+      rows > 0x7fffffffLL)
+    return IDX_ERR_ARG;
+  if (rows == 0) return IDX_OK;
+  if (!logits || !aligned(logits, 4) || !ke || !out_idx) return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_topk(logits, rows, logits_row_stride, ks, ke, k, out_idx, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// MXFP4 row encoder: contiguous output (query quantization) and paged scatter
+// (indexer K quant-and-cache).
+//
+// Format: P1 "[Kernel] MXFP4 indexer cache for GLM-5.2 / DSA", sections
+// "Changes" (E2M1 values + UE8M0 block-32 scales, written through an int64
+// slot mapping) and "Benefit" (68 bytes per token); the block-split page
+// layout of its live-validation comment; OCP MX v1.0 for E2M1 / E8M0.
+//
+// Work mapping: 16 lanes per 128-wide row, 8 consecutive elements per lane
+// (one 16-byte load for bf16, two for fp32), so 4 lanes cover one 32-element
+// block and a wave encodes 4 rows per step.  The block amax is an integer max
+// over the magnitude bits (monotone for finite floats) reduced across the 4
+// lanes with two xor-shuffles; the UE8M0 exponent is read off the amax bit
+// fields; the elements are converted by the gfx950 scaled FP4 conversion,
+// which divides by the power-of-two scale and rounds to nearest even, keeping
+// the sign of zero.  Each lane stores 4 code bytes (a row's 64 code bytes are
+// one coalesced 64-byte segment); lanes 0,4,8,12 of a row store the 4 scale bytes.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mxidx {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Smallest E with amax <= 6 * 2^E, clamped to [-127, 127], from the bits of a
+// non-negative finite fp32 amax = 1.f * 2^e:  E = e - 2 when f <= 0.5, else
+// e - 1.  Exponent fields 0 and 1 (amax < 2^-125) always clamp to -127.
+__device__ __forceinline__ int block_exponent(uint32_t a) {
+  const uint32_t ex = a >> 23;
+  if (ex <= 1u) return -127;
+  const int e = (int)ex - 127;
+  return ((a & 0x7fffffu) <= 0x400000u) ? e - 2 : e - 1;
+}
+
+// 2^E as an fp32 value (E in [-127, 126]; 2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2f(int E) {
+  return __uint_as_float(E >= -126 ? (uint32_t)(E + 127) << 23 : 0x00400000u);
+}
+
+struct Bf16In {
+  uint4 v;
+  __device__ __forceinline__ void load(const void* base, int64_t row, int64_t stride, int sub) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + row * stride + 8 * sub;
+    v = *reinterpret_cast<const uint4*>(p);
+  }
+  // integer max over the 8 magnitudes, as fp32 bit patterns
+  __device__ __forceinline__ uint32_t amax_bits() const {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = max(m, w[i] & 0x7fffu);
+      m = max(m, (w[i] >> 16) & 0x7fffu);
+    }
+    return m << 16;
+  }
+  __device__ __forceinline__ uint32_t encode(float scale) const {
+    uint32_t out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, v.x), scale, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, v.y), scale, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, v.z), scale, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, v.w), scale, 3);
+    return out;
+  }
+};
+
+struct F32In {
+  uint4 lo, hi;
+  __device__ __forceinline__ void load(const void* base, int64_t row, int64_t stride, int sub) {
+    const float* p = static_cast<const float*>(base) + row * stride + 8 * sub;
+    lo = *reinterpret_cast<const uint4*>(p);
+    hi = *reinterpret_cast<const uint4*>(p + 4);
+  }
+  __device__ __forceinline__ uint32_t amax_bits() const {
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = max(m, w[i] & 0x7fffffffu);
+    return m;
+  }
+  __device__ __forceinline__ uint32_t encode(float scale) const {
+    uint32_t out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(lo.x), __uint_as_float(lo.y), scale, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(lo.z), __uint_as_float(lo.w), scale, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(hi.x), __uint_as_float(hi.y), scale, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, __uint_as_float(hi.z), __uint_as_float(hi.w), scale, 3);
+    return out;
+  }
+};
+
+constexpr int kRowsPerBlock = 16;   // 256 threads, 16 lanes per row
+
+// kPaged = false: row r -> values[r*64], scales[r*4].
+// kPaged = true:  row r -> slot = slot_mapping[r] (skipped unless 0 <= slot < num_slots),
+//                 codes at page*4352 + off*64, scales at page*4352 + 4096 + off*4.
+template <typename In, bool kPaged>
+__global__ __launch_bounds__(256) void mxfp4_rows_kernel(const void* __restrict__ x, int64_t rows,
+                                                          int64_t stride,
+                                                          const int64_t* __restrict__ slot_mapping,
+                                                          int64_t num_slots,
+                                                          uint8_t* __restrict__ dst_codes,
+                                                          uint8_t* __restrict__ dst_scales) {
+  const int sub = threadIdx.x & 15;
+  for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4); row < rows;
+       row += (int64_t)gridDim.x * kRowsPerBlock) {
+    uint8_t* cdst;
+    uint8_t* sdst;
+    if constexpr (kPaged) {
+      const int64_t slot = slot_mapping[row];
+      if (slot < 0 || slot >= num_slots) continue;   // same decision for all 16 lanes of the row
+      const int64_t page = slot / kPage;
+      const int64_t off = slot % kPage;
+      cdst = dst_codes + page * kPageBytes + off * kCodeBytes;
+      sdst = dst_codes + page * kPageBytes + kPageCodeBytes + off * kScaleBytes;
+    } else {
+      cdst = dst_codes + row * kCodeBytes;
+      sdst = dst_scales + row * kScaleBytes;
+    }
+    In in;
+    in.load(x, row, stride, sub);
+    uint32_t a = in.amax_bits();
+    a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+    a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+    const int E = block_exponent(a);
+    // An all-zero block needs no division (its codes are the sign bits alone);
+    // dividing by 1 keeps the subnormal scale out of the common case.
+    const float scale = (a == 0u) ? 1.0f : pow2f(E);
+    const uint32_t codes = in.encode(scale);
+    *reinterpret_cast<uint32_t*>(cdst + 4 * sub) = codes;
+    if ((sub & 3) == 0) sdst[sub >> 2] = (uint8_t)(E + 127);
+  }
+}
+
+int grid_for_rows(int64_t rows) {
+  const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t cap = 256 * 32;   // grid-stride beyond ~32 resident blocks per CU
+  return (int)(blocks < cap ? blocks : cap);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, bool f32, int64_t rows, int64_t row_stride,
+                           uint8_t* values, uint8_t* scales, hipStream_t stream) {
+  const int grid = grid_for_rows(rows);
+  if (f32)
+    hipLaunchKernelGGL((mxfp4_rows_kernel<F32In, false>), dim3(grid), dim3(256), 0, stream, x, rows,
+                       row_stride, nullptr, 0, values, scales);
+  else
+    hipLaunchKernelGGL((mxfp4_rows_kernel<Bf16In, false>), dim3(grid), dim3(256), 0, stream, x, rows,
+                       row_stride, nullptr, 0, values, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_insert(const void* k, bool f32, int64_t num_tokens, int64_t row_stride,
+                         const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
+                         hipStream_t stream) {
+  const int grid = grid_for_rows(num_tokens);
+  const int64_t num_slots = num_pages * kPage;
+  if (f32)
+    hipLaunchKernelGGL((mxfp4_rows_kernel<F32In, true>), dim3(grid), dim3(256), 0, stream, k,
+                       num_tokens, row_stride, slot_mapping, num_slots, cache, nullptr);
+  else
+    hipLaunchKernelGGL((mxfp4_rows_kernel<Bf16In, true>), dim3(grid), dim3(256), 0, stream, k,
+                       num_tokens, row_stride, slot_mapping, num_slots, cache, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace mxidx

@@ -1,0 +1,40 @@
+// Host-side launchers of the gfx950 kernels.  Arguments are validated by the
+// C ABI layer (abi.hip) before these are called; each launcher only sizes the
+// grid and enqueues on `stream`, returning the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxidx {
+
+hipError_t launch_quantize(const void* x, bool f32, int64_t rows, int64_t row_stride,
+                           uint8_t* values, uint8_t* scales, hipStream_t stream);
+
+hipError_t launch_insert(const void* k, bool f32, int64_t num_tokens, int64_t row_stride,
+                         const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
+                         hipStream_t stream);
+
+hipError_t launch_gather(const uint8_t* cache, int64_t num_pages, const int32_t* block_table,
+                         int64_t bt_row_stride, const int32_t* seq_lens,
+                         const int64_t* cu_seq_offsets, int batch, int64_t max_seq_len,
+                         int64_t total_tokens, uint8_t* k_values, uint8_t* k_scales,
+                         hipStream_t stream);
+
+hipError_t launch_logits_prefill(const uint8_t* q_values, const uint8_t* q_scales,
+                                 const uint8_t* k_values, const uint8_t* k_scales,
+                                 const float* weights, const int32_t* ks, const int32_t* ke,
+                                 int64_t T, int H, int64_t S, float* logits, int64_t ld,
+                                 int clean, hipStream_t stream);
+
+hipError_t launch_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
+                               const float* weights, const uint8_t* cache, int64_t num_pages,
+                               const int32_t* block_table, int64_t bt_row_stride,
+                               const int32_t* context_lens, int B, int next_n, int H,
+                               int64_t max_context_len, float* logits, int64_t ld, int clean,
+                               hipStream_t stream);
+
+hipError_t launch_topk(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
+                       const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream);
+
+}  // namespace mxidx

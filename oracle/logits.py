@@ -62,35 +62,48 @@ def _dequant_q(q_codes, q_scales):
 
 
 def mqa_logits(q_codes, q_scales, k_codes, k_scales, w, ks, ke, width=None, chunk=64,
-               rows=None):
+               rows=None, with_bound=False):
     """Dense logits, float64 [len(rows), width], -inf outside [ks, ke).
 
     q_codes [T, H, 64], q_scales [T, H, 4], k_codes [S, 64], k_scales [S, 4],
-    w [T, H] (float32 values), ks/ke [T].  ``rows`` selects query rows
-    (default all); ``width`` defaults to S.
+    w [T, H] (float32 values), ks/ke [T] (ke is clipped to S).  ``rows``
+    selects query rows (default all); ``width`` defaults to S.  With
+    ``with_bound`` also returns A (see ``abs_bound``) for the same entries
+    (0 where masked).
     """
     check_exact(q_codes, q_scales, k_codes, k_scales)
     T = np.asarray(q_codes).shape[0]
     S = np.asarray(k_codes).shape[0]
     width = S if width is None else width
     rows = np.arange(T) if rows is None else np.asarray(rows)
+    ks = np.asarray(ks)
+    ke = np.minimum(np.asarray(ke), S)
     khat = dequantize_rows(k_codes, k_scales)                    # [S, 128]
     out = np.full((len(rows), width), -np.inf, dtype=np.float64)
+    bound = np.zeros((len(rows), width), dtype=np.float64) if with_bound else None
     w = np.asarray(w, dtype=np.float64)
     for c0 in range(0, len(rows), chunk):
         rr = rows[c0:c0 + chunk]
         qh = _dequant_q(np.asarray(q_codes)[rr], np.asarray(q_scales)[rr])  # [c, H, 128]
-        lo = int(np.min(np.asarray(ks)[rr]))
-        hi = int(np.max(np.asarray(ke)[rr]))
+        lo = int(np.min(ks[rr]))
+        hi = int(np.max(ke[rr]))
         if hi <= lo:
             continue
         d = qh @ khat[lo:hi].T                                   # [c, H, hi-lo]
         score = np.einsum("th,ths->ts", w[rr], np.maximum(d, 0.0))
+        if with_bound:
+            ab = np.zeros_like(d)
+            for b in range(NBLOCKS):
+                sl = slice(b * BLOCK, (b + 1) * BLOCK)
+                ab += np.abs(qh[:, :, sl] @ khat[lo:hi, sl].T)
+            bnd = np.einsum("th,ths->ts", np.abs(w[rr]), ab)
         for j, t in enumerate(rr):
             a, b = int(ks[t]), int(ke[t])
             if b > a:
                 out[c0 + j, a:b] = score[j, a - lo:b - lo]
-    return out
+                if with_bound:
+                    bound[c0 + j, a:b] = bnd[j, a - lo:b - lo]
+    return (out, bound) if with_bound else out
 
 
 def abs_bound(q_codes, q_scales, k_codes, k_scales, w, rows, cols):
@@ -117,7 +130,7 @@ def decode_visible_end(context_lens, next_n):
 
 
 def paged_mqa_logits(q_codes, q_scales, w, cache, block_table, context_lens, next_n,
-                     width, page_size=PAGE_SIZE, seqs=None):
+                     width, page_size=PAGE_SIZE, seqs=None, with_bound=False):
     """Paged decode logits, float64 [B*next_n, width] (-inf where not visible).
 
     q_codes [B*next_n, H, 64], q_scales [B*next_n, H, 4], w [B*next_n, H].
@@ -126,6 +139,7 @@ def paged_mqa_logits(q_codes, q_scales, w, cache, block_table, context_lens, nex
     """
     B = len(context_lens)
     out = np.full((B * next_n, width), -np.inf, dtype=np.float64)
+    bound = np.zeros((B * next_n, width), dtype=np.float64) if with_bound else None
     ke_all = decode_visible_end(context_lens, next_n)
     seqs = range(B) if seqs is None else seqs
     for b in seqs:
@@ -133,7 +147,10 @@ def paged_mqa_logits(q_codes, q_scales, w, cache, block_table, context_lens, nex
         kc, ksc = gather(cache, np.asarray(block_table)[b:b + 1], [L], [0], L, page_size)
         r = np.arange(b * next_n, (b + 1) * next_n)
         sub = mqa_logits(np.asarray(q_codes)[r], np.asarray(q_scales)[r], kc, ksc,
-                         np.asarray(w)[r], np.zeros(next_n, np.int64), ke_all[r],
-                         width=L)
-        out[r, :L] = sub
-    return out
+                         np.asarray(w)[r], np.zeros(next_n, np.int64), np.maximum(ke_all[r], 0),
+                         width=L, with_bound=with_bound)
+        if with_bound:
+            out[r, :L], bound[r, :L] = sub
+        else:
+            out[r, :L] = sub
+    return (out, bound) if with_bound else out

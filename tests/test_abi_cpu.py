@@ -1,0 +1,116 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, rejects host-checkable bad arguments with IDX_ERR_ARG before
+touching a device, treats empty work as a no-op, and fails closed
+(IDX_ERR_NO_DEVICE) when no device is present."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_paged_cache_quant_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxidx.h")
+
+OK, ERR_ARG, ERR_NO_DEVICE, ERR_ARCH, ERR_LAUNCH = 0, 1, 2, 3, 4
+
+# Fake, suitably aligned "device" addresses: never dereferenced, because every
+# call below either fails validation or stops at the device gate.
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10001)      # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mx.lib_path):
+        from mxfp4_paged_cache_quant_amd import build
+        build.build()
+    return mx.lib()
+
+
+def _has_gpu():
+    import torch
+    return torch.cuda.is_available()
+
+
+def test_header_declarations_are_exported(L):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(idx_[a-z_]+)\s*\(", text))
+    assert declared == set(mx.EXPORTS), declared ^ set(mx.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_version_and_strerror(L):
+    assert L.idx_version() == 100
+    for st in range(5):
+        assert L.idx_strerror(st)
+    assert L.idx_strerror(99) == b"unknown status"
+
+
+def test_quantize_argument_validation(L):
+    assert L.idx_quantize(P, 2, 4, 128, P, P2, None) == ERR_ARG           # bad dtype
+    assert L.idx_quantize(P, 0, -1, 128, P, P2, None) == ERR_ARG          # negative rows
+    assert L.idx_quantize(P, 0, 4, 100, P, P2, None) == ERR_ARG           # stride < 128
+    assert L.idx_quantize(P, 0, 4, 132, P, P2, None) == ERR_ARG           # bf16 stride % 8
+    assert L.idx_quantize(P, 1, 4, 130, P, P2, None) == ERR_ARG           # f32 stride % 4
+    assert L.idx_quantize(MIS, 0, 4, 128, P, P2, None) == ERR_ARG         # misaligned input
+    assert L.idx_quantize(None, 0, 4, 128, P, P2, None) == ERR_ARG        # null input
+    assert L.idx_quantize(P, 0, 4, 128, None, P2, None) == ERR_ARG        # null output
+    assert L.idx_quantize(None, 0, 0, 128, None, None, None) == OK        # empty: no-op
+
+
+def test_insert_argument_validation(L):
+    assert L.idx_insert(P, 0, 4, 128, P, P2, 4, 32, None) == ERR_ARG      # page size != 64
+    assert L.idx_insert(P, 0, 4, 128, None, P2, 4, 64, None) == ERR_ARG   # null slot mapping
+    assert L.idx_insert(P, 0, 4, 128, P, None, 4, 64, None) == ERR_ARG    # null cache
+    assert L.idx_insert(P, 0, 4, 128, P, P2, -1, 64, None) == ERR_ARG     # negative pages
+    assert L.idx_insert(None, 0, 0, 128, None, None, 0, 64, None) == OK
+
+
+def test_gather_argument_validation(L):
+    assert L.idx_gather(P, 4, 64, P, 1, P, P, 2, 128, 256, P, P2, None) == ERR_ARG  # bt stride < 2 pages
+    assert L.idx_gather(MIS, 4, 64, P, 2, P, P, 2, 128, 256, P, P2, None) == ERR_ARG
+    assert L.idx_gather(P, 4, 64, P, 2, P, P, 2, 128, 256, MIS, P2, None) == ERR_ARG
+    assert L.idx_gather(P, 4, 64, P, 2, P, P, 0, 128, 256, P, P2, None) == OK        # no sequences
+
+
+def test_logits_argument_validation(L):
+    # H must be a multiple of 16 in [16, 128]
+    for H in (0, 8, 24, 144):
+        assert L.idx_logits_prefill(P, P, P, P, P, None, P, 4, H, 64, P, 64, 1, None) == ERR_ARG
+        assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 1, 1, H, 64, P, 64, 1, None) == ERR_ARG
+    assert L.idx_logits_prefill(P, P, P, P, P, None, P, 4, 32, 64, P, 63, 1, None) == ERR_ARG   # ld < S
+    assert L.idx_logits_prefill(P, P, P, P, P, None, None, 4, 32, 64, P, 64, 1, None) == ERR_ARG  # null ke
+    assert L.idx_logits_prefill(P, P, P, P, MIS, None, P, 4, 32, 64, P, 64, 1, None) == ERR_ARG
+    assert L.idx_logits_prefill(P, P, P, P, P, None, P, 0, 32, 64, P, 64, 1, None) == OK
+    assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 1, 0, 32, 64, P, 64, 1, None) == ERR_ARG   # next_n 0
+    assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 1, 17, 32, 64, P, 64, 1, None) == ERR_ARG  # next_n 17
+    assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 1, 1, 32, 65, P, 65, 1, None) == ERR_ARG   # bt stride
+    assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 63, 1, None) == ERR_ARG   # ld
+    assert L.idx_logits_paged(P, P, P, P, 4, 48, P, 1, P, 1, 1, 32, 64, P, 64, 1, None) == ERR_ARG   # page
+    assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 0, 1, 32, 64, P, 64, 1, None) == OK
+
+
+def test_topk_argument_validation(L):
+    for k in (0, -3, 2049):
+        assert L.idx_topk(P, 4, 64, None, P, k, P, None) == ERR_ARG
+    assert L.idx_topk(P, 4, 64, None, None, 8, P, None) == ERR_ARG   # null ke
+    assert L.idx_topk(MIS, 4, 64, None, P, 8, P, None) == ERR_ARG
+    assert L.idx_topk(P, 0, 64, None, P, 8, P, None) == OK
+
+
+@pytest.mark.skipif(_has_gpu(), reason="checks the no-device path")
+def test_fails_closed_without_device(L):
+    assert L.idx_init(0) == ERR_NO_DEVICE
+    assert L.idx_quantize(P, 0, 4, 128, P, P2, None) == ERR_NO_DEVICE
+    assert L.idx_topk(P, 4, 64, None, P, 8, P, None) == ERR_NO_DEVICE
+    assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 64, 1, None) == ERR_NO_DEVICE
+
+
+def test_python_wrapper_raises_on_error(L):
+    with pytest.raises(mx.MxidxError):
+        mx._check(ERR_ARG, "probe")

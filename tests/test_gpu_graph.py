@@ -1,0 +1,59 @@
+"""HIP graph capture of one decode step (insert -> q quantize -> paged logits ->
+top-k): every replay, with eager work and host synchronization between the
+replays, must equal the eager result bit for bit (the pages' CUDA Graph tests,
+P2 "Validation")."""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_paged_cache_quant_amd as mx
+import workloads
+from oracle import logits as olog
+from tests.gpu_helpers import dev, host, new_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_step_graph_replays_match_eager():
+    case = workloads.decode_case(50, seq_lens=[1000, 4000, 64, 2500], H=32, next_n=1, topk=512)
+    B, W = 4, case["width"]
+    cache = new_cache(case["num_pages"], fill=0)
+    mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
+    last = np.cumsum(case["context_lens"]) - 1                 # the newest token of each sequence
+    k_new = dev(case["k"][last])
+    slot_new = dev(case["slot_mapping"][last])
+    q = dev(case["q"])
+    w = dev(case["w"])
+    bt = dev(case["block_table"])
+    ctx = dev(case["context_lens"])
+    ke = dev(olog.decode_visible_end(case["context_lens"], 1).astype(np.int32))
+    qv = torch.empty((B, 32, 64), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((B, 32, 4), dtype=torch.uint8, device="cuda")
+    logits = torch.empty((B, W), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda")
+
+    def step():
+        mx.insert(k_new, slot_new, cache)
+        mx.quantize(q, qv, qs)
+        mx.logits_paged(qv, qs, w, cache, bt, ctx, 1, W, logits=logits, clean=True)
+        mx.topk(logits, None, ke, 512, out=idx)
+
+    step()                                                     # warm-up (and gate) outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    rng = np.random.default_rng(1)
+    for rep in range(3):
+        newq = workloads.bf16_bits(rng.standard_normal(case["q"].shape).astype(np.float32))
+        q.copy_(dev(newq))
+        g.replay()
+        torch.cuda.synchronize()
+        got_logits, got_idx, got_cache = host(logits).copy(), host(idx).copy(), host(cache).copy()
+        _ = torch.randn(1000, device="cuda").sum().item()       # unrelated eager work in between
+        step()                                                 # eager reference, same inputs
+        torch.cuda.synchronize()
+        assert np.array_equal(got_logits, host(logits)), rep
+        assert np.array_equal(got_idx, host(idx)), rep
+        assert np.array_equal(got_cache, host(cache)), rep

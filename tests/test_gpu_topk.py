@@ -1,0 +1,91 @@
+"""GPU parity: per-row top-k sets equal the oracle's on identical float32 input."""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_paged_cache_quant_amd as mx
+from oracle import topk as otk
+from tests.gpu_helpers import dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(x, ks, ke, k, use_ks=True):
+    out = mx.topk(dev(x), dev(ks) if use_ks else None, dev(ke), k)
+    torch.cuda.synchronize()
+    got = host(out)
+    ref = otk.top_k_per_row(x, ks if use_ks else np.zeros(len(ke), np.int32), ke, k)
+    for r in range(x.shape[0]):
+        a = int(ks[r]) if use_ks else 0
+        n = max(0, min(int(ke[r]), x.shape[1]) - a)
+        m = min(k, n)
+        assert np.all(got[r, m:] == -1), r
+        assert sorted(got[r, :m].tolist()) == sorted(ref[r, :m].tolist()), r
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (63, 64), (64, 64), (65, 64), (3000, 2048), (2049, 2048),
+                                 (8192, 2048), (16384, 2048), (16385, 2048), (40000, 2048),
+                                 (131072, 2048), (5000, 1), (20000, 7)])
+def test_topk_random_rows(n, k):
+    rng = np.random.default_rng(n * 31 + k)
+    R = 6
+    x = rng.standard_normal((R, n)).astype(np.float32)
+    x[0, : n // 3] = np.round(x[0, : n // 3] * 4) / 4         # many exact ties
+    x[1, ::7] = 0.0
+    x[1, 3::7] = -0.0                                          # +0 / -0 ties
+    x[2] = np.abs(x[2])
+    ks = np.zeros(R, np.int32)
+    ke = np.full(R, n, np.int32)
+    ks[3] = n // 5
+    ke[4] = max(1, n - n // 7)
+    ks[5], ke[5] = n // 3, n // 3                               # empty range
+    _check(x, ks, ke, k)
+    _check(x, ks, ke, k, use_ks=False)
+
+
+def test_topk_all_equal_and_heavy_ties_take_lowest_columns():
+    n, k = 50000, 2048
+    x = np.ones((3, n), np.float32)
+    x[1, :10] = 2.0                                            # 10 winners, then 2038 lowest-index ties
+    x[2] = np.float32(1.0) + (np.arange(n) % 3 == 0) * np.float32(2 ** -20)
+    ks = np.zeros(3, np.int32)
+    ke = np.full(3, n, np.int32)
+    out = host(mx.topk(dev(x), dev(ks), dev(ke), k))
+    assert sorted(out[0].tolist()) == list(range(k))
+    assert sorted(out[1].tolist()) == list(range(k))
+    ref = otk.top_k_per_row(x, ks, ke, k)
+    for r in range(3):
+        assert sorted(out[r].tolist()) == sorted(ref[r].tolist())
+
+
+def test_topk_wide_threshold_bin_uses_memory_path():
+    # > 8192 keys share the level-1 bin of the k-th value (values differ only in
+    # low mantissa bits), so the candidate list cannot live in LDS.
+    rng = np.random.default_rng(5)
+    n, k = 60000, 2048
+    base = np.float32(1.5)
+    bits = base.view(np.uint32) + rng.integers(0, 1 << 20, size=n).astype(np.uint32)
+    x = bits.view(np.float32).reshape(1, n).copy()
+    x[0, rng.integers(0, n, 500)] = 3.0
+    _check(x, np.zeros(1, np.int32), np.full(1, n, np.int32), k)
+
+
+def test_topk_row_stride_and_ke_beyond_width():
+    rng = np.random.default_rng(9)
+    full = rng.standard_normal((4, 9000)).astype(np.float32)
+    t = dev(full)[:, :7000]                                    # row stride 9000
+    ke = np.array([7000, 6000, 9000, 100], np.int32)          # 9000 > width: clipped to the stride
+    out = host(mx.topk(t, None, dev(ke), 300))
+    ref = otk.top_k_per_row(full[:, :9000], np.zeros(4, np.int32), ke, 300)
+    for r in range(4):
+        assert sorted(out[r].tolist()) == sorted(ref[r].tolist())
+
+
+def test_topk_deterministic_across_runs():
+    rng = np.random.default_rng(3)
+    x = dev(np.round(rng.standard_normal((8, 30000)).astype(np.float32) * 8) / 8)
+    ke = dev(np.full(8, 30000, np.int32))
+    a = host(mx.topk(x, None, ke, 2048))
+    b = host(mx.topk(x, None, ke, 2048))
+    assert np.array_equal(a, b)

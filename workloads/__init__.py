@@ -62,13 +62,13 @@ def _values(rng, shape, dist, dtype):
     return bf16_bits(x) if dtype == "bf16" else x
 
 
-def allocate_pages(rng, seq_lens, spare_pages, page_size=PAGE_SIZE):
+def allocate_pages(rng, seq_lens, spare_pages, page_size=PAGE_SIZE, min_cols=1):
     """Fragmented page allocation.
 
     Physical page ids are a random permutation of all pages; sequence b takes
     the next ceil(L_b / P) ids of it.  ``spare_pages`` ids are never used (they
-    stay canary-filled).  Unused block-table entries point at page 0 (always a
-    valid page), never past the cache.
+    stay canary-filled).  The table has at least ``min_cols`` columns; unused
+    entries point at page 0 (always a valid page), never past the cache.
     Returns (block_table int32 [B, max_pages], slot_mapping int64 [sum L],
     num_pages).
     """
@@ -76,7 +76,7 @@ def allocate_pages(rng, seq_lens, spare_pages, page_size=PAGE_SIZE):
     need = (seq_lens + page_size - 1) // page_size
     num_pages = int(need.sum()) + int(spare_pages)
     perm = rng.permutation(num_pages).astype(np.int32)
-    max_pages = max(1, int(need.max()) if len(need) else 1)
+    max_pages = max(min_cols, int(need.max()) if len(need) else 1)
     bt = np.zeros((len(seq_lens), max_pages), dtype=np.int32)
     slots = []
     pos = 0
@@ -107,8 +107,9 @@ def decode_case(seed, seq_lens=None, H=32, next_n=1, dtype="bf16", k_dist="norma
     k = _values(st["k"], (N, HEAD_DIM), k_dist, dtype)
     q = _values(st["q"], (B * next_n, H, HEAD_DIM), q_dist, dtype)
     w = (st["w"].random((B * next_n, H), dtype=np.float32) * np.float32(w_scale)).astype(np.float32)
-    bt, slots, num_pages = allocate_pages(st["pages"], seq_lens, spare_pages)
     width = int(seq_lens.max()) if width is None else int(width)
+    bt, slots, num_pages = allocate_pages(st["pages"], seq_lens, spare_pages,
+                                          min_cols=-(-width // PAGE_SIZE))
     return dict(name=name, kind="decode", dtype=dtype, k=k, q=q, w=w,
                 slot_mapping=slots, block_table=bt, context_lens=seq_lens,
                 num_pages=num_pages, page_size=PAGE_SIZE, next_n=next_n, H=H,
