@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP4 paged indexer-cache hot path on one MI355X.
+
+Decode step (the headline): batch 16, one query token each, 8192-token
+contexts, 32 index heads, head_dim 128, MXFP4 cache (page 64, permuted block
+table), top-2048.  One step = insert of the 16 new tokens' K (quantize +
+scatter) -> MXFP4 quantization of the 16x32 query rows -> paged logits over
+all 131072 cached tokens -> top-2048 per row.  Metric: scored cache tokens per
+second = sum over rows of the visible context / step time.
+
+Timing: the step is captured in HIP graphs; W untimed warm-up steps, then
+exactly K steps between two device synchronizations.  The steps rotate over
+`--sets` independent copies of the inputs (caches included) so that the 8.9 MB
+cache is read from HBM rather than from the 256 MB Infinity Cache.
+
+Also reported: per-kernel average durations (HIP events around graphs of
+back-to-back launches of one kernel over the rotating sets, on the stream the
+kernels run on), the roofline of the dominant kernel, the prefill-chunk
+logits throughput (8192 x 8192 causal, 32 heads) against the FP4 MFMA peak,
+and the CPU oracle timed on a bounded sample of the decode step.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=960)
+    ap.add_argument("--warmup", type=int, default=96)
+    ap.add_argument("--sets", type=int, default=96, help="rotating input sets (defeats the MALL)")
+    ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
+    ap.add_argument("--prefill", choices=["chunk", "none"], default="chunk")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def dev(a):
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+class DecodeSet:
+    """One independent copy of every input and output of the decode step."""
+
+    def __init__(self, base, case):
+        import torch
+        B, H = len(case["context_lens"]), case["H"]
+        self.cache = base["cache"].clone()
+        self.k_new = base["k_new"].clone()
+        self.slot_new = base["slot_new"].clone()
+        self.q = base["q"].clone()
+        self.w = base["w"].clone()
+        self.bt = base["bt"].clone()
+        self.ctx = base["ctx"].clone()
+        self.ke = base["ke"].clone()
+        self.qv = torch.empty((B, H, 64), dtype=torch.uint8, device="cuda")
+        self.qs = torch.empty((B, H, 4), dtype=torch.uint8, device="cuda")
+        self.logits = torch.empty((B, case["width"]), dtype=torch.float32, device="cuda")
+        self.idx = torch.empty((B, case["topk"]), dtype=torch.int32, device="cuda")
+
+
+def build_decode_sets(case, n_sets):
+    import numpy as np
+    import torch
+    import mxfp4_paged_cache_quant_amd as mx
+    cache = torch.zeros((case["num_pages"], 64 * 68), dtype=torch.uint8, device="cuda")
+    mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
+    last = np.cumsum(case["context_lens"]) - 1
+    L = case["context_lens"].astype(np.int64)
+    ke = (L - case["next_n"] + 1).astype(np.int32)           # next_n == 1: the row sees L tokens
+    base = dict(cache=cache, k_new=dev(case["k"][last]), slot_new=dev(case["slot_mapping"][last]),
+                q=dev(case["q"]), w=dev(case["w"]), bt=dev(case["block_table"]),
+                ctx=dev(case["context_lens"]), ke=dev(ke))
+    sets = [DecodeSet(base, case) for _ in range(n_sets)]
+    torch.cuda.synchronize()
+    return sets
+
+
+def decode_ops(case):
+    """The four calls of one decode step, each as f(set)."""
+    import mxfp4_paged_cache_quant_amd as mx
+    W, K = case["width"], case["topk"]
+    return {
+        "insert": lambda s: mx.insert(s.k_new, s.slot_new, s.cache),
+        "quantize": lambda s: mx.quantize(s.q, s.qv, s.qs),
+        "logits_paged": lambda s: mx.logits_paged(s.qv, s.qs, s.w, s.cache, s.bt, s.ctx, 1, W,
+                                                  logits=s.logits, clean=True),
+        "topk": lambda s: mx.topk(s.logits, None, s.ke, K, out=s.idx),
+    }
+
+
+def capture(fn_list):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fn_list:
+            fn()
+    return g
+
+
+def time_graph(g, reps):
+    """Average ms per replay, HIP events on the current stream."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        g.replay()
+    stop.record()
+    stop.synchronize()
+    return start.elapsed_time(stop) / reps
+
+
+def bench_decode(args, case):
+    import torch
+    sets = build_decode_sets(case, args.sets)
+    ops = decode_ops(case)
+    order = ["insert", "quantize", "logits_paged", "topk"]
+
+    def step_fns(lo, hi):
+        return [(lambda s=s, name=name: ops[name](s)) for s in sets[lo:hi] for name in order]
+
+    # eager warm-up of every call (also runs the architecture gate outside capture)
+    for fn in step_fns(0, 1):
+        fn()
+    torch.cuda.synchronize()
+    G = len(sets)
+    g_full = capture(step_fns(0, G))
+    rem = args.steps % G
+    g_rem = capture(step_fns(0, rem)) if rem else None
+    wfull, wrem = divmod(args.warmup, G)
+    g_wrem = capture(step_fns(0, wrem)) if wrem else None
+    for _ in range(wfull):
+        g_full.replay()
+    if g_wrem is not None:
+        g_wrem.replay()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for _ in range(args.steps // G):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # per-kernel average durations: a graph of G back-to-back launches of one kernel
+    per_kernel = {}
+    for name in order:
+        g = capture([(lambda s=s: ops[name](s)) for s in sets])
+        per_kernel[name] = time_graph(g, args.kernel_reps) / G * 1e3     # us per launch
+        del g
+    return elapsed, per_kernel
+
+
+def bench_prefill(args):
+    import numpy as np
+    import torch
+    import mxfp4_paged_cache_quant_amd as mx
+    import workloads
+    case = workloads.prefill_chunk()
+    T, S, H = case["T"], case["S"], case["H"]
+    cache = torch.zeros((case["num_pages"], 64 * 68), dtype=torch.uint8, device="cuda")
+    k, slots, q, w = dev(case["k"]), dev(case["slot_mapping"]), dev(case["q"]), dev(case["w"])
+    bt, sl, cu = dev(case["block_table"]), dev(case["seq_lens"]), dev(case["cu_seq_offsets"])
+    ks, ke = dev(case["ks"]), dev(case["ke"])
+    kv = torch.empty((S, 64), dtype=torch.uint8, device="cuda")
+    ksc = torch.empty((S, 4), dtype=torch.uint8, device="cuda")
+    qv = torch.empty((T, H, 64), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((T, H, 4), dtype=torch.uint8, device="cuda")
+    logits = torch.empty((T, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, case["topk"]), dtype=torch.int32, device="cuda")
+    ops = {
+        "insert": lambda: mx.insert(k, slots, cache),
+        "quantize": lambda: mx.quantize(q, qv, qs),
+        "gather": lambda: mx.gather(cache, bt, sl, cu, S, S, k_values=kv, k_scales=ksc),
+        "logits_prefill": lambda: mx.logits_prefill(qv, qs, kv, ksc, w, ks, ke, logits=logits,
+                                                    clean=False),
+        "topk": lambda: mx.topk(logits, ks, ke, case["topk"], out=idx),
+    }
+    for fn in ops.values():
+        fn()
+    torch.cuda.synchronize()
+    per = {}
+    for name, fn in ops.items():
+        g = capture([fn] * 4)
+        per[name] = time_graph(g, 10) / 4 * 1e3
+    step_us = sum(per.values())
+    pairs = int(np.sum(case["ke"].astype(np.int64) - case["ks"]))
+    flops = 2.0 * H * 128 * pairs
+    tflops = flops / (per["logits_prefill"] * 1e-6) / 1e12
+    return {
+        "workload": case["name"], "T": T, "S": S, "heads": H, "causal_pairs": pairs,
+        "logits_flop": flops, "logits_us": round(per["logits_prefill"], 2),
+        "logits_tflops": round(tflops, 1),
+        "logits_frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
+        "step_us": round(step_us, 2),
+        "kernels_us": {k2: round(v, 2) for k2, v in per.items()},
+    }
+
+
+def cpu_baseline(case, seconds):
+    """The oracle (never tuned for this) on a bounded sample of the decode step."""
+    import numpy as np
+    from oracle import logits as olog, mxfp4 as omx, paged_cache as opc, topk as otk
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    B = len(case["context_lens"])
+    H = case["H"]
+    cache = np.zeros((case["num_pages"], 64 * 68), np.uint8)
+    cache = opc.insert(cache, omx.bf16_bits_to_f64(case["k"]), case["slot_mapping"])
+    last = np.cumsum(case["context_lens"]) - 1
+    scored, t_total, seqs_done = 0, 0.0, 0
+    b = 0
+    while t_total < seconds:
+        t0 = time.perf_counter()
+        cache = opc.insert(cache, omx.bf16_bits_to_f64(case["k"][last[b:b + 1]]),
+                           case["slot_mapping"][last[b:b + 1]])
+        qc, qsc = omx.quantize_rows(omx.bf16_bits_to_f64(case["q"][b:b + 1]))
+        qc, qsc = qc.reshape(1, H, 64), qsc.reshape(1, H, 4)
+        L = int(case["context_lens"][b])
+        ref = olog.paged_mqa_logits(qc, qsc, case["w"][b:b + 1], cache, case["block_table"][b:b + 1],
+                                    case["context_lens"][b:b + 1], 1, L)
+        otk.top_k_per_row(ref.astype(np.float32), [0], [L], case["topk"])
+        t_total += time.perf_counter() - t0
+        scored += L
+        seqs_done += 1
+        b = (b + 1) % B
+    return {"value": scored / t_total, "unit": "scored cache tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{seqs_done} single-sequence decode steps (new-token insert, q quantize, "
+                      f"paged logits over 8192 tokens, top-2048) of the 16x8192 workload, "
+                      f"{t_total:.1f} s of CPU time"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the MXFP4 indexer path has no multi-GPU mode in this "
+              "build (sharding is by sequence with no exchange; see the design notes). "
+              "Run with --gpus 1.", flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mxfp4_paged_cache_quant_amd as mx
+    import workloads
+
+    torch.cuda.set_device(0)
+    mx.init(0)
+    case = workloads.paged_decode()
+    log(f"[bench] decode workload {case['name']}: building {args.sets} rotating sets")
+    elapsed, per_kernel = bench_decode(args, case)
+    ms_per_step = elapsed / args.steps * 1e3
+    scored = int(np.sum(case["context_lens"]))
+    value = scored * args.steps / elapsed
+    log(f"[bench] decode: {ms_per_step * 1e3:.2f} us/step, kernels {per_kernel}")
+
+    B, H, L = len(case["context_lens"]), case["H"], int(case["context_lens"][0])
+    alg_bytes = {
+        "insert": B * (256 + 8 + 68),
+        "quantize": B * H * (256 + 68),
+        "logits_paged": scored * (68 + 4) + B * H * (68 + 4),
+        "topk": scored * 4 + B * case["topk"] * 4,
+    }
+    dominant = max(per_kernel, key=per_kernel.get)
+    achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "alg_bytes_per_launch": alg_bytes[dominant],
+                "avg_launch_us": round(per_kernel[dominant], 3)}
+    kernels = {k: {"avg_us": round(v, 3), "alg_bytes": alg_bytes[k],
+                   "gbs": round(alg_bytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in per_kernel.items()}
+
+    prefill = None
+    if args.prefill == "chunk":
+        log("[bench] prefill chunk 8192x8192")
+        prefill = bench_prefill(args)
+        log(f"[bench] prefill: {prefill}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    out = {
+        "metric": "scored cache tokens/sec (paged decode) + prefill logits TFLOP/s, % of roofline",
+        "value": round(value, 1),
+        "unit": "scored cache tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": case["name"], "batch": B, "context": L, "heads": H,
+                   "head_dim": 128, "page_size": 64, "next_n": 1, "topk": case["topk"],
+                   "step": "insert(16 new tokens)+quantize(q)+logits_paged+topk",
+                   "rotating_sets": args.sets, "hip_graph": True, "parallelism": "none"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
