@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=96, help="rotating input sets (defeats the MALL)")
     ap.add_argument("--kernel-reps", type=int, default=20, help="graph replays per kernel timing")
     ap.add_argument("--prefill", choices=["chunk", "none"], default="chunk")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context decode and long prefill measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -224,6 +226,87 @@ def bench_prefill(args):
     }
 
 
+def time_fn(fn, reps, per_graph=4):
+    """Average us per call of fn, from a graph of per_graph back-to-back calls."""
+    g = capture([fn] * per_graph)
+    t = time_graph(g, reps) / per_graph * 1e3
+    del g
+    return t
+
+
+def bench_long_decode():
+    """64 sequences of 32K..128K tokens: cache build (insert), paged logits, top-k."""
+    import numpy as np
+    import torch
+    import mxfp4_paged_cache_quant_amd as mx
+    import workloads
+    case = workloads.long_decode()
+    B, H, W = len(case["context_lens"]), case["H"], case["width"]
+    N = int(np.sum(case["context_lens"]))
+    k, slots = dev(case["k"]), dev(case["slot_mapping"])
+    cache = torch.zeros((case["num_pages"], 64 * 68), dtype=torch.uint8, device="cuda")
+    qv, qs = mx.quantize(dev(case["q"]))
+    w, bt, ctx = dev(case["w"]), dev(case["block_table"]), dev(case["context_lens"])
+    ke = dev(case["context_lens"].astype(np.int32))
+    logits = torch.empty((B, W), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, case["topk"]), dtype=torch.int32, device="cuda")
+    ins = lambda: mx.insert(k, slots, cache)  # noqa: E731
+    lg = lambda: mx.logits_paged(qv, qs, w, cache, bt, ctx, 1, W, logits=logits, clean=True)  # noqa: E731
+    tk = lambda: mx.topk(logits, None, ke, case["topk"], out=idx)  # noqa: E731
+    for fn in (ins, lg, tk):
+        fn()
+    torch.cuda.synchronize()
+    t_ins = time_fn(ins, 5, 2)
+    t_lg = time_fn(lg, 10, 4)
+    t_tk = time_fn(tk, 10, 4)
+    b_ins = N * (256 + 8 + 68)
+    b_lg = N * 72 + B * H * 72
+    b_tk = N * 4 + B * case["topk"] * 4
+    return {
+        "workload": case["name"], "tokens": N, "cache_bytes": case["num_pages"] * 64 * 68,
+        "insert_us": round(t_ins, 1), "insert_gbs": round(b_ins / t_ins / 1e3, 1),
+        "logits_paged_us": round(t_lg, 1), "logits_paged_gbs": round(b_lg / t_lg / 1e3, 1),
+        "logits_paged_frac_hbm": round(b_lg / t_lg / 1e3 / HBM_PEAK_GBS, 4),
+        "topk_us": round(t_tk, 1), "topk_gbs": round(b_tk / t_tk / 1e3, 1),
+        "decode_step_us": round(t_lg + t_tk, 1),
+        "scored_tokens_per_s": round(N / ((t_lg + t_tk) * 1e-6), 1),
+    }
+
+
+def bench_long_prefill():
+    """16384 queries over 122880 cached tokens, 64 heads: logits and top-k."""
+    import numpy as np
+    import torch
+    import mxfp4_paged_cache_quant_amd as mx
+    import workloads
+    case = workloads.long_prefill()
+    T, S, H = case["T"], case["S"], case["H"]
+    cache = torch.zeros((case["num_pages"], 64 * 68), dtype=torch.uint8, device="cuda")
+    mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
+    kv, ksc = mx.gather(cache, dev(case["block_table"]), dev(case["seq_lens"]),
+                        dev(case["cu_seq_offsets"]), S, S)
+    qv, qs = mx.quantize(dev(case["q"]))
+    w, ks, ke = dev(case["w"]), dev(case["ks"]), dev(case["ke"])
+    logits = torch.empty((T, S), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, case["topk"]), dtype=torch.int32, device="cuda")
+    lg = lambda: mx.logits_prefill(qv, qs, kv, ksc, w, ks, ke, logits=logits, clean=False)  # noqa: E731
+    tk = lambda: mx.topk(logits, ks, ke, case["topk"], out=idx)  # noqa: E731
+    lg()
+    tk()
+    torch.cuda.synchronize()
+    t_lg = time_fn(lg, 3, 2)
+    t_tk = time_fn(tk, 3, 2)
+    pairs = int(np.sum(case["ke"].astype(np.int64) - case["ks"]))
+    flops = 2.0 * H * 128 * pairs
+    tflops = flops / (t_lg * 1e-6) / 1e12
+    return {
+        "workload": case["name"], "causal_pairs": pairs, "logits_flop": flops,
+        "logits_us": round(t_lg, 1), "logits_tflops": round(tflops, 1),
+        "logits_frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
+        "topk_us": round(t_tk, 1), "topk_gbs": round((pairs * 4 + T * case["topk"] * 4) / t_tk / 1e3, 1),
+    }
+
+
 def cpu_baseline(case, seconds):
     """The oracle (never tuned for this) on a bounded sample of the decode step."""
     import numpy as np
@@ -307,6 +390,17 @@ def main():
         prefill = bench_prefill(args)
         log(f"[bench] prefill: {prefill}")
 
+    long_decode = long_prefill = None
+    if not args.no_long:
+        log("[bench] long-context decode 64 x U[32K,128K]")
+        long_decode = bench_long_decode()
+        log(f"[bench] long decode: {long_decode}")
+        torch.cuda.empty_cache()
+        log("[bench] long prefill 16384 x 122880")
+        long_prefill = bench_long_prefill()
+        log(f"[bench] long prefill: {long_prefill}")
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
@@ -332,6 +426,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "prefill": prefill,
+        "long_decode": long_decode,
+        "long_prefill": long_prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

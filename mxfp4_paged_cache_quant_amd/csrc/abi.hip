@@ -126,7 +126,7 @@ int idx_logits_prefill(const uint8_t* q_values, const uint8_t* q_scales, const u
                        const uint8_t* k_scales, const float* weights, const int32_t* ks,
                        const int32_t* ke, int64_t T, int H, int64_t S, float* logits,
                        int64_t logits_row_stride, int clean, hipStream_t stream) {
-  if (T < 0 || S < 0 || !heads_ok(H)) return IDX_ERR_ARG;
+  if (T < 0 || S < 0 || S > 0x7fffffffLL - 1024 || !heads_ok(H)) return IDX_ERR_ARG;
   if (T == 0 || S == 0) return IDX_OK;
   if (logits_row_stride < S) return IDX_ERR_ARG;
   if (!q_values || !aligned(q_values, 16) || !q_scales || !k_values || !aligned(k_values, 16) ||

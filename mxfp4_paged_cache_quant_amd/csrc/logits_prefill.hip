@@ -32,12 +32,30 @@ namespace {
 
 constexpr int kKeyChunk = 1024;
 
+// B operands of 64 consecutive keys: lane (g, n) takes the 16 code bytes of
+// block g of key c0 + 16*j + n for each tile j, and that key's 4 scale bytes
+// (the block's byte is extracted when the tile is used).  Keys past the last
+// one are clamped to it: their columns are never stored.
+struct KTile {
+  uint4 code[4];
+  uint32_t scale[4];
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ kv, const uint8_t* __restrict__ ksc,
+                                       int c0, int last, int g, int n) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = min(c0 + 16 * j + n, last);
+      code[j] = *reinterpret_cast<const uint4*>(kv + (int64_t)key * kCodeBytes + g * 16);
+      scale[j] = *reinterpret_cast<const uint32_t*>(ksc + (int64_t)key * kScaleBytes);
+    }
+  }
+};
+
 template <int NH, int RW>
 __global__ __launch_bounds__(256) void logits_prefill_kernel(
     const uint8_t* __restrict__ q_values, const uint8_t* __restrict__ q_scales,
     const uint8_t* __restrict__ k_values, const uint8_t* __restrict__ k_scales,
     const float* __restrict__ weights, const int32_t* __restrict__ ks,
-    const int32_t* __restrict__ ke, int64_t T, int64_t S, float* __restrict__ logits, int64_t ld,
+    const int32_t* __restrict__ ke, int64_t T, int S, float* __restrict__ logits, int64_t ld,
     int clean, int64_t n_qb, int64_t n_kc) {
   constexpr int H = 16 * NH;
   const int lane = threadIdx.x & 63;
@@ -55,23 +73,43 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(
     kc = blockIdx.x % n_kc;
   }
   const int64_t t0 = qb * (4 * RW) + wave * RW;
-  const int64_t c_begin = kc * kKeyChunk;
-  const int64_t c_end = min(c_begin + (int64_t)kKeyChunk, S);
+  const int c_begin = (int)kc * kKeyChunk;
+  const int c_end = min(c_begin + kKeyChunk, S);
 
-  int64_t lo[RW], hi[RW];
-  bool any = false;
+  // visible range of each row (empty for rows past T), and the key window
+  // [need_lo, need_hi) inside this chunk that any of the rows needs
+  int lo[RW], hi[RW];
+  int need_lo = c_end, need_hi = c_begin;
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     const int64_t t = t0 + i;
     lo[i] = 0;
     hi[i] = 0;
     if (t < T) {
-      lo[i] = ks ? max((int64_t)ks[t], (int64_t)0) : 0;
-      hi[i] = min((int64_t)ke[t], S);
-      any |= (lo[i] < hi[i]) && (lo[i] < c_end) && (hi[i] > c_begin);
+      lo[i] = ks ? max(ks[t], 0) : 0;
+      hi[i] = min(ke[t], S);
+      if (lo[i] < hi[i]) {
+        need_lo = min(need_lo, max(lo[i], c_begin));
+        need_hi = max(need_hi, min(hi[i], c_end));
+      }
     }
   }
-  if (!any && !clean) return;
+  float* lrow[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) lrow[i] = logits + min(t0 + i, T - 1) * ld;
+  const int k_first = c_begin + ((need_lo - c_begin) & ~63);
+  if (clean) {
+    // -inf for the keys of this chunk that the computed window below does not
+    // cover (inside the window, masked columns are written at store time)
+    for (int c0 = c_begin; c0 < c_end; c0 += 64) {
+      if (need_lo < need_hi && c0 >= k_first && c0 < need_hi) continue;
+      const int col = c0 + lane;
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+        if (t0 + i < T && col < c_end) lrow[i][col] = neg_inf();
+    }
+  }
+  if (need_lo >= need_hi) return;
 
   uint4 a[RW][NH];
   int sa[RW][NH];
@@ -89,51 +127,44 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(
   }
 
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  for (int64_t c0 = c_begin; c0 < c_end; c0 += 64) {
-    bool need = false;
-#pragma unroll
-    for (int i = 0; i < RW; ++i) need |= (c0 < hi[i]) && (c0 + 64 > lo[i]);
-    const int64_t col = c0 + lane;
-    if (!need) {
-      if (clean && col < S)
-#pragma unroll
-        for (int i = 0; i < RW; ++i)
-          if (t0 + i < T) logits[(t0 + i) * ld + col] = neg_inf();
-      continue;
-    }
-    uint4 bk[4];
+  const int last = S - 1;
+  KTile nxt;
+  nxt.load(k_values, k_scales, k_first, last, g, n);
+  for (int c0 = k_first; c0 < need_hi; c0 += 64) {
+    const KTile cur = nxt;
+    if (c0 + 64 < need_hi) nxt.load(k_values, k_scales, c0 + 64, last, g, n);   // prefetch
     int bs[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t key = c0 + 16 * j + n;
-      if (key < S) {
-        bk[j] = *reinterpret_cast<const uint4*>(k_values + key * kCodeBytes + g * 16);
-        const uint32_t s4 = *reinterpret_cast<const uint32_t*>(k_scales + key * kScaleBytes);
-        bs[j] = (int)((s4 >> (8 * g)) & 0xffu);
-      } else {
-        bk[j] = make_uint4(0, 0, 0, 0);
-        bs[j] = 127;
-      }
-    }
+    for (int j = 0; j < 4; ++j) bs[j] = (int)((cur.scale[j] >> (8 * g)) & 0xffu);
+    const int col = c0 + lane;
+    // All rows x head groups x tiles, no per-row branches: rows that see
+    // nothing of these 64 keys are masked at the store.  The MFMAs of the next
+    // (row, group) are issued before the epilogue of the current one.
+    float acc[RW][4];
+    v4f d[2][4];
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const int64_t t = t0 + i;
-      if (t >= T) continue;
-      if (!((c0 < hi[i]) && (c0 + 64 > lo[i]))) {
-        if (clean && col < S) logits[t * ld + col] = neg_inf();
-        continue;
-      }
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) d[0][j] = mfma_fp4(a[0][0], cur.code[j], sa[0][0], bs[j], zero);
 #pragma unroll
-      for (int grp = 0; grp < NH; ++grp)
+    for (int p = 0; p < RW * NH; ++p) {
+      const int i = p / NH, grp = p % NH;
+      if (p + 1 < RW * NH) {
+        const int i1 = (p + 1) / NH, g1 = (p + 1) % NH;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[j] = relu_weighted(mfma_fp4(a[i][grp], bk[j], sa[i][grp], bs[j], zero), wv[i][grp], acc[j]);
-      const float out = reduce_tiles(acc, lane);
-      if (col >= lo[i] && col < hi[i])
-        logits[t * ld + col] = out;
-      else if (clean && col < S)
-        logits[t * ld + col] = neg_inf();
+          d[(p + 1) & 1][j] = mfma_fp4(a[i1][g1], cur.code[j], sa[i1][g1], bs[j], zero);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = relu_weighted(d[p & 1][j], wv[i][grp], grp == 0 ? 0.f : acc[i][j]);
+      if (grp == NH - 1) {
+        const float out = reduce_tiles(acc[i], lane);
+        if (t0 + i < T) {
+          if (col >= lo[i] && col < hi[i])
+            lrow[i][col] = out;
+          else if (clean && col < c_end)
+            lrow[i][col] = neg_inf();
+        }
+      }
     }
   }
 }
@@ -142,11 +173,12 @@ template <int NH, int RW>
 hipError_t launch_cfg(const uint8_t* qv, const uint8_t* qs, const uint8_t* kv, const uint8_t* ksc,
                       const float* w, const int32_t* ks, const int32_t* ke, int64_t T, int64_t S,
                       float* logits, int64_t ld, int clean, hipStream_t stream) {
+  // column indices are int32 inside the kernel (S < 2^31 is checked by the ABI)
   const int64_t n_qb = (T + 4 * RW - 1) / (4 * RW);
   const int64_t n_kc = (S + kKeyChunk - 1) / kKeyChunk;
   const int64_t grid = n_qb * n_kc;
   hipLaunchKernelGGL((logits_prefill_kernel<NH, RW>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     qv, qs, kv, ksc, w, ks, ke, T, S, logits, ld, clean, n_qb, n_kc);
+                     qv, qs, kv, ksc, w, ks, ke, T, (int)S, logits, ld, clean, n_qb, n_kc);
   return hipGetLastError();
 }
 

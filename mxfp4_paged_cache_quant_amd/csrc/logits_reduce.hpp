@@ -7,13 +7,18 @@
 
 namespace mxidx {
 
+// max(x, 0) for a finite float as one integer max: negative values (sign bit
+// set, including -0.0) compare below 0 as int32 and become +0.0.  (A float max
+// would also canonicalize its operand, costing a second instruction.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // acc += sum_i w[i] * max(d[i], 0) over the 4 heads a lane holds in one
 // 16x16 MFMA output tile (heads 4*(lane/16) + i of the 16-head group).
 __device__ __forceinline__ float relu_weighted(const v4f d, const float4 w, float acc) {
-  acc = fmaf(w.x, fmaxf(d[0], 0.0f), acc);
-  acc = fmaf(w.y, fmaxf(d[1], 0.0f), acc);
-  acc = fmaf(w.z, fmaxf(d[2], 0.0f), acc);
-  acc = fmaf(w.w, fmaxf(d[3], 0.0f), acc);
+  acc = fmaf(w.x, relu(d[0]), acc);
+  acc = fmaf(w.y, relu(d[1]), acc);
+  acc = fmaf(w.z, relu(d[2]), acc);
+  acc = fmaf(w.w, relu(d[3]), acc);
   return acc;
 }
 

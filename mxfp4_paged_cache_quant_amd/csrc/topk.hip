@@ -2,49 +2,47 @@
 // "SparseAttnIndexerKpool"; exact sets, as P2 "Validation" tests them).
 //
 // Ranking: value descending, then column ascending; -0.0 == +0.0.  The output
-// holds the min(k, n) selected columns (in column order within each selection
-// stage) followed by -1.
+// holds the min(k, n) selected columns, in column order, followed by -1.
 //
-// Radix select on order-preserving 32-bit keys, one 1024-thread workgroup per
-// row, histograms in LDS:
-//   level 1: bits 31..21 (2048 bins), level 2: bits 20..10 (2048 bins),
-//   level 3: bits 9..0 (1024 bins).
-// Each level finds the bin in which the running count from the top crosses
-// the number still needed; after level 3 the exact k-th key T is known, and a
-// final ordered pass takes every key > T plus the lowest-column keys == T.
-// Order-dependent writes use block-wide prefix sums (never atomics), so the
-// output is deterministic.
+// Radix select on order-preserving 32-bit keys with one workgroup per row
+// (1024 threads for small batches, 512 when there are many rows).  Each level histograms the next (up to) 11-bit digit of the
+// candidate keys in LDS and finds the bin where the running count from the top
+// crosses the number still needed; when the digits are exhausted the exact
+// k-th key T is known, and a final ordered pass takes every key > T plus the
+// lowest-column keys == T.  Ordered writes come from one workgroup prefix sum
+// of per-thread counts (no atomics), so the output is deterministic.
 //
-// Where the row lives during the passes:
-//   * n <= 16384: the keys are cached in LDS on the first (only) HBM read;
-//   * longer rows: a second HBM pass writes the level-1 winners (keys above
-//     the threshold bin) directly and compacts the threshold bin's candidates
-//     (key, column) into LDS; if the bin holds more than 8192 candidates, the
-//     later levels re-read the row from memory and filter by prefix.
+// The row is held in registers, E keys per thread, with every load of a
+// thread issued before any is used (the passes are latency-bound otherwise):
+//   * n <= threads*E: one HBM read.  The key range [kmin, kmax] is reduced first
+//     and the digits are taken from u = key - kmin, starting at the top bit of
+//     kmax - kmin, so the first histogram spreads the row over up to 2048 bins
+//     (fixed top-bit digits would pile similar logits into a few bins);
+//   * longer rows, in chunks of threads*E: a first read histograms bits 31..21,
+//     a second read writes the keys above the threshold bin directly and
+//     compacts the bin's (key, column) pairs into LDS (up to 8192, else the
+//     remaining levels re-read the row filtered by the bin).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mxidx {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kCacheKeys = 16384;            // 64 KB of LDS
-constexpr int kCandPairs = kCacheKeys / 2;   // (key, column) pairs in the same space
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxWaves = kMaxThreads / kWave;
+constexpr int kBins = 2048;
+constexpr int kCandPairs = 8192;   // (key, column) pairs in dynamic LDS (64 KB), long rows only
 
-struct TopkShared {
-  uint32_t hist[2048];
-  uint32_t buf[kCacheKeys];   // cached keys, or candidate keys [0, 8192) + columns [8192, 16384)
-  uint32_t wave_sums[kWaves];
-  int sel[2];                 // selected bin, count strictly above it
+struct Shared {
+  uint32_t hist[kBins];
+  uint32_t wave_tot[2 * kMaxWaves];
+  uint32_t sel[2];                 // selected bin, count strictly above it
 };
 
-__device__ __forceinline__ uint32_t key_of(const float* row, int64_t c) {
-  return f32_key(__float_as_uint(row[c]));
-}
-
-// Exclusive prefix sum over the workgroup (thread order); also returns the total.
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_sums, uint32_t& total) {
+// Exclusive prefix sum over the workgroup in thread order; also returns the total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, Shared& s, uint32_t& total) {
+  constexpr int kWaves = NT / kWave;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   uint32_t x = v;
@@ -53,141 +51,164 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* wave_sums, 
     const uint32_t y = (uint32_t)__shfl_up((int)x, d);
     if (lane >= d) x += y;
   }
-  if (lane == 63) wave_sums[wid] = x;
+  if (lane == 63) s.wave_tot[wid] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    const uint32_t s = wave_sums[i];
-    before += (i < wid) ? s : 0u;
-    tot += s;
+    const uint32_t w = s.wave_tot[i];
+    before += (i < wid) ? w : 0u;
+    tot += w;
   }
   __syncthreads();
   total = tot;
   return before + x - v;
 }
 
-// Finds the bin b (scanning from the top) where the count of keys in bins > b
-// is < need and the count in bins >= b is >= need.  Requires need >= 1 and a
-// histogram total >= need.  Result in s.sel[0] (bin), s.sel[1] (count above).
-__device__ void select_bin(TopkShared& s, int nbins, uint32_t need) {
-  const int t = threadIdx.x;
-  const int b0 = nbins - 1 - 2 * t;
-  const int b1 = b0 - 1;
-  const uint32_t c0 = (b0 >= 0) ? s.hist[b0] : 0u;
-  const uint32_t c1 = (b1 >= 0) ? s.hist[b1] : 0u;
+// Bin b (from the top) with count(bins > b) < need <= count(bins >= b); needs
+// need >= 1 and a histogram total >= need.  s.sel = {b, count above b}.
+template <int NT>
+__device__ void select_bin(Shared& s, uint32_t need) {
+  constexpr int per = kBins / NT;                 // bins per thread, descending
+  const int top = kBins - 1 - per * (int)threadIdx.x;
+  uint32_t c[per];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    c[j] = s.hist[top - j];
+    sum += c[j];
+  }
   uint32_t total;
-  const uint32_t before = block_scan(c0 + c1, s.wave_sums, total);
-  if (b0 >= 0 && before < need && before + c0 >= need) {
-    s.sel[0] = b0;
-    s.sel[1] = (int)before;
-  }
-  if (b1 >= 0 && before + c0 < need && before + c0 + c1 >= need) {
-    s.sel[0] = b1;
-    s.sel[1] = (int)(before + c0);
-  }
-  __syncthreads();
-}
-
-__device__ __forceinline__ void clear_hist(TopkShared& s) {
-  for (int i = threadIdx.x; i < 2048; i += kThreads) s.hist[i] = 0;
-  __syncthreads();
-}
-
-// Candidate sources.  get(i, key, col) returns false when item i is not part
-// of the current candidate set.
-struct CachedRow {     // all n keys of the row in LDS, column = lo + i
-  const uint32_t* keys;
-  int64_t lo;
-  __device__ bool get(int64_t i, uint32_t& key, int64_t& col) const {
-    key = keys[i];
-    col = lo + i;
-    return true;
-  }
-};
-struct CandPairs {     // compacted (key, column) pairs of the level-1 bin, in column order
-  const uint32_t* keys;
-  const uint32_t* cols;
-  __device__ bool get(int64_t i, uint32_t& key, int64_t& col) const {
-    key = keys[i];
-    col = (int64_t)cols[i];
-    return true;
-  }
-};
-struct GlobalRow {     // re-read from memory, keeping keys of the level-1 bin
-  const float* row;
-  int64_t lo;
-  uint32_t bin1;
-  __device__ bool get(int64_t i, uint32_t& key, int64_t& col) const {
-    key = key_of(row, lo + i);
-    col = lo + i;
-    return (key >> 21) == bin1;
-  }
-};
-
-// Levels 2 and 3 on a candidate source; returns the exact threshold key and
-// the number of keys equal to it that must still be taken.
-template <typename Src>
-__device__ void refine(TopkShared& s, const Src& src, int64_t count, uint32_t bin1, uint32_t need2,
-                       uint32_t& thresh, uint32_t& need_ties) {
-  clear_hist(s);
-  for (int64_t i = threadIdx.x; i < count; i += kThreads) {
-    uint32_t key;
-    int64_t col;
-    if (src.get(i, key, col) && (key >> 21) == bin1) atomicAdd(&s.hist[(key >> 10) & 2047u], 1u);
-  }
-  __syncthreads();
-  select_bin(s, 2048, need2);
-  const uint32_t bin2 = (uint32_t)s.sel[0];
-  const uint32_t need3 = need2 - (uint32_t)s.sel[1];
-  const uint32_t prefix = (bin1 << 11) | bin2;
-  __syncthreads();
-  clear_hist(s);
-  for (int64_t i = threadIdx.x; i < count; i += kThreads) {
-    uint32_t key;
-    int64_t col;
-    if (src.get(i, key, col) && (key >> 10) == prefix) atomicAdd(&s.hist[key & 1023u], 1u);
-  }
-  __syncthreads();
-  select_bin(s, 1024, need3);
-  thresh = (prefix << 10) | (uint32_t)s.sel[0];
-  need_ties = need3 - (uint32_t)s.sel[1];
-  __syncthreads();
-}
-
-// Ordered final pass: writes every candidate with key > thresh (restricted to
-// the level-1 bin when only_bin1) and the first need_ties candidates with
-// key == thresh, at out[base + rank in candidate order].
-template <typename Src>
-__device__ void emit(TopkShared& s, const Src& src, int64_t count, uint32_t thresh,
-                     uint32_t need_ties, bool only_bin1, uint32_t bin1, int32_t* out,
-                     uint32_t base, int k) {
-  uint32_t gt_base = 0, tie_base = 0;
-  for (int64_t c0 = 0; c0 < count; c0 += kThreads) {
-    const int64_t i = c0 + threadIdx.x;
-    uint32_t key = 0;
-    int64_t col = 0;
-    bool gt = false, tie = false;
-    if (i < count && src.get(i, key, col) && (!only_bin1 || (key >> 21) == bin1)) {
-      gt = key > thresh;
-      tie = key == thresh;
+  uint32_t run = block_scan<NT>(sum, s, total);
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    if (run < need && run + c[j] >= need) {
+      s.sel[0] = (uint32_t)(top - j);
+      s.sel[1] = run;
     }
-    uint32_t total;
-    const uint32_t pre = block_scan((gt ? 1u : 0u) | (tie ? 0x10000u : 0u), s.wave_sums, total);
-    const uint32_t gt_pre = gt_base + (pre & 0xffffu);
-    const uint32_t tie_pre = tie_base + (pre >> 16);
-    const uint32_t pos = base + gt_pre + min(tie_pre, need_ties);
-    if ((gt || (tie && tie_pre < need_ties)) && pos < (uint32_t)k) out[pos] = (int32_t)col;
-    gt_base += total & 0xffffu;
-    tie_base += total >> 16;
+    run += c[j];
+  }
+  __syncthreads();
+}
+
+template <int NT>
+__device__ __forceinline__ void clear_hist(Shared& s) {
+  for (int i = threadIdx.x; i < kBins; i += NT) s.hist[i] = 0;
+  __syncthreads();
+}
+
+// Keys E*t + e (e < E) of the segment src[0, n) into thread t's registers;
+// returns how many are valid.  All loads are issued before any is used.
+template <int E>
+__device__ __forceinline__ int load_keys(const float* __restrict__ src, int64_t n, bool vec,
+                                         uint32_t (&key)[E]) {
+  const int64_t first = (int64_t)E * threadIdx.x;
+  const int nv = (int)max((int64_t)0, min((int64_t)E, n - first));
+  if (vec && nv == E) {
+    uint4 v[E / 4];
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) v[q] = *reinterpret_cast<const uint4*>(src + first + 4 * q);
+#pragma unroll
+    for (int q = 0; q < E / 4; ++q) {
+      key[4 * q + 0] = f32_key(v[q].x);
+      key[4 * q + 1] = f32_key(v[q].y);
+      key[4 * q + 2] = f32_key(v[q].z);
+      key[4 * q + 3] = f32_key(v[q].w);
+    }
+  } else {
+    uint32_t raw[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) raw[e] = (e < nv) ? __float_as_uint(src[first + e]) : 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) key[e] = f32_key(raw[e]);
+  }
+  return nv;
+}
+
+// One radix level over register-held keys: u = key - kmin; candidates have
+// u >> shift == prefix (all when shift >= 32); digit = the bits from shift-1
+// down to nsh.
+template <int E>
+__device__ __forceinline__ void hist_level(Shared& s, const uint32_t (&key)[E], int nv, uint32_t kmin,
+                                           int shift, uint32_t prefix, int nsh, uint32_t dmask) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t u = key[e] - kmin;
+    if (e < nv && (shift >= 32 || (u >> shift) == prefix)) atomicAdd(&s.hist[(u >> nsh) & dmask], 1u);
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ logits, int64_t ld,
-                                                        const int32_t* __restrict__ ks,
-                                                        const int32_t* __restrict__ ke, int k,
-                                                        int32_t* __restrict__ out_idx) {
-  __shared__ TopkShared s;
+// Levels from `shift` down to bit 0 on register-held keys.  Returns u_t (the
+// exact threshold, as key - kmin) and how many keys equal to it to take.
+template <int NT, int E>
+__device__ void refine_regs(Shared& s, const uint32_t (&key)[E], int nv, uint32_t kmin, int shift,
+                            uint32_t prefix, uint32_t need, uint32_t& u_t, uint32_t& need_ties) {
+  while (shift > 0) {
+    const int nsh = shift > 11 ? shift - 11 : 0;
+    const uint32_t dmask = (1u << (shift - nsh)) - 1u;
+    clear_hist<NT>(s);
+    hist_level(s, key, nv, kmin, shift, prefix, nsh, dmask);
+    __syncthreads();
+    select_bin<NT>(s, need);
+    need -= s.sel[1];
+    prefix = (prefix << (shift - nsh)) | s.sel[0];
+    shift = nsh;
+    __syncthreads();
+  }
+  u_t = prefix;
+  need_ties = need;
+}
+
+// Ordered output of register-held candidates (thread t holds consecutive
+// candidates, so thread order is candidate order): every u > u_t, and the
+// first need_ties with u == u_t, at out[base + rank].  gt_run / tie_run carry
+// the counts of earlier chunks and are advanced by this chunk's totals.
+template <int NT, bool kCols, int E>
+__device__ __forceinline__ void emit_regs(Shared& s, const uint32_t (&key)[E],
+                                          const uint32_t (&cols)[E], int64_t col0, int nv,
+                                          uint32_t kmin, uint32_t u_t,
+                                          uint32_t need_ties, bool filt, uint32_t bin1,
+                                          int32_t* __restrict__ out, uint32_t base, int k,
+                                          uint32_t& gt_run, uint32_t& tie_run) {
+  uint32_t cg = 0, ct = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t u = key[e] - kmin;
+    const bool ok = e < nv && (!filt || (key[e] >> 21) == bin1);
+    cg += (ok && u > u_t) ? 1u : 0u;
+    ct += (ok && u == u_t) ? 1u : 0u;
+  }
+  uint32_t total;
+  const uint32_t pre = block_scan<NT>(cg | (ct << 16), s, total);
+  uint32_t g = gt_run + (pre & 0xffffu);
+  uint32_t t = tie_run + (pre >> 16);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t u = key[e] - kmin;
+    const bool ok = e < nv && (!filt || (key[e] >> 21) == bin1);
+    const int64_t col = kCols ? (int64_t)cols[e] : col0 + e;
+    if (ok && u > u_t) {
+      const uint32_t pos = base + g + min(t, need_ties);
+      if (pos < (uint32_t)k) out[pos] = (int32_t)col;
+      ++g;
+    } else if (ok && u == u_t) {
+      if (t < need_ties && base + g + t < (uint32_t)k) out[base + g + t] = (int32_t)col;
+      ++t;
+    }
+  }
+  gt_run += total & 0xffffu;
+  tie_run += total >> 16;
+}
+
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logits, int64_t ld,
+                                                  const int32_t* __restrict__ ks,
+                                                  const int32_t* __restrict__ ke, int k,
+                                                  int32_t* __restrict__ out_idx) {
+  constexpr int kWaves = NT / kWave;
+  constexpr int64_t C = (int64_t)NT * E;          // keys held per pass
+  __shared__ Shared s;
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];   // long rows only
   const int64_t r = blockIdx.x;
   const float* row = logits + r * ld;
   int32_t* out = out_idx + r * (int64_t)k;
@@ -196,80 +217,200 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const int64_t n = hi > lo ? hi - lo : 0;
 
   if (n <= k) {
-    for (int i = threadIdx.x; i < k; i += kThreads) out[i] = (i < n) ? (int32_t)(lo + i) : -1;
+    for (int i = threadIdx.x; i < k; i += NT) out[i] = (i < n) ? (int32_t)(lo + i) : -1;
+    return;
+  }
+  const float* src = row + lo;
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+
+  if (n <= C) {
+    // ---- the whole row in registers: one read ----
+    uint32_t key[E];
+    const int nv = load_keys<E>(src, n, vec, key);
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (e < nv) {
+        kmin = min(kmin, key[e]);
+        kmax = max(kmax, key[e]);
+      }
+    for (int d = 32; d >= 1; d >>= 1) {
+      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
+      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
+    }
+    if (lane == 0) {
+      s.wave_tot[wid] = kmin;
+      s.wave_tot[kWaves + wid] = kmax;
+    }
+    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+      kmin = min(kmin, s.wave_tot[w]);
+      kmax = max(kmax, s.wave_tot[kWaves + w]);
+    }
+    __syncthreads();
+    const uint32_t range = kmax - kmin;
+    const int L = range ? 32 - __clz(range) : 0;     // bit length of the key range
+    uint32_t u_t = 0, need_ties = (uint32_t)k;        // all keys equal: the lowest columns
+    if (L > 0) refine_regs<NT>(s, key, nv, kmin, L, 0u, (uint32_t)k, u_t, need_ties);
+    uint32_t gr = 0, tr = 0;
+    emit_regs<NT, false>(s, key, key, lo + (int64_t)E * threadIdx.x, nv, kmin, u_t, need_ties,
+                         false, 0u, out, 0u, k, gr, tr);
     return;
   }
 
-  // Level 1 (bits 31..21), first read of the row.
-  clear_hist(s);
-  const bool cached = n <= kCacheKeys;
-  for (int64_t i = threadIdx.x; i < n; i += kThreads) {
-    const uint32_t key = key_of(row, lo + i);
-    if (cached) s.buf[i] = key;
-    atomicAdd(&s.hist[key >> 21], 1u);
+  // ---- long row, chunks of C keys ----
+  // Pass 1: level-1 histogram of bits 31..21.  Workgroups of <= 8 waves keep
+  // one histogram per wave (fewer colliding LDS atomics), merged afterwards.
+  constexpr bool kWaveHist = kWaves <= 8;
+  uint32_t* wh = kWaveHist ? dyn + wid * kBins : s.hist;
+  if (kWaveHist) {
+    for (int i = lane; i < kBins; i += kWave) wh[i] = 0;
+    __syncthreads();
+  } else {
+    clear_hist<NT>(s);
+  }
+  for (int64_t c0 = 0; c0 < n; c0 += C) {
+    uint32_t key[E];
+    const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (e < nv) atomicAdd(&wh[key[e] >> 21], 1u);
   }
   __syncthreads();
-  select_bin(s, 2048, (uint32_t)k);
-  const uint32_t bin1 = (uint32_t)s.sel[0];
-  const uint32_t above1 = (uint32_t)s.sel[1];
-  const uint32_t m = s.hist[bin1];
-  __syncthreads();
-
-  uint32_t thresh, need_ties;
-  if (cached) {
-    const CachedRow src{s.buf, lo};
-    refine(s, src, n, bin1, (uint32_t)k - above1, thresh, need_ties);
-    emit(s, src, n, thresh, need_ties, false, bin1, out, 0u, k);
-    return;
-  }
-
-  // Long row: second read writes the keys above bin1 and compacts bin1.
-  const bool fits = m <= (uint32_t)kCandPairs;
-  uint32_t* cand_keys = s.buf;
-  uint32_t* cand_cols = s.buf + kCandPairs;
-  {
-    uint32_t above_base = 0, cand_base = 0;
-    for (int64_t c0 = 0; c0 < n; c0 += kThreads) {
-      const int64_t i = c0 + threadIdx.x;
-      bool gt = false, eq = false;
-      uint32_t key = 0;
-      if (i < n) {
-        key = key_of(row, lo + i);
-        gt = (key >> 21) > bin1;
-        eq = (key >> 21) == bin1;
-      }
-      uint32_t total;
-      const uint32_t pre = block_scan((gt ? 1u : 0u) | (eq ? 0x10000u : 0u), s.wave_sums, total);
-      const uint32_t pos = above_base + (pre & 0xffffu);
-      if (gt && pos < (uint32_t)k) out[pos] = (int32_t)(lo + i);
-      if (eq && fits) {
-        const uint32_t p = min(cand_base + (pre >> 16), (uint32_t)(kCandPairs - 1));
-        cand_keys[p] = key;
-        cand_cols[p] = (uint32_t)(lo + i);
-      }
-      above_base += total & 0xffffu;
-      cand_base += total >> 16;
+  if (kWaveHist) {
+    for (int b = threadIdx.x; b < kBins; b += NT) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) c += dyn[w * kBins + b];
+      s.hist[b] = c;
     }
     __syncthreads();
   }
-  if (fits) {
-    const CandPairs src{cand_keys, cand_cols};
-    refine(s, src, (int64_t)m, bin1, (uint32_t)k - above1, thresh, need_ties);
-    emit(s, src, (int64_t)m, thresh, need_ties, true, bin1, out, above1, k);
-  } else {
-    const GlobalRow src{row, lo, bin1};
-    refine(s, src, n, bin1, (uint32_t)k - above1, thresh, need_ties);
-    emit(s, src, n, thresh, need_ties, true, bin1, out, above1, k);
+  select_bin<NT>(s, (uint32_t)k);
+  const uint32_t bin1 = s.sel[0];
+  const uint32_t above1 = s.sel[1];
+  const uint32_t m = s.hist[bin1];
+  __syncthreads();                          // per-wave histograms are dead from here
+  const bool fits = m <= (uint32_t)kCandPairs;
+  uint32_t* cand_keys = dyn;
+  uint32_t* cand_cols = dyn + kCandPairs;
+  {
+    // Pass 2: keys above bin1 go straight out; bin1's keys become candidates.
+    uint32_t gbase = 0, cbase = 0;
+    for (int64_t c0 = 0; c0 < n; c0 += C) {
+      uint32_t key[E];
+      const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+      uint32_t cg = 0, cq = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        cg += (e < nv && (key[e] >> 21) > bin1) ? 1u : 0u;
+        cq += (e < nv && (key[e] >> 21) == bin1) ? 1u : 0u;
+      }
+      uint32_t total;
+      const uint32_t pre = block_scan<NT>(cg | (cq << 16), s, total);
+      uint32_t g = gbase + (pre & 0xffffu), q = cbase + (pre >> 16);
+      const int64_t col0 = lo + c0 + (int64_t)E * threadIdx.x;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (e >= nv) continue;
+        const uint32_t b = key[e] >> 21;
+        if (b > bin1) {
+          if (g < (uint32_t)k) out[g] = (int32_t)(col0 + e);
+          ++g;
+        } else if (b == bin1) {
+          if (fits && q < (uint32_t)kCandPairs) {
+            cand_keys[q] = key[e];
+            cand_cols[q] = (uint32_t)(col0 + e);
+          }
+          ++q;
+        }
+      }
+      gbase += total & 0xffffu;
+      cbase += total >> 16;
+    }
+    __syncthreads();
   }
+  uint32_t u_t, need_ties;
+  if (fits) {
+    // candidates back into registers, consecutive per thread
+    constexpr int E2 = kCandPairs / NT;
+    uint32_t key[E2], cols[E2];
+    const int first = E2 * threadIdx.x;
+    const int nv = max(0, min(E2, (int)m - first));
+#pragma unroll
+    for (int e = 0; e < E2; ++e) {
+      key[e] = (e < nv) ? cand_keys[first + e] : 0u;
+      cols[e] = (e < nv) ? cand_cols[first + e] : 0u;
+    }
+    refine_regs<NT>(s, key, nv, 0u, 21, bin1, (uint32_t)k - above1, u_t, need_ties);
+    uint32_t gr = 0, tr = 0;
+    emit_regs<NT, true>(s, key, cols, 0, nv, 0u, u_t, need_ties, false, bin1, out, above1, k, gr, tr);
+    return;
+  }
+  // more than 8192 keys in the threshold bin: the remaining levels re-read the row
+  uint32_t need = (uint32_t)k - above1, prefix = bin1;
+  for (int shift = 21; shift > 0;) {
+    const int nsh = shift > 11 ? shift - 11 : 0;
+    const uint32_t dmask = (1u << (shift - nsh)) - 1u;
+    clear_hist<NT>(s);
+    for (int64_t c0 = 0; c0 < n; c0 += C) {
+      uint32_t key[E];
+      const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+      hist_level(s, key, nv, 0u, shift, prefix, nsh, dmask);
+    }
+    __syncthreads();
+    select_bin<NT>(s, need);
+    need -= s.sel[1];
+    prefix = (prefix << (shift - nsh)) | s.sel[0];
+    shift = nsh;
+    __syncthreads();
+  }
+  u_t = prefix;
+  need_ties = need;
+  uint32_t gr = 0, tr = 0;
+  for (int64_t c0 = 0; c0 < n; c0 += C) {
+    uint32_t key[E];
+    const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+    emit_regs<NT, false>(s, key, key, lo + c0 + (int64_t)E * threadIdx.x, nv, 0u, u_t, need_ties,
+                         true, bin1, out, above1, k, gr, tr);
+  }
+}
+
+template <int NT, int E>
+hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
+                      const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {
+  const bool long_rows = ld > (int64_t)NT * E;
+  // 64 KB: candidate pairs, or first the per-wave histograms (<= 8 x 8 KB)
+  const size_t dyn = long_rows ? (size_t)kCandPairs * 2 * sizeof(uint32_t) : 0;
+  if (long_rows) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<NT, E>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+      attr_set = true;
+    }
+  }
+  hipLaunchKernelGGL((topk_kernel<NT, E>), dim3((unsigned)rows), dim3(NT), dyn, stream, logits, ld,
+                     ks, ke, k, out_idx);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_topk(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                        const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)rows), dim3(kThreads), 0, stream, logits, ld, ks,
-                     ke, k, out_idx);
-  return hipGetLastError();
+  // Few rows: 1024 threads per row (the row's latency is the step's); many
+  // rows: 512 threads per row, two rows per CU.  Keys per thread: the smallest
+  // size that holds a full row in one pass (up to 16).
+  if (rows < 512) {
+    if (ld <= 4 * 1024) return launch_cfg<1024, 4>(logits, rows, ld, ks, ke, k, out_idx, stream);
+    if (ld <= 8 * 1024) return launch_cfg<1024, 8>(logits, rows, ld, ks, ke, k, out_idx, stream);
+    return launch_cfg<1024, 16>(logits, rows, ld, ks, ke, k, out_idx, stream);
+  }
+  if (ld <= 8 * 512) return launch_cfg<512, 8>(logits, rows, ld, ks, ke, k, out_idx, stream);
+  return launch_cfg<512, 16>(logits, rows, ld, ks, ke, k, out_idx, stream);
 }
 
 }  // namespace mxidx

@@ -89,3 +89,22 @@ def test_topk_deterministic_across_runs():
     a = host(mx.topk(x, None, ke, 2048))
     b = host(mx.topk(x, None, ke, 2048))
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("rows,n,k", [(600, 3000, 2048), (520, 20000, 2048), (512, 9000, 100)])
+def test_topk_many_rows(rows, n, k):
+    # 512 or more rows select the many-rows launch shape (512-thread workgroups)
+    rng = np.random.default_rng(rows + n)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    x[::3] = np.round(x[::3] * 8) / 8
+    ks = rng.integers(0, n // 4, rows).astype(np.int32)
+    ke = (n - rng.integers(0, n // 4, rows)).astype(np.int32)
+    _check(x, ks, ke, k)
+
+
+def test_topk_many_rows_wide_threshold_bin():
+    rng = np.random.default_rng(6)
+    rows, n, k = 512, 40000, 2048
+    bits = np.float32(1.5).view(np.uint32) + rng.integers(0, 1 << 20, size=(rows, n)).astype(np.uint32)
+    x = bits.view(np.float32).copy()
+    _check(x, np.zeros(rows, np.int32), np.full(rows, n, np.int32), k)
