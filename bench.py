@@ -50,6 +50,12 @@ def parse():
     ap.add_argument("--prefill", choices=["chunk", "none"], default="chunk")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context decode and long prefill measurements")
+    ap.add_argument("--only", choices=["decode", "prefill", "long_decode", "long_prefill", "copy"],
+                    help="run one section only and print its result (for profiler runs)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch kernels directly instead of replaying HIP graphs")
+    ap.add_argument("--pmc-summarize", nargs=2, metavar=("PMC_DIR", "SECTION"),
+                    help="write profiles/pmc_bytes_SECTION.json from rocprofv3 counter runs")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -114,8 +120,22 @@ def decode_ops(case):
     }
 
 
+EAGER = False          # --eager: launch directly instead of through HIP graphs (profiler runs)
+
+
+class _Eager:
+    def __init__(self, fns):
+        self.fns = list(fns)
+
+    def replay(self):
+        for fn in self.fns:
+            fn()
+
+
 def capture(fn_list):
     import torch
+    if EAGER:
+        return _Eager(fn_list)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for fn in fn_list:
@@ -307,6 +327,36 @@ def bench_long_prefill():
     }
 
 
+def bench_copy(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size: the HBM rate torch's copy kernel reaches,
+    and the reference for scaling the profiler's byte counters."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    stop.record()
+    stop.synchronize()
+    us = start.elapsed_time(stop) / reps * 1e3
+    # read-only reference: a torch reduction over the same bytes
+    src.sum()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        src.sum()
+    stop.record()
+    stop.synchronize()
+    us_r = start.elapsed_time(stop) / reps * 1e3
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "us": round(us, 1),
+            "gbs": round(2 * nbytes / us / 1e3, 1),
+            "read_only_sum_us": round(us_r, 1), "read_only_gbs": round(nbytes / us_r / 1e3, 1)}
+
+
 def cpu_baseline(case, seconds):
     """The oracle (never tuned for this) on a bounded sample of the decode step."""
     import numpy as np
@@ -344,8 +394,101 @@ def cpu_baseline(case, seconds):
                       f"{t_total:.1f} s of CPU time"}
 
 
+# ---------------------------------------------------------------------------
+# HBM traffic from rocprofv3 byte counters
+# ---------------------------------------------------------------------------
+
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {          # kernel-name prefix -> the source it is compiled from
+    "logits_paged_kernel": "logits_paged.hip",
+    "logits_prefill_kernel": "logits_prefill.hip",
+    "topk_kernel": "topk.hip",
+    "mxfp4_rows_kernel": "insert.hip",
+    "gather_kernel": "gather.hip",
+}
+
+
+def _source_hash(kernel):
+    import hashlib
+    for prefix, src in KERNEL_SOURCES.items():
+        if kernel.startswith(prefix):
+            path = os.path.join(ROOT, "mxfp4_paged_cache_quant_amd", "csrc", src)
+            h = hashlib.sha256(open(path, "rb").read())
+            for common in ("common.hpp", "logits_reduce.hpp"):
+                h.update(open(os.path.join(os.path.dirname(path), common), "rb").read())
+            return h.hexdigest()[:16]
+    return None
+
+
+def _short(name):
+    name = name.replace("mxidx::(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0]
+
+
+def _mean_counter(csv_path):
+    import csv
+    import collections
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(csv_path)):
+        agg[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def pmc_summarize(root, section):
+    """Turn the FETCH_SIZE / WRITE_SIZE runs of `section` (and of the plain copy)
+    into profiles/pmc_bytes_<section>.json: bytes per dispatch per kernel,
+    scaled by what the counters read for a copy of known size."""
+    def run(sec, ctr):
+        return _mean_counter(os.path.join(root, f"{sec}_{ctr}", "run_counter_collection.csv"))
+    copy_f = run("copy", "FETCH_SIZE")["__amd_rocclr_copyBuffer"]
+    copy_w = run("copy", "WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    nbytes = 1 << 30
+    f_scale = nbytes / (copy_f * 1024.0)           # bytes per counted KiB, reads
+    w_scale = nbytes / (copy_w * 1024.0)
+    fetch, write = run(section, "FETCH_SIZE"), run(section, "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(fetch) & set(write)):
+        src = _source_hash(k)
+        if src is None:
+            continue
+        kernels[k] = {"fetch_kib": round(fetch[k], 1), "write_kib": round(write[k], 1),
+                      "read_bytes": round(fetch[k] * 1024 * f_scale),
+                      "write_bytes": round(write[k] * 1024 * w_scale),
+                      "traffic_bytes": round(fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale),
+                      "source_sha256_16": src}
+    out = {"section": section,
+           "commands": [f"rocprofv3 --pmc {c} -f csv -d <dir>/{sec}_{c} -o run -- python3 bench.py "
+                        f"--only {sec} --eager" for sec in ("copy", section)
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")],
+           "calibration": {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
+                           "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+                           "read_bytes_per_counted_kib": f_scale * 1024,
+                           "write_bytes_per_counted_kib": w_scale * 1024},
+           "kernels": kernels}
+    path = os.path.join(PROFILES, f"pmc_bytes_{section}.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    return path
+
+
+def measured_traffic(section, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel's source changed since."""
+    path = os.path.join(PROFILES, f"pmc_bytes_{section}.json")
+    if not os.path.exists(path):
+        return None
+    data = json.load(open(path))
+    for k, v in data["kernels"].items():
+        if k.startswith(kernel) and v["source_sha256_16"] == _source_hash(k):
+            return v["traffic_bytes"]
+    return None
+
+
 def main():
     args = parse()
+    if args.pmc_summarize:
+        print(pmc_summarize(*args.pmc_summarize))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the MXFP4 indexer path has no multi-GPU mode in this "
@@ -360,6 +503,14 @@ def main():
 
     torch.cuda.set_device(0)
     mx.init(0)
+    global EAGER
+    EAGER = args.eager
+    if args.only is not None:
+        section = {"prefill": lambda: bench_prefill(args), "long_decode": bench_long_decode,
+                   "long_prefill": bench_long_prefill, "copy": bench_copy}
+        if args.only in section:
+            print(json.dumps({"section": args.only, "result": section[args.only]()}), flush=True)
+            return
     case = workloads.paged_decode()
     log(f"[bench] decode workload {case['name']}: building {args.sets} rotating sets")
     elapsed, per_kernel = bench_decode(args, case)
@@ -377,12 +528,20 @@ def main():
     }
     dominant = max(per_kernel, key=per_kernel.get)
     achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-6) / 1e9
+    dom_kernel = {"insert": "mxfp4_rows_kernel<Bf16In, true>", "quantize": "mxfp4_rows_kernel<Bf16In, false>",
+                  "logits_paged": "logits_paged_kernel", "topk": "topk_kernel"}[dominant]
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "alg_bytes_per_launch": alg_bytes[dominant],
+                "traffic": measured_traffic("decode", dom_kernel),
+                "alg_bytes_per_launch": alg_bytes[dominant],
                 "avg_launch_us": round(per_kernel[dominant], 3)}
     kernels = {k: {"avg_us": round(v, 3), "alg_bytes": alg_bytes[k],
                    "gbs": round(alg_bytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in per_kernel.items()}
+
+    if args.only == "decode":
+        print(json.dumps({"section": "decode", "us_per_step": round(ms_per_step * 1e3, 3),
+                          "kernels_us": per_kernel}), flush=True)
+        return
 
     prefill = None
     if args.prefill == "chunk":
@@ -400,6 +559,9 @@ def main():
         long_prefill = bench_long_prefill()
         log(f"[bench] long prefill: {long_prefill}")
         torch.cuda.empty_cache()
+
+    copy = bench_copy()
+    log(f"[bench] device copy: {copy}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -428,6 +590,7 @@ def main():
         "prefill": prefill,
         "long_decode": long_decode,
         "long_prefill": long_prefill,
+        "device_copy": copy,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -83,6 +83,7 @@ typedef enum { IDX_BF16 = 0, IDX_F32 = 1 } idx_dtype;
 #define IDX_PAGE_SIZE 64
 #define IDX_MAX_HEADS 128
 #define IDX_TOPK_MAX 2048
+#define IDX_MAX_DECODE_SEQS 65535
 
 /* Version of this ABI (major * 100 + minor). */
 int idx_version(void);
@@ -170,7 +171,10 @@ int idx_logits_prefill(const uint8_t* q_values, const uint8_t* q_scales,
  *   logits [B*next_n, logits_row_stride] fp32 out, logits_row_stride >= max_context_len.
  *   clean != 0: columns of [0, max_context_len) that a row does not score
  *   are set to -inf; clean == 0: they are left untouched.
- * page_size must be 64; H a multiple of 16 in [16, 128]; next_n in [1, 16]. */
+ * page_size must be 64; H a multiple of 16 in [16, 128]; next_n in [1, 16];
+ * 1 <= B <= IDX_MAX_DECODE_SEQS; num_pages >= 1; B * ceil(max_context_len / 64)
+ * < 2^31.  Pages whose block-table entry lies outside [0, num_pages) are
+ * skipped (their logits are not written). */
 int idx_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
                      const float* weights, const uint8_t* cache, int64_t num_pages,
                      int page_size, const int32_t* block_table, int64_t bt_row_stride,

@@ -146,12 +146,15 @@ int idx_logits_paged(const uint8_t* q_values, const uint8_t* q_scales, const flo
                      const int32_t* context_lens, int B, int next_n, int H,
                      int64_t max_context_len, float* logits, int64_t logits_row_stride, int clean,
                      hipStream_t stream) {
-  if (page_size != IDX_PAGE_SIZE || num_pages < 0 || B < 0 || B > 65535 || next_n < 1 ||
-      next_n > 16 || !heads_ok(H) || max_context_len < 0)
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0 || B < 0 || B > IDX_MAX_DECODE_SEQS ||
+      next_n < 1 || next_n > 16 || !heads_ok(H) || max_context_len < 0 ||
+      max_context_len > 0x7fffffffLL - IDX_PAGE_SIZE)
     return IDX_ERR_ARG;
   if (B == 0 || max_context_len == 0) return IDX_OK;
   const int64_t pages_per_seq = (max_context_len + IDX_PAGE_SIZE - 1) / IDX_PAGE_SIZE;
-  if (bt_row_stride < pages_per_seq || logits_row_stride < max_context_len) return IDX_ERR_ARG;
+  if (bt_row_stride < pages_per_seq || logits_row_stride < max_context_len || num_pages < 1 ||
+      (int64_t)B * pages_per_seq > 0x7fffffffLL)
+    return IDX_ERR_ARG;
   if (!q_values || !aligned(q_values, 16) || !q_scales || !weights || !aligned(weights, 16) ||
       !cache || !aligned(cache, 16) || !block_table || !context_lens || !logits ||
       !aligned(logits, 4))

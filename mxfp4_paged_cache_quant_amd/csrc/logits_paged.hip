@@ -57,13 +57,18 @@ __global__ __launch_bounds__(256) void logits_paged_kernel(
   if (page < 0 || page >= num_pages) return;
   const uint8_t* pbase = cache + page * kPageBytes;
 
+  // the cache streams through once per call: non-temporal loads
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   uint4 bk[4];
   int bs[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tk = 16 * j + n;
-    bk[j] = *reinterpret_cast<const uint4*>(pbase + tk * kCodeBytes + g * 16);
-    const uint32_t s4 = *reinterpret_cast<const uint32_t*>(pbase + kPageCodeBytes + tk * kScaleBytes);
+    const u32x4 c = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(pbase + tk * kCodeBytes + g * 16));
+    bk[j] = make_uint4(c.x, c.y, c.z, c.w);
+    const uint32_t s4 = __builtin_nontemporal_load(
+        reinterpret_cast<const uint32_t*>(pbase + kPageCodeBytes + tk * kScaleBytes));
     bs[j] = (int)((s4 >> (8 * g)) & 0xffu);
     if (tok0 + tk >= L) {        // unwritten slots past the context: neutral operands
       bk[j] = make_uint4(0, 0, 0, 0);

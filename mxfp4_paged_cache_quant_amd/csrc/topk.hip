@@ -4,24 +4,26 @@
 // Ranking: value descending, then column ascending; -0.0 == +0.0.  The output
 // holds the min(k, n) selected columns, in column order, followed by -1.
 //
-// Radix select on order-preserving 32-bit keys with one workgroup per row
-// (1024 threads for small batches, 512 when there are many rows).  Each level histograms the next (up to) 11-bit digit of the
-// candidate keys in LDS and finds the bin where the running count from the top
-// crosses the number still needed; when the digits are exhausted the exact
-// k-th key T is known, and a final ordered pass takes every key > T plus the
-// lowest-column keys == T.  Ordered writes come from one workgroup prefix sum
-// of per-thread counts (no atomics), so the output is deterministic.
+// Radix select on order-preserving 32-bit keys with 11-bit digits and one
+// workgroup per row (1024 threads for small batches, 512 threads when there
+// are many rows).  Each level histograms the next digit of
+// the candidate keys in LDS and finds the bin where the running count from
+// the top crosses the number still needed; when the digits are exhausted the
+// exact k-th key T is known, and a final ordered pass takes every key > T plus
+// the lowest-column keys == T.  Ordered writes come from one workgroup prefix
+// sum of per-thread counts (no atomics), so the output is deterministic.  A
+// level costs three barriers: histogram complete, scan totals, selection.
 //
 // The row is held in registers, E keys per thread, with every load of a
 // thread issued before any is used (the passes are latency-bound otherwise):
-//   * n <= threads*E: one HBM read.  The key range [kmin, kmax] is reduced first
-//     and the digits are taken from u = key - kmin, starting at the top bit of
-//     kmax - kmin, so the first histogram spreads the row over up to 2048 bins
+//   * n <= threads*E: one HBM read.  The key range [kmin, kmax] is reduced
+//     first and the digits are taken from u = key - kmin, starting at the top
+//     bit of kmax - kmin, so the first histogram spreads the row over the bins
 //     (fixed top-bit digits would pile similar logits into a few bins);
-//   * longer rows, in chunks of threads*E: a first read histograms bits 31..21,
-//     a second read writes the keys above the threshold bin directly and
-//     compacts the bin's (key, column) pairs into LDS (up to 8192, else the
-//     remaining levels re-read the row filtered by the bin).
+//   * longer rows, in chunks of threads*E: a first read histograms the top
+//     digit of the keys, a second read writes the keys above the threshold bin
+//     directly and compacts the bin's (key, column) pairs into LDS (up to
+//     8192, else the remaining levels re-read the row filtered by the bin).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -30,18 +32,21 @@ namespace {
 
 constexpr int kMaxThreads = 1024;
 constexpr int kMaxWaves = kMaxThreads / kWave;
-constexpr int kBins = 2048;
 constexpr int kCandPairs = 8192;   // (key, column) pairs in dynamic LDS (64 KB), long rows only
+constexpr int kWaveHistBins = 2048;
 
+template <int BINS>
 struct Shared {
-  uint32_t hist[kBins];
-  uint32_t wave_tot[2 * kMaxWaves];
-  uint32_t sel[2];                 // selected bin, count strictly above it
+  uint32_t hist[BINS];
+  uint32_t wave_tot[2][2 * kMaxWaves];  // ping-pong: consecutive scans need one barrier each
+  uint32_t sel[2];                      // selected bin, count strictly above it
 };
 
-// Exclusive prefix sum over the workgroup in thread order; also returns the total.
-template <int NT>
-__device__ __forceinline__ uint32_t block_scan(uint32_t v, Shared& s, uint32_t& total) {
+// Exclusive prefix sum over the workgroup in thread order; also returns the
+// total.  One barrier; consecutive calls must alternate `parity`.
+template <int NT, int BINS>
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, Shared<BINS>& s, int parity,
+                                               uint32_t& total) {
   constexpr int kWaves = NT / kWave;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -51,26 +56,27 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, Shared& s, uint32_t& 
     const uint32_t y = (uint32_t)__shfl_up((int)x, d);
     if (lane >= d) x += y;
   }
-  if (lane == 63) s.wave_tot[wid] = x;
+  uint32_t* wt = s.wave_tot[parity];
+  if (lane == 63) wt[wid] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int i = 0; i < kWaves; ++i) {
-    const uint32_t w = s.wave_tot[i];
+    const uint32_t w = wt[i];
     before += (i < wid) ? w : 0u;
     tot += w;
   }
-  __syncthreads();
   total = tot;
   return before + x - v;
 }
 
 // Bin b (from the top) with count(bins > b) < need <= count(bins >= b); needs
-// need >= 1 and a histogram total >= need.  s.sel = {b, count above b}.
-template <int NT>
-__device__ void select_bin(Shared& s, uint32_t need) {
-  constexpr int per = kBins / NT;                 // bins per thread, descending
-  const int top = kBins - 1 - per * (int)threadIdx.x;
+// need >= 1 and a histogram total >= need.  Sets s.sel = {b, count above b}
+// and leaves the histogram cleared for the next level.  Two barriers.
+template <int NT, int BINS>
+__device__ void select_bin(Shared<BINS>& s, uint32_t need, int parity) {
+  constexpr int per = BINS / NT;                 // bins per thread, descending
+  const int top = BINS - 1 - per * (int)threadIdx.x;
   uint32_t c[per];
   uint32_t sum = 0;
 #pragma unroll
@@ -79,7 +85,7 @@ __device__ void select_bin(Shared& s, uint32_t need) {
     sum += c[j];
   }
   uint32_t total;
-  uint32_t run = block_scan<NT>(sum, s, total);
+  uint32_t run = block_scan<NT>(sum, s, parity, total);
 #pragma unroll
   for (int j = 0; j < per; ++j) {
     if (run < need && run + c[j] >= need) {
@@ -87,14 +93,14 @@ __device__ void select_bin(Shared& s, uint32_t need) {
       s.sel[1] = run;
     }
     run += c[j];
+    s.hist[top - j] = 0;                          // every read of the histogram is done
   }
   __syncthreads();
 }
 
-template <int NT>
-__device__ __forceinline__ void clear_hist(Shared& s) {
-  for (int i = threadIdx.x; i < kBins; i += NT) s.hist[i] = 0;
-  __syncthreads();
+template <int NT, int BINS>
+__device__ __forceinline__ void clear_hist(Shared<BINS>& s) {
+  for (int i = threadIdx.x; i < BINS; i += NT) s.hist[i] = 0;
 }
 
 // Keys E*t + e (e < E) of the segment src[0, n) into thread t's registers;
@@ -126,11 +132,11 @@ __device__ __forceinline__ int load_keys(const float* __restrict__ src, int64_t 
 }
 
 // One radix level over register-held keys: u = key - kmin; candidates have
-// u >> shift == prefix (all when shift >= 32); digit = the bits from shift-1
-// down to nsh.
-template <int E>
-__device__ __forceinline__ void hist_level(Shared& s, const uint32_t (&key)[E], int nv, uint32_t kmin,
-                                           int shift, uint32_t prefix, int nsh, uint32_t dmask) {
+// u >> shift == prefix (all when shift >= 32); digit = bits shift-1 .. nsh.
+template <int E, int BINS>
+__device__ __forceinline__ void hist_level(Shared<BINS>& s, const uint32_t (&key)[E], int nv,
+                                           uint32_t kmin, int shift, uint32_t prefix, int nsh,
+                                           uint32_t dmask) {
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t u = key[e] - kmin;
@@ -138,22 +144,31 @@ __device__ __forceinline__ void hist_level(Shared& s, const uint32_t (&key)[E], 
   }
 }
 
-// Levels from `shift` down to bit 0 on register-held keys.  Returns u_t (the
-// exact threshold, as key - kmin) and how many keys equal to it to take.
-template <int NT, int E>
-__device__ void refine_regs(Shared& s, const uint32_t (&key)[E], int nv, uint32_t kmin, int shift,
-                            uint32_t prefix, uint32_t need, uint32_t& u_t, uint32_t& need_ties) {
+template <int BINS>
+constexpr int digit_bits() {
+  int b = 0;
+  while ((1 << b) < BINS) ++b;
+  return b;
+}
+
+// Levels from `shift` down to bit 0 on register-held keys (histogram clear on
+// entry).  Returns u_t (the exact threshold, as key - kmin) and how many keys
+// equal to it to take.
+template <int NT, int BINS, int E>
+__device__ void refine_regs(Shared<BINS>& s, const uint32_t (&key)[E], int nv, uint32_t kmin,
+                            int shift, uint32_t prefix, uint32_t need, int& parity, uint32_t& u_t,
+                            uint32_t& need_ties) {
+  constexpr int D = digit_bits<BINS>();
   while (shift > 0) {
-    const int nsh = shift > 11 ? shift - 11 : 0;
+    const int nsh = shift > D ? shift - D : 0;
     const uint32_t dmask = (1u << (shift - nsh)) - 1u;
-    clear_hist<NT>(s);
     hist_level(s, key, nv, kmin, shift, prefix, nsh, dmask);
     __syncthreads();
-    select_bin<NT>(s, need);
+    select_bin<NT>(s, need, parity);
+    parity ^= 1;
     need -= s.sel[1];
     prefix = (prefix << (shift - nsh)) | s.sel[0];
     shift = nsh;
-    __syncthreads();
   }
   u_t = prefix;
   need_ties = need;
@@ -161,31 +176,33 @@ __device__ void refine_regs(Shared& s, const uint32_t (&key)[E], int nv, uint32_
 
 // Ordered output of register-held candidates (thread t holds consecutive
 // candidates, so thread order is candidate order): every u > u_t, and the
-// first need_ties with u == u_t, at out[base + rank].  gt_run / tie_run carry
+// first need_ties with u == u_t, at out[base + rank].  Candidates are the
+// valid keys (with key >> fshift == fbin when filt).  gt_run / tie_run carry
 // the counts of earlier chunks and are advanced by this chunk's totals.
-template <int NT, bool kCols, int E>
-__device__ __forceinline__ void emit_regs(Shared& s, const uint32_t (&key)[E],
+template <int NT, bool kCols, int BINS, int E>
+__device__ __forceinline__ void emit_regs(Shared<BINS>& s, const uint32_t (&key)[E],
                                           const uint32_t (&cols)[E], int64_t col0, int nv,
-                                          uint32_t kmin, uint32_t u_t,
-                                          uint32_t need_ties, bool filt, uint32_t bin1,
+                                          uint32_t kmin, uint32_t u_t, uint32_t need_ties,
+                                          bool filt, int fshift, uint32_t fbin,
                                           int32_t* __restrict__ out, uint32_t base, int k,
-                                          uint32_t& gt_run, uint32_t& tie_run) {
+                                          int& parity, uint32_t& gt_run, uint32_t& tie_run) {
   uint32_t cg = 0, ct = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t u = key[e] - kmin;
-    const bool ok = e < nv && (!filt || (key[e] >> 21) == bin1);
+    const bool ok = e < nv && (!filt || (key[e] >> fshift) == fbin);
     cg += (ok && u > u_t) ? 1u : 0u;
     ct += (ok && u == u_t) ? 1u : 0u;
   }
   uint32_t total;
-  const uint32_t pre = block_scan<NT>(cg | (ct << 16), s, total);
+  const uint32_t pre = block_scan<NT>(cg | (ct << 16), s, parity, total);
+  parity ^= 1;
   uint32_t g = gt_run + (pre & 0xffffu);
   uint32_t t = tie_run + (pre >> 16);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t u = key[e] - kmin;
-    const bool ok = e < nv && (!filt || (key[e] >> 21) == bin1);
+    const bool ok = e < nv && (!filt || (key[e] >> fshift) == fbin);
     const int64_t col = kCols ? (int64_t)cols[e] : col0 + e;
     if (ok && u > u_t) {
       const uint32_t pos = base + g + min(t, need_ties);
@@ -200,14 +217,14 @@ __device__ __forceinline__ void emit_regs(Shared& s, const uint32_t (&key)[E],
   tie_run += total >> 16;
 }
 
-template <int NT, int E>
+template <int NT, int E, int BINS>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logits, int64_t ld,
                                                   const int32_t* __restrict__ ks,
                                                   const int32_t* __restrict__ ke, int k,
                                                   int32_t* __restrict__ out_idx) {
   constexpr int kWaves = NT / kWave;
   constexpr int64_t C = (int64_t)NT * E;          // keys held per pass
-  __shared__ Shared s;
+  __shared__ Shared<BINS> s;
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];   // long rows only
   const int64_t r = blockIdx.x;
   const float* row = logits + r * ld;
@@ -224,11 +241,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
   const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
+  int parity = 0;
 
   if (n <= C) {
     // ---- the whole row in registers: one read ----
     uint32_t key[E];
     const int nv = load_keys<E>(src, n, vec, key);
+    clear_hist<NT>(s);                            // overlaps the loads
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e)
@@ -241,63 +260,64 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
     }
     if (lane == 0) {
-      s.wave_tot[wid] = kmin;
-      s.wave_tot[kWaves + wid] = kmax;
+      s.wave_tot[1][wid] = kmin;
+      s.wave_tot[1][kMaxWaves + wid] = kmax;
     }
     __syncthreads();
     for (int w = 0; w < kWaves; ++w) {
-      kmin = min(kmin, s.wave_tot[w]);
-      kmax = max(kmax, s.wave_tot[kWaves + w]);
+      kmin = min(kmin, s.wave_tot[1][w]);
+      kmax = max(kmax, s.wave_tot[1][kMaxWaves + w]);
     }
-    __syncthreads();
+    // wave_tot[1] is next written by the second scan, after at least one more barrier
     const uint32_t range = kmax - kmin;
     const int L = range ? 32 - __clz(range) : 0;     // bit length of the key range
     uint32_t u_t = 0, need_ties = (uint32_t)k;        // all keys equal: the lowest columns
-    if (L > 0) refine_regs<NT>(s, key, nv, kmin, L, 0u, (uint32_t)k, u_t, need_ties);
+    if (L > 0) refine_regs<NT>(s, key, nv, kmin, L, 0u, (uint32_t)k, parity, u_t, need_ties);
     uint32_t gr = 0, tr = 0;
     emit_regs<NT, false>(s, key, key, lo + (int64_t)E * threadIdx.x, nv, kmin, u_t, need_ties,
-                         false, 0u, out, 0u, k, gr, tr);
+                         false, 0, 0u, out, 0u, k, parity, gr, tr);
     return;
   }
 
   // ---- long row, chunks of C keys ----
-  // Pass 1: level-1 histogram of bits 31..21.  Workgroups of <= 8 waves keep
-  // one histogram per wave (fewer colliding LDS atomics), merged afterwards.
+  // Pass 1: histogram of the top digit.  Workgroups of <= 8 waves keep one
+  // 11-bit histogram per wave (fewer colliding LDS atomics), merged
+  // afterwards; larger workgroups use the shared histogram's full width.
   constexpr bool kWaveHist = kWaves <= 8;
-  uint32_t* wh = kWaveHist ? dyn + wid * kBins : s.hist;
-  if (kWaveHist) {
-    for (int i = lane; i < kBins; i += kWave) wh[i] = 0;
-    __syncthreads();
-  } else {
-    clear_hist<NT>(s);
-  }
+  constexpr int D1 = kWaveHist ? 11 : digit_bits<BINS>();
+  constexpr int S1 = 32 - D1;
+  uint32_t* wh = kWaveHist ? dyn + wid * kWaveHistBins : s.hist;
+  if (kWaveHist)
+    for (int i = lane; i < kWaveHistBins; i += kWave) wh[i] = 0;
+  clear_hist<NT>(s);
+  __syncthreads();
   for (int64_t c0 = 0; c0 < n; c0 += C) {
     uint32_t key[E];
     const int nv = load_keys<E>(src + c0, n - c0, vec, key);
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (e < nv) atomicAdd(&wh[key[e] >> 21], 1u);
+      if (e < nv) atomicAdd(&wh[key[e] >> S1], 1u);
   }
   __syncthreads();
   if (kWaveHist) {
-    for (int b = threadIdx.x; b < kBins; b += NT) {
+    for (int b = threadIdx.x; b < kWaveHistBins; b += NT) {
       uint32_t c = 0;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) c += dyn[w * kBins + b];
+      for (int w = 0; w < kWaves; ++w) c += dyn[w * kWaveHistBins + b];
       s.hist[b] = c;
     }
     __syncthreads();
   }
-  select_bin<NT>(s, (uint32_t)k);
+  select_bin<NT>(s, (uint32_t)k, parity);
+  parity ^= 1;
   const uint32_t bin1 = s.sel[0];
   const uint32_t above1 = s.sel[1];
-  const uint32_t m = s.hist[bin1];
-  __syncthreads();                          // per-wave histograms are dead from here
-  const bool fits = m <= (uint32_t)kCandPairs;
-  uint32_t* cand_keys = dyn;
+  uint32_t* cand_keys = dyn;                      // the per-wave histograms are dead now
   uint32_t* cand_cols = dyn + kCandPairs;
+  uint32_t m;                                     // keys in bin1
   {
-    // Pass 2: keys above bin1 go straight out; bin1's keys become candidates.
+    // Pass 2: keys above bin1 go straight out; bin1's keys become candidates
+    // (stored while they fit; their count decides the path afterwards).
     uint32_t gbase = 0, cbase = 0;
     for (int64_t c0 = 0; c0 < n; c0 += C) {
       uint32_t key[E];
@@ -305,22 +325,23 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       uint32_t cg = 0, cq = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        cg += (e < nv && (key[e] >> 21) > bin1) ? 1u : 0u;
-        cq += (e < nv && (key[e] >> 21) == bin1) ? 1u : 0u;
+        cg += (e < nv && (key[e] >> S1) > bin1) ? 1u : 0u;
+        cq += (e < nv && (key[e] >> S1) == bin1) ? 1u : 0u;
       }
       uint32_t total;
-      const uint32_t pre = block_scan<NT>(cg | (cq << 16), s, total);
+      const uint32_t pre = block_scan<NT>(cg | (cq << 16), s, parity, total);
+      parity ^= 1;
       uint32_t g = gbase + (pre & 0xffffu), q = cbase + (pre >> 16);
       const int64_t col0 = lo + c0 + (int64_t)E * threadIdx.x;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         if (e >= nv) continue;
-        const uint32_t b = key[e] >> 21;
+        const uint32_t b = key[e] >> S1;
         if (b > bin1) {
           if (g < (uint32_t)k) out[g] = (int32_t)(col0 + e);
           ++g;
         } else if (b == bin1) {
-          if (fits && q < (uint32_t)kCandPairs) {
+          if (q < (uint32_t)kCandPairs) {
             cand_keys[q] = key[e];
             cand_cols[q] = (uint32_t)(col0 + e);
           }
@@ -330,10 +351,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       gbase += total & 0xffffu;
       cbase += total >> 16;
     }
+    m = cbase;
     __syncthreads();
   }
   uint32_t u_t, need_ties;
-  if (fits) {
+  if (m <= (uint32_t)kCandPairs) {
     // candidates back into registers, consecutive per thread
     constexpr int E2 = kCandPairs / NT;
     uint32_t key[E2], cols[E2];
@@ -344,28 +366,29 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       key[e] = (e < nv) ? cand_keys[first + e] : 0u;
       cols[e] = (e < nv) ? cand_cols[first + e] : 0u;
     }
-    refine_regs<NT>(s, key, nv, 0u, 21, bin1, (uint32_t)k - above1, u_t, need_ties);
+    refine_regs<NT>(s, key, nv, 0u, S1, bin1, (uint32_t)k - above1, parity, u_t, need_ties);
     uint32_t gr = 0, tr = 0;
-    emit_regs<NT, true>(s, key, cols, 0, nv, 0u, u_t, need_ties, false, bin1, out, above1, k, gr, tr);
+    emit_regs<NT, true>(s, key, cols, 0, nv, 0u, u_t, need_ties, false, S1, bin1, out, above1, k,
+                        parity, gr, tr);
     return;
   }
   // more than 8192 keys in the threshold bin: the remaining levels re-read the row
+  constexpr int D = digit_bits<BINS>();
   uint32_t need = (uint32_t)k - above1, prefix = bin1;
-  for (int shift = 21; shift > 0;) {
-    const int nsh = shift > 11 ? shift - 11 : 0;
+  for (int shift = S1; shift > 0;) {
+    const int nsh = shift > D ? shift - D : 0;
     const uint32_t dmask = (1u << (shift - nsh)) - 1u;
-    clear_hist<NT>(s);
     for (int64_t c0 = 0; c0 < n; c0 += C) {
       uint32_t key[E];
       const int nv = load_keys<E>(src + c0, n - c0, vec, key);
       hist_level(s, key, nv, 0u, shift, prefix, nsh, dmask);
     }
     __syncthreads();
-    select_bin<NT>(s, need);
+    select_bin<NT>(s, need, parity);
+    parity ^= 1;
     need -= s.sel[1];
     prefix = (prefix << (shift - nsh)) | s.sel[0];
     shift = nsh;
-    __syncthreads();
   }
   u_t = prefix;
   need_ties = need;
@@ -374,11 +397,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
     uint32_t key[E];
     const int nv = load_keys<E>(src + c0, n - c0, vec, key);
     emit_regs<NT, false>(s, key, key, lo + c0 + (int64_t)E * threadIdx.x, nv, 0u, u_t, need_ties,
-                         true, bin1, out, above1, k, gr, tr);
+                         true, S1, bin1, out, above1, k, parity, gr, tr);
   }
 }
 
-template <int NT, int E>
+template <int NT, int E, int BINS>
 hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                       const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {
   const bool long_rows = ld > (int64_t)NT * E;
@@ -387,13 +410,13 @@ hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32
   if (long_rows) {
     static bool attr_set = false;
     if (!attr_set) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<NT, E>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<NT, E, BINS>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
       attr_set = true;
     }
   }
-  hipLaunchKernelGGL((topk_kernel<NT, E>), dim3((unsigned)rows), dim3(NT), dyn, stream, logits, ld,
-                     ks, ke, k, out_idx);
+  hipLaunchKernelGGL((topk_kernel<NT, E, BINS>), dim3((unsigned)rows), dim3(NT), dyn, stream, logits,
+                     ld, ks, ke, k, out_idx);
   return hipGetLastError();
 }
 
@@ -402,15 +425,16 @@ hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32
 hipError_t launch_topk(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                        const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {
   // Few rows: 1024 threads per row (the row's latency is the step's); many
-  // rows: 512 threads per row, two rows per CU.  Keys per thread: the smallest
-  // size that holds a full row in one pass (up to 16).
+  // rows: 512 threads, two rows per CU.  Wider digits (fewer levels) lose:
+  // the per-level histogram clear and scan grow with the bin count.
+  // Keys per thread: the smallest size that holds a full row in one pass.
   if (rows < 512) {
-    if (ld <= 4 * 1024) return launch_cfg<1024, 4>(logits, rows, ld, ks, ke, k, out_idx, stream);
-    if (ld <= 8 * 1024) return launch_cfg<1024, 8>(logits, rows, ld, ks, ke, k, out_idx, stream);
-    return launch_cfg<1024, 16>(logits, rows, ld, ks, ke, k, out_idx, stream);
+    if (ld <= 4 * 1024) return launch_cfg<1024, 4, 2048>(logits, rows, ld, ks, ke, k, out_idx, stream);
+    if (ld <= 8 * 1024) return launch_cfg<1024, 8, 2048>(logits, rows, ld, ks, ke, k, out_idx, stream);
+    return launch_cfg<1024, 16, 2048>(logits, rows, ld, ks, ke, k, out_idx, stream);
   }
-  if (ld <= 8 * 512) return launch_cfg<512, 8>(logits, rows, ld, ks, ke, k, out_idx, stream);
-  return launch_cfg<512, 16>(logits, rows, ld, ks, ke, k, out_idx, stream);
+  if (ld <= 8 * 512) return launch_cfg<512, 8, 2048>(logits, rows, ld, ks, ke, k, out_idx, stream);
+  return launch_cfg<512, 16, 2048>(logits, rows, ld, ks, ke, k, out_idx, stream);
 }
 
 }  // namespace mxidx

@@ -43,7 +43,9 @@ def test_paged_tiny():
 @pytest.mark.parametrize("H,next_n,lens", [(16, 1, [1, 63, 64, 65, 300]),
                                            (64, 3, [5, 64, 129, 250]),
                                            (128, 2, [100, 17]),
-                                           (48, 16, [40, 200])])
+                                           (48, 16, [40, 200]),
+                                           (32, 1, [0, 5, 0, 700, 64, 0, 1]),
+                                           (32, 2, list(np.random.default_rng(5).integers(0, 1500, 300)))])
 def test_paged_ragged_heads_and_next_n(H, next_n, lens):
     case = workloads.decode_case(H * 7 + next_n, seq_lens=lens, H=H, next_n=next_n, spare_pages=2,
                                  width=max(lens) + 37)
