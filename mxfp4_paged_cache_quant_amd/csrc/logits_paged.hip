@@ -6,18 +6,31 @@
 // with row r = b*next_n + i and token s read from page block_table[b, s/64]
 // of the block-split MXFP4 cache (P1 live-validation comment).
 //
-// Design (HBM-bound: 68 bytes of K per scored token):
-//  * grid = (logical pages / 4, sequences); each wave owns one 64-token page.
-//  * The page's codes are loaded straight into MFMA B operands: lane l takes
-//    16 bytes (block l/16 of token 16*j + l%16) for each of the 4 token tiles
-//    j, so a wave reads the page's 4096 code bytes as one contiguous 4 KB
-//    sweep, plus each token's 4 scale bytes.
+// Design (HBM-bound: 68 bytes of K per scored token, 4 bytes of logit out):
+//  * grid = (logical pages / 2, sequences), one wave per workgroup, so the
+//    dispatcher balances ragged sequence lengths at the finest grain; each
+//    wave owns two consecutive pages of one sequence and has both pages'
+//    loads in flight before it computes either.
+//  * A page's base address is wave-uniform: it goes into a buffer descriptor
+//    in scalar registers and every lane keeps one fixed offset, so a page
+//    costs no vector address arithmetic.  A missing page (past the context,
+//    or an invalid block-table entry) gets a zero-length descriptor: its
+//    loads return zeros without touching memory.
+//  * Lane l takes 16 bytes (block l/16 of token 16*j + l%16) for each of the
+//    page's 4 token tiles j -- the page's 4096 code bytes as one contiguous
+//    sweep -- plus each token's 4 scale bytes.  The cache streams through
+//    once per call, so the loads and logit stores are non-temporal.
 //  * Heads are the MFMA M dimension: per 16-head group one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1, UE8M0 scale per 32-wide
-//    block and lane) per token tile gives the exact scaled head dots.
-//  * ReLU and the head weights are applied on the fp32 MFMA output; the four
-//    lane groups' partial sums are combined by two xor-shuffles, after which
+//    block and lane) per token tile gives the exact scaled head dots.  An
+//    output column depends on its own token only, so tokens past the context
+//    need no masking of operands, only of stores.
+//  * ReLU and the head weights are applied on the fp32 MFMA output; two
+//    xor-shuffles combine the four lane groups' partial sums, after which
 //    lane l owns token l of the page and the wave stores 64 consecutive floats.
+//  * Vector memory counters retire in issue order, so a wait for a load also
+//    waits for every store issued before it: for single-row decode the logit
+//    stores are issued after the wave's last load.
 #include "common.hpp"
 #include "launch.hpp"
 #include "logits_reduce.hpp"
@@ -25,80 +38,154 @@
 namespace mxidx {
 namespace {
 
-constexpr int kPagesPerBlock = 4;   // 4 waves, one page each
+constexpr int kPagesPerWave = 2;
+// Dword 3 of a raw buffer descriptor: data format 32 (bits 18:15 = 4); raw
+// loads and stores move bytes and ignore the format otherwise.
+constexpr int kBufferFormat = 0x00020000;
+constexpr int kNonTemporal = 2;                 // cache-policy bits of buffer ops: nt
+constexpr uint32_t kDropOffset = 0x40000000u;   // beyond any descriptor: the store is dropped
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFormat);
+}
+
+struct PageRegs {
+  uint4 code[4];      // tile j: block g of token 16*j + n
+  uint32_t scale[4];  // tile j: the 4 scale bytes of token 16*j + n
+};
 
 template <int NH>
-__global__ __launch_bounds__(256) void logits_paged_kernel(
+struct QueryRegs {
+  uint4 a[NH];        // group grp: block g of head 16*grp + n
+  int sa[NH];         // its UE8M0 scale byte
+  float4 w[NH];       // weights of heads 16*grp + 4*g .. +3
+};
+
+template <int NH>
+__device__ __forceinline__ QueryRegs<NH> load_query(const uint8_t* __restrict__ q_values,
+                                                    const uint8_t* __restrict__ q_scales,
+                                                    const float* __restrict__ weights, int64_t r,
+                                                    int g, int n) {
+  constexpr int H = 16 * NH;
+  QueryRegs<NH> q;
+#pragma unroll
+  for (int grp = 0; grp < NH; ++grp) {
+    const int64_t qrow = r * H + 16 * grp + n;
+    q.a[grp] = *reinterpret_cast<const uint4*>(q_values + qrow * kCodeBytes + g * 16);
+    q.sa[grp] = q_scales[qrow * kScaleBytes + g];
+    q.w[grp] = *reinterpret_cast<const float4*>(weights + r * H + 16 * grp + 4 * g);
+  }
+  return q;
+}
+
+// Weighted ReLU head sum for the 64 tokens of one page; lane l returns token l.
+template <int NH>
+__device__ __forceinline__ float page_score(const PageRegs& pg, const QueryRegs<NH>& q, int lane) {
+  const int g = lane >> 4;
+  int bs[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bs[j] = (int)((pg.scale[j] >> (8 * g)) & 0xffu);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int grp = 0; grp < NH; ++grp)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = relu_weighted(mfma_fp4(q.a[grp], pg.code[j], q.sa[grp], bs[j], zero), q.w[grp], acc[j]);
+  return reduce_tiles(acc, lane);
+}
+
+template <int NH, bool kOneRow>
+__global__ __launch_bounds__(kWave) void logits_paged_kernel(
     const uint8_t* __restrict__ q_values, const uint8_t* __restrict__ q_scales,
     const float* __restrict__ weights, const uint8_t* __restrict__ cache, int64_t num_pages,
     const int32_t* __restrict__ block_table, int64_t bt_row_stride,
     const int32_t* __restrict__ context_lens, int next_n, int64_t width,
     float* __restrict__ logits, int64_t ld, int clean) {
-  constexpr int H = 16 * NH;
   const int b = blockIdx.y;
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x;
   const int g = lane >> 4;       // 32-element block this lane supplies / head quad it receives
   const int n = lane & 15;       // token within a 16-token tile / head within a group
-  const int64_t lp = (int64_t)blockIdx.x * kPagesPerBlock + (threadIdx.x >> 6);
-  const int64_t tok0 = lp * kPage;
-  if (tok0 >= width) return;
-  // context lengths beyond the row width are a precondition violation; clamp so
-  // that no store leaves the row
-  const int64_t L = min((int64_t)context_lens[b], width);
-  const int64_t col = tok0 + lane;
+  const int64_t lp0 = (int64_t)blockIdx.x * kPagesPerWave;
+  const int64_t wpages = (width + kPage - 1) / kPage;
   const int64_t row0 = (int64_t)b * next_n;
 
-  if (tok0 >= L) {               // the whole page lies past the context
-    if (clean && col < width)
-      for (int i = 0; i < next_n; ++i) logits[(row0 + i) * ld + col] = neg_inf();
+  // Context length and the wave's block-table entries in one round trip: both
+  // as vector loads (a scalar load of the length would have to retire before
+  // the table load could issue).  Lane p < 2 reads the entry of page lp0 + p;
+  // the other lanes fall outside the descriptor and read 0 without an access.
+  const int bt_count = (int)min((int64_t)kPagesPerWave, wpages - lp0);
+  const int bt_lane = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_rsrc(block_table + (int64_t)b * bt_row_stride + lp0, 4 * bt_count), 4u * lane, 0, 0);
+  const uint32_t ctx_raw =
+      __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(context_lens + b, 4), 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::"v"(bt_lane));   // keeps the table load here, not sunk past the branch below
+  const int64_t ctx = (int32_t)__builtin_amdgcn_readfirstlane(ctx_raw);
+  QueryRegs<NH> q0;
+  if (kOneRow) q0 = load_query<NH>(q_values, q_scales, weights, row0, g, n);
+  // context lengths beyond the row width are a precondition violation; clamp so
+  // that no store leaves the row
+  const int64_t L = min(ctx, width);
+
+  // Store of one page-row: scored columns get v, other columns of the row
+  // width get -inf when cleaning, the rest is left untouched.
+  auto store = [&](int64_t r, int64_t tok0, int64_t ke, float v) {
+    const int64_t col = tok0 + lane;
+    const bool scored = col < ke;
+    const bool keep = scored || (clean && col < width);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(logits + r * ld + tok0, kPage * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scored ? v : neg_inf()), rs,
+                                          keep ? 4u * lane : kDropOffset, 0, kNonTemporal);
+  };
+
+  if (lp0 * kPage >= L) {        // both pages lie past the context: -inf fill only
+    if (clean)
+      for (int i = 0; i < next_n; ++i)
+#pragma unroll
+        for (int p = 0; p < kPagesPerWave; ++p) store(row0 + i, (lp0 + p) * kPage, 0, 0.f);
     return;
   }
-  const int64_t page = block_table[(int64_t)b * bt_row_stride + lp];
-  if (page < 0 || page >= num_pages) return;
-  const uint8_t* pbase = cache + page * kPageBytes;
+  const int np = (int)min((int64_t)kPagesPerWave, (L - lp0 * kPage + kPage - 1) / kPage);
 
-  // the cache streams through once per call: non-temporal loads
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  uint4 bk[4];
-  int bs[4];
+  PageRegs pg[kPagesPerWave];
+  bool page_ok[kPagesPerWave];   // false: invalid block-table entry, the page is skipped
+  const uint32_t off_code = 64u * n + 16u * g;
+  const uint32_t off_scale = kPageCodeBytes + 4u * n;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tk = 16 * j + n;
-    const u32x4 c = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(pbase + tk * kCodeBytes + g * 16));
-    bk[j] = make_uint4(c.x, c.y, c.z, c.w);
-    const uint32_t s4 = __builtin_nontemporal_load(
-        reinterpret_cast<const uint32_t*>(pbase + kPageCodeBytes + tk * kScaleBytes));
-    bs[j] = (int)((s4 >> (8 * g)) & 0xffu);
-    if (tok0 + tk >= L) {        // unwritten slots past the context: neutral operands
-      bk[j] = make_uint4(0, 0, 0, 0);
-      bs[j] = 127;
+  for (int p = 0; p < kPagesPerWave; ++p) {
+    const int pid = __builtin_amdgcn_readlane(bt_lane, p);
+    const bool valid = pid >= 0 && pid < num_pages;
+    page_ok[p] = p >= np || valid;
+    const int live = __builtin_amdgcn_readfirstlane((p < np && valid) ? 1 : 0);
+    const int64_t page = __builtin_amdgcn_readfirstlane(live ? pid : 0);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(cache + page * kPageBytes, live ? kPageBytes : 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, off_code + 1024u * j, 0, kNonTemporal);
+      pg[p].code[j] = make_uint4(c.x, c.y, c.z, c.w);
+      pg[p].scale[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_scale + 64u * j, 0, kNonTemporal);
     }
   }
+  __builtin_amdgcn_sched_barrier(0);   // every page load issues before any compute
 
-  for (int i = 0; i < next_n; ++i) {
-    const int64_t r = row0 + i;
-    const int64_t ke = L - next_n + i + 1;
-    if (tok0 >= ke) {
-      if (clean && col < width) logits[r * ld + col] = neg_inf();
-      continue;
-    }
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (kOneRow) {
+    float out[kPagesPerWave];
 #pragma unroll
-    for (int grp = 0; grp < NH; ++grp) {
-      const int64_t qrow = r * H + 16 * grp + n;
-      const uint4 a = *reinterpret_cast<const uint4*>(q_values + qrow * kCodeBytes + g * 16);
-      const int sa = q_scales[qrow * kScaleBytes + g];
-      const float4 w = *reinterpret_cast<const float4*>(weights + r * H + 16 * grp + 4 * g);
-      const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < kPagesPerWave; ++p) out[p] = page_score<NH>(pg[p], q0, lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = relu_weighted(mfma_fp4(a, bk[j], sa, bs[j], zero), w, acc[j]);
+    for (int p = 0; p < kPagesPerWave; ++p)
+      if (page_ok[p]) store(row0, (lp0 + p) * kPage, L, out[p]);
+  } else {
+    for (int i = 0; i < next_n; ++i) {
+      const int64_t r = row0 + i;
+      const int64_t ke = L - next_n + i + 1;
+      const QueryRegs<NH> q = load_query<NH>(q_values, q_scales, weights, r, g, n);
+#pragma unroll
+      for (int p = 0; p < kPagesPerWave; ++p)
+        if (page_ok[p]) store(r, (lp0 + p) * kPage, ke, page_score<NH>(pg[p], q, lane));
     }
-    const float out = reduce_tiles(acc, lane);
-    if (col < ke)
-      logits[r * ld + col] = out;
-    else if (clean && col < width)
-      logits[r * ld + col] = neg_inf();
   }
 }
 
@@ -108,10 +195,13 @@ hipError_t launch_nh(const uint8_t* qv, const uint8_t* qs, const float* w, const
                      int B, int next_n, int64_t width, float* logits, int64_t ld, int clean,
                      hipStream_t stream) {
   const int64_t pages = (width + kPage - 1) / kPage;
-  const int64_t gx = (pages + kPagesPerBlock - 1) / kPagesPerBlock;
-  hipLaunchKernelGGL((logits_paged_kernel<NH>), dim3((unsigned)gx, (unsigned)B), dim3(256), 0, stream,
-                     qv, qs, w, cache, num_pages, bt, bt_stride, ctx, next_n, width, logits, ld,
-                     clean);
+  const dim3 grid((unsigned)((pages + kPagesPerWave - 1) / kPagesPerWave), (unsigned)B);
+  if (next_n == 1)
+    hipLaunchKernelGGL((logits_paged_kernel<NH, true>), grid, dim3(kWave), 0, stream, qv, qs, w,
+                       cache, num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean);
+  else
+    hipLaunchKernelGGL((logits_paged_kernel<NH, false>), grid, dim3(kWave), 0, stream, qv, qs, w,
+                       cache, num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean);
   return hipGetLastError();
 }
 
