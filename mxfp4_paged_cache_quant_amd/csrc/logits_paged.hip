@@ -92,7 +92,7 @@ __device__ __forceinline__ float page_score(const PageRegs& pg, const QueryRegs<
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc[j] = relu_weighted(mfma_fp4(q.a[grp], pg.code[j], q.sa[grp], bs[j], zero), q.w[grp], acc[j]);
-  return reduce_tiles(acc, lane);
+  return reduce_tiles(acc);
 }
 
 template <int NH, bool kOneRow>

@@ -14,15 +14,25 @@
 // for the whole chunk and sweeps the keys 64 at a time (4 MFMA B tiles loaded
 // straight from the contiguous K rows, 16 bytes per lane).  Per 16-head group
 // and 16-key tile: one MFMA, then ReLU + weight FMA on the 4 outputs of each
-// lane; a 2-step xor-shuffle reduction leaves logit (t, c0+lane) in lane
-// `lane`, so each row's 64 results are one coalesced 256-byte store.
-// Rows whose visible range misses the 64 keys skip their MFMAs (causal tiles
-// above the diagonal cost nothing unless clean output asks for -inf fill).
+// lane; a cross-lane reduction (two lane-swap steps) leaves logit
+// (t, c0+lane) in lane `lane`, so each row's 64 results are one coalesced
+// 256-byte store.  Keys past the key window or past S cost nothing unless
+// clean output asks for -inf fill.
+//
+// The kernel is bound by its vector ALU, not by the MFMA: the ReLU and the
+// weight FMA are 2 wave-wide VALU instructions (4 cycles each on a 16-lane
+// SIMD) per MFMA output register, i.e. 32 VALU cycles per 16-cycle MFMA, so
+// every other VALU instruction is kept out of the loop: tile loads and logit
+// stores go through buffer descriptors whose base (key tile, logits row) is
+// wave-uniform and lives in scalar registers, and lane masks are computed only
+// for the tiles that straddle a row's [ks, ke) boundary.
 //
 // Block order: workgroup id i runs on XCD i % 8; the j-th workgroup of an XCD
 // gets query block (j / n_kc) * 8 + i % 8 and key chunk j % n_kc, so one XCD's
 // resident workgroups share a query block in its L2, and the causal work is
-// spread evenly over the 8 XCDs.
+// spread evenly over the 8 XCDs.  Query blocks are taken last to first: under
+// causal masking the late rows see the most keys, so the longest workgroups
+// are dispatched first and the short ones fill the tail.
 #include "common.hpp"
 #include "launch.hpp"
 #include "logits_reduce.hpp"
@@ -32,20 +42,36 @@ namespace {
 
 constexpr int kKeyChunk = 1024;
 
-// B operands of 64 consecutive keys: lane (g, n) takes the 16 code bytes of
-// block g of key c0 + 16*j + n for each tile j, and that key's 4 scale bytes
-// (the block's byte is extracted when the tile is used).  Keys past the last
-// one are clamped to it: their columns are never stored.
+// Dword 3 of a raw buffer descriptor: data format 32 (bits 18:15 = 4); raw
+// loads and stores move bytes and ignore the format otherwise.
+constexpr int kBufferFormat = 0x00020000;
+constexpr int kNonTemporal = 2;                 // cache-policy bits of buffer ops: nt
+constexpr uint32_t kDropOffset = 0x40000000u;   // beyond any descriptor: the store is dropped
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFormat);
+}
+
+// B operands of 64 consecutive keys c0..c0+63: lane (g, n) takes the 16 code
+// bytes of block g of key c0 + 16*j + n for each tile j, and that key's 4
+// scale bytes (the block's byte is extracted when the tile is used).  Keys at
+// or past S lie outside the descriptors and read as zeros; their columns are
+// never stored.
 struct KTile {
   uint4 code[4];
   uint32_t scale[4];
   __device__ __forceinline__ void load(const uint8_t* __restrict__ kv, const uint8_t* __restrict__ ksc,
-                                       int c0, int last, int g, int n) {
+                                       int c0, int S, uint32_t off_code, uint32_t off_scale) {
+    c0 = __builtin_amdgcn_readfirstlane(c0);   // wave-uniform: descriptors stay in scalar registers
+    const int keys = __builtin_amdgcn_readfirstlane(max(min(S - c0, 64), 0));
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(kv + (int64_t)c0 * kCodeBytes, keys * kCodeBytes);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(ksc + (int64_t)c0 * kScaleBytes, keys * kScaleBytes);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int key = min(c0 + 16 * j + n, last);
-      code[j] = *reinterpret_cast<const uint4*>(kv + (int64_t)key * kCodeBytes + g * 16);
-      scale[j] = *reinterpret_cast<const uint32_t*>(ksc + (int64_t)key * kScaleBytes);
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rc, off_code + 1024u * j, 0, 0);
+      code[j] = make_uint4(c.x, c.y, c.z, c.w);
+      scale[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_scale + 64u * j, 0, 0);
     }
   }
 };
@@ -59,17 +85,17 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(
     int clean, int64_t n_qb, int64_t n_kc) {
   constexpr int H = 16 * NH;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4;
   const int n = lane & 15;
 
   int64_t qb, kc;
   if (n_qb % 8 == 0) {
     const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
-    qb = (j / n_kc) * 8 + x;
+    qb = n_qb - 1 - ((j / n_kc) * 8 + x);
     kc = j % n_kc;
   } else {
-    qb = blockIdx.x / n_kc;
+    qb = n_qb - 1 - blockIdx.x / n_kc;
     kc = blockIdx.x % n_kc;
   }
   const int64_t t0 = qb * (4 * RW) + wave * RW;
@@ -97,16 +123,29 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(
   float* lrow[RW];
 #pragma unroll
   for (int i = 0; i < RW; ++i) lrow[i] = logits + min(t0 + i, T - 1) * ld;
+  // Store of row i's 64 results for keys c0..c0+63: scored columns get v,
+  // other columns of the chunk get -inf when cleaning, the rest is untouched.
+  auto store = [&](int i, int c0, float v) {
+    c0 = __builtin_amdgcn_readfirstlane(c0);
+    uint32_t off = 4u * lane;
+    if (t0 + i >= T) off = kDropOffset;
+    if (!(c0 >= lo[i] && c0 + 64 <= hi[i])) {        // a tile that straddles [ks, ke)
+      const int col = c0 + lane;
+      const bool scored = col >= lo[i] && col < hi[i];
+      if (!scored) v = neg_inf();
+      if (!scored && !(clean && col < c_end)) off = kDropOffset;
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), buffer_rsrc(lrow[i] + c0, 64 * 4), off,
+                                          0, kNonTemporal);
+  };
   const int k_first = c_begin + ((need_lo - c_begin) & ~63);
   if (clean) {
     // -inf for the keys of this chunk that the computed window below does not
     // cover (inside the window, masked columns are written at store time)
     for (int c0 = c_begin; c0 < c_end; c0 += 64) {
       if (need_lo < need_hi && c0 >= k_first && c0 < need_hi) continue;
-      const int col = c0 + lane;
 #pragma unroll
-      for (int i = 0; i < RW; ++i)
-        if (t0 + i < T && col < c_end) lrow[i][col] = neg_inf();
+      for (int i = 0; i < RW; ++i) store(i, c0, neg_inf());
     }
   }
   if (need_lo >= need_hi) return;
@@ -127,23 +166,20 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(
   }
 
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  const int last = S - 1;
-  KTile nxt;
-  nxt.load(k_values, k_scales, k_first, last, g, n);
-  for (int c0 = k_first; c0 < need_hi; c0 += 64) {
-    const KTile cur = nxt;
-    if (c0 + 64 < need_hi) nxt.load(k_values, k_scales, c0 + 64, last, g, n);   // prefetch
+  const uint32_t off_code = 64u * n + 16u * g;
+  const uint32_t off_scale = 4u * n;
+  // One 64-key step over the wave's rows.  All rows x head groups x tiles,
+  // no per-row branches: rows that see nothing of these keys are masked at the
+  // store.  The MFMAs of the next (row, group) are issued before the epilogue
+  // of the current one.
+  auto step = [&](int c0, const KTile& kt) {
     int bs[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bs[j] = (int)((cur.scale[j] >> (8 * g)) & 0xffu);
-    const int col = c0 + lane;
-    // All rows x head groups x tiles, no per-row branches: rows that see
-    // nothing of these 64 keys are masked at the store.  The MFMAs of the next
-    // (row, group) are issued before the epilogue of the current one.
+    for (int j = 0; j < 4; ++j) bs[j] = (int)((kt.scale[j] >> (8 * g)) & 0xffu);
     float acc[RW][4];
     v4f d[2][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d[0][j] = mfma_fp4(a[0][0], cur.code[j], sa[0][0], bs[j], zero);
+    for (int j = 0; j < 4; ++j) d[0][j] = mfma_fp4(a[0][0], kt.code[j], sa[0][0], bs[j], zero);
 #pragma unroll
     for (int p = 0; p < RW * NH; ++p) {
       const int i = p / NH, grp = p % NH;
@@ -151,21 +187,24 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(
         const int i1 = (p + 1) / NH, g1 = (p + 1) % NH;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          d[(p + 1) & 1][j] = mfma_fp4(a[i1][g1], cur.code[j], sa[i1][g1], bs[j], zero);
+          d[(p + 1) & 1][j] = mfma_fp4(a[i1][g1], kt.code[j], sa[i1][g1], bs[j], zero);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         acc[i][j] = relu_weighted(d[p & 1][j], wv[i][grp], grp == 0 ? 0.f : acc[i][j]);
-      if (grp == NH - 1) {
-        const float out = reduce_tiles(acc[i], lane);
-        if (t0 + i < T) {
-          if (col >= lo[i] && col < hi[i])
-            lrow[i][col] = out;
-          else if (clean && col < c_end)
-            lrow[i][col] = neg_inf();
-        }
-      }
+      if (grp == NH - 1) store(i, c0, reduce_tiles(acc[i]));
     }
+  };
+  // Two tile buffers, the next tile's loads in flight during a step (a
+  // prefetch past the window reads keys nobody stores, or nothing past S).
+  KTile kt0, kt1;
+  kt0.load(k_values, k_scales, k_first, S, off_code, off_scale);
+  for (int c0 = k_first; c0 < need_hi; c0 += 128) {
+    kt1.load(k_values, k_scales, c0 + 64, S, off_code, off_scale);
+    step(c0, kt0);
+    if (c0 + 64 >= need_hi) break;
+    kt0.load(k_values, k_scales, c0 + 128, S, off_code, off_scale);
+    step(c0 + 64, kt1);
   }
 }
 

@@ -25,20 +25,22 @@ __device__ __forceinline__ float relu_weighted(const v4f d, const float4 w, floa
 // Lane (g = lane/16, n = lane%16) holds acc[j] = partial logit of token 16*j + n
 // over the heads of lane group g.  Returns, in lane (g, n), the full sum over
 // the 4 lane groups for token 16*g + n, i.e. token `lane` of the 64.
-// Fixed summation order: ((g) + (g^2)) + ((g^1) + (g^3)).
-__device__ __forceinline__ float reduce_tiles(const float acc[4], int lane) {
-  const int g = lane >> 4;
-  const bool lo_half = g < 2;
-  const float keep0 = lo_half ? acc[0] : acc[2];
-  const float keep1 = lo_half ? acc[1] : acc[3];
-  const float send0 = lo_half ? acc[2] : acc[0];
-  const float send1 = lo_half ? acc[3] : acc[1];
-  const float p0 = keep0 + __shfl_xor(send0, 32);
-  const float p1 = keep1 + __shfl_xor(send1, 32);
-  const bool odd = g & 1;
-  const float keep = odd ? p1 : p0;
-  const float send = odd ? p0 : p1;
-  return keep + __shfl_xor(send, 16);
+// gfx950's lane swaps do the two exchanges without LDS: v_permlane32_swap(x, y)
+// yields [x lanes 0-31 | y lanes 0-31] and [x lanes 32-63 | y lanes 32-63];
+// v_permlane16_swap(x, y) yields [x row 0 | y row 0 | x row 2 | y row 2] and
+// the same with rows 1 and 3 (a row is 16 lanes).
+// Fixed summation order: ((g=0) + (g=2)) + ((g=1) + (g=3)).
+__device__ __forceinline__ float reduce_tiles(const float acc[4]) {
+  const auto s02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]),
+                                                    __float_as_uint(acc[2]), false, false);
+  const auto s13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[1]),
+                                                    __float_as_uint(acc[3]), false, false);
+  // p0: tile 0 (lanes 0-31) / tile 2 (lanes 32-63) summed over g and g^2; p1: tiles 1 / 3
+  const float p0 = __uint_as_float(s02[0]) + __uint_as_float(s02[1]);
+  const float p1 = __uint_as_float(s13[0]) + __uint_as_float(s13[1]);
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1),
+                                                  false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 }  // namespace mxidx
