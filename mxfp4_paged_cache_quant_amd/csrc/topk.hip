@@ -35,11 +35,17 @@ constexpr int kMaxWaves = kMaxThreads / kWave;
 constexpr int kCandPairs = 8192;   // (key, column) pairs in dynamic LDS (64 KB), long rows only
 constexpr int kWaveHistBins = 2048;
 
+constexpr int kFewCand = 64;       // threshold bins this small are resolved by ranking
+
 template <int BINS>
 struct Shared {
   uint32_t hist[BINS];
   uint32_t wave_tot[2][2 * kMaxWaves];  // ping-pong: consecutive scans need one barrier each
-  uint32_t sel[2];                      // selected bin, count strictly above it
+  uint32_t sel[3];                      // selected bin, count strictly above it, count in it
+  // few-candidate resolve (zeroed at kernel start)
+  uint32_t ccount;
+  uint32_t ckey[kFewCand], ccol[kFewCand], crank[kFewCand], cgt[kFewCand];
+  uint32_t res[2];
 };
 
 // Exclusive prefix sum over the workgroup in thread order; also returns the
@@ -91,6 +97,7 @@ __device__ void select_bin(Shared<BINS>& s, uint32_t need, int parity) {
     if (run < need && run + c[j] >= need) {
       s.sel[0] = (uint32_t)(top - j);
       s.sel[1] = run;
+      s.sel[2] = c[j];
     }
     run += c[j];
     s.hist[top - j] = 0;                          // every read of the histogram is done
@@ -174,6 +181,56 @@ __device__ void refine_regs(Shared<BINS>& s, const uint32_t (&key)[E], int nv, u
   need_ties = need;
 }
 
+// The threshold bin (keys with u >> shift == prefix) holds at most kFewCand
+// keys and the `need`-th largest of them is the k-th of the row: gather the
+// bin's (key, column) pairs and rank them directly -- rank = number of bin
+// keys before it in (key desc, column asc) order, counted pairwise by the
+// whole workgroup -- instead of histogramming the remaining digits.  Returns
+// u_t and the number of keys equal to it to take, as refine_regs does.
+template <int NT, int BINS, int E>
+__device__ void resolve_few(Shared<BINS>& s, const uint32_t (&key)[E], int nv, uint32_t col0,
+                            uint32_t kmin, int shift, uint32_t prefix, uint32_t need,
+                            uint32_t& u_t, uint32_t& need_ties) {
+  constexpr int kPerCand = NT / kFewCand;        // threads per candidate
+  constexpr int kJ = kFewCand / kPerCand;        // comparisons per thread
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t u = key[e] - kmin;
+    if (e < nv && (u >> shift) == prefix) {
+      const uint32_t slot = atomicAdd(&s.ccount, 1u);
+      s.ckey[slot] = key[e];
+      s.ccol[slot] = col0 + (uint32_t)e;
+    }
+  }
+  __syncthreads();
+  const uint32_t cnt = s.ccount;
+  const uint32_t i = threadIdx.x / kPerCand;
+  const uint32_t j0 = (threadIdx.x % kPerCand) * kJ;
+  if (i < cnt) {
+    const uint32_t ki = s.ckey[i], ci = s.ccol[i];
+    uint32_t before = 0, greater = 0;
+#pragma unroll
+    for (int jj = 0; jj < kJ; ++jj) {
+      const uint32_t j = j0 + jj;
+      if (j < cnt) {
+        const uint32_t kj = s.ckey[j], cj = s.ccol[j];
+        before += (kj > ki || (kj == ki && cj < ci)) ? 1u : 0u;
+        greater += kj > ki ? 1u : 0u;
+      }
+    }
+    if (before) atomicAdd(&s.crank[i], before);
+    if (greater) atomicAdd(&s.cgt[i], greater);
+  }
+  __syncthreads();
+  if (threadIdx.x < cnt && s.crank[threadIdx.x] == need - 1) {   // exactly one candidate
+    s.res[0] = s.ckey[threadIdx.x] - kmin;
+    s.res[1] = need - s.cgt[threadIdx.x];
+  }
+  __syncthreads();
+  u_t = s.res[0];
+  need_ties = s.res[1];
+}
+
 // Ordered output of register-held candidates (thread t holds consecutive
 // candidates, so thread order is candidate order): every u > u_t, and the
 // first need_ties with u == u_t, at out[base + rank].  Candidates are the
@@ -242,6 +299,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   int parity = 0;
+  if (threadIdx.x < kFewCand) {                 // read only after later barriers
+    s.crank[threadIdx.x] = 0;
+    s.cgt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) s.ccount = 0;
+  }
 
   if (n <= C) {
     // ---- the whole row in registers: one read ----
@@ -272,7 +334,27 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
     const uint32_t range = kmax - kmin;
     const int L = range ? 32 - __clz(range) : 0;     // bit length of the key range
     uint32_t u_t = 0, need_ties = (uint32_t)k;        // all keys equal: the lowest columns
-    if (L > 0) refine_regs<NT>(s, key, nv, kmin, L, 0u, (uint32_t)k, parity, u_t, need_ties);
+    if (L > 0) {
+      // first digit over the whole range, then either a direct ranking of a
+      // small threshold bin or the remaining digits
+      constexpr int D = digit_bits<BINS>();
+      const int nsh = L > D ? L - D : 0;
+      hist_level(s, key, nv, kmin, L, 0u, nsh, (1u << (L - nsh)) - 1u);
+      __syncthreads();
+      select_bin<NT>(s, (uint32_t)k, parity);
+      parity ^= 1;
+      const uint32_t need = (uint32_t)k - s.sel[1];
+      const uint32_t bin = s.sel[0];
+      if (nsh == 0) {
+        u_t = bin;
+        need_ties = need;
+      } else if (s.sel[2] <= (uint32_t)kFewCand) {
+        resolve_few<NT>(s, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x), kmin, nsh, bin, need,
+                        u_t, need_ties);
+      } else {
+        refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
+      }
+    }
     uint32_t gr = 0, tr = 0;
     emit_regs<NT, false>(s, key, key, lo + (int64_t)E * threadIdx.x, nv, kmin, u_t, need_ties,
                          false, 0, 0u, out, 0u, k, parity, gr, tr);

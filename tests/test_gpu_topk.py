@@ -108,3 +108,21 @@ def test_topk_many_rows_wide_threshold_bin():
     bits = np.float32(1.5).view(np.uint32) + rng.integers(0, 1 << 20, size=(rows, n)).astype(np.uint32)
     x = bits.view(np.float32).copy()
     _check(x, np.zeros(rows, np.int32), np.full(rows, n, np.int32), k)
+
+
+@pytest.mark.parametrize("n,k,width", [(8192, 2048, 20), (3000, 700, 5), (16384, 2048, 64), (8192, 1, 3)])
+def test_topk_ties_across_the_kth_value(n, k, width):
+    # `width` equal values straddle rank k (a small threshold bin whose ties
+    # are broken by column), in rows of distinct values otherwise
+    rng = np.random.default_rng(n + k + width)
+    R = 4
+    x = rng.standard_normal((R, n)).astype(np.float32)
+    for r in range(R):
+        order = np.argsort(-x[r], kind="stable")
+        lo_rank = max(0, k - 1 - width // 2)
+        x[r, order[lo_rank:lo_rank + width]] = x[r, order[lo_rank]]
+    ks = np.zeros(R, np.int32)
+    ke = np.full(R, n, np.int32)
+    ks[1] = 7
+    ke[2] = n - 5
+    _check(x, ks, ke, k)
