@@ -19,7 +19,10 @@
 //   * n <= threads*E: one HBM read.  The key range [kmin, kmax] is reduced
 //     first and the digits are taken from u = key - kmin, starting at the top
 //     bit of kmax - kmin, so the first histogram spreads the row over the bins
-//     (fixed top-bit digits would pile similar logits into a few bins);
+//     (fixed top-bit digits would pile similar logits into a few bins).  When
+//     the first level's threshold bin holds at most 64 keys (the usual case:
+//     2048 bins over the row's own range), those keys are ranked directly
+//     instead of histogramming the remaining digits;
 //   * longer rows, in chunks of threads*E: a first read histograms the top
 //     digit of the keys, a second read writes the keys above the threshold bin
 //     directly and compacts the bin's (key, column) pairs into LDS (up to
