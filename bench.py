@@ -4,8 +4,9 @@
 Decode step (the headline): batch 16, one query token each, 8192-token
 contexts, 32 index heads, head_dim 128, MXFP4 cache (page 64, permuted block
 table), top-2048.  One step = insert of the 16 new tokens' K (quantize +
-scatter) -> MXFP4 quantization of the 16x32 query rows -> paged logits over
-all 131072 cached tokens -> top-2048 per row.  Metric: scored cache tokens per
+scatter) and MXFP4 quantization of the 16x32 query rows (one launch,
+idx_insert_quantize) -> paged logits over all 131072 cached tokens ->
+top-2048 per row.  Metric: scored cache tokens per
 second = sum over rows of the visible context / step time.
 
 Timing: the step is captured in HIP graphs; W untimed warm-up steps, then
@@ -112,8 +113,8 @@ def decode_ops(case):
     import mxfp4_paged_cache_quant_amd as mx
     W, K = case["width"], case["topk"]
     return {
-        "insert": lambda s: mx.insert(s.k_new, s.slot_new, s.cache),
-        "quantize": lambda s: mx.quantize(s.q, s.qv, s.qs),
+        # the new tokens' K into the cache and the query rows to MXFP4, one launch
+        "insert_quantize": lambda s: mx.insert_quantize(s.k_new, s.slot_new, s.cache, s.q, s.qv, s.qs),
         # clean=False: the top-k reads each row only up to its visible end
         "logits_paged": lambda s: mx.logits_paged(s.qv, s.qs, s.w, s.cache, s.bt, s.ctx, 1, W,
                                                   logits=s.logits, clean=False),
@@ -163,7 +164,7 @@ def bench_decode(args, case):
     import torch
     sets = build_decode_sets(case, args.sets)
     ops = decode_ops(case)
-    order = ["insert", "quantize", "logits_paged", "topk"]
+    order = ["insert_quantize", "logits_paged", "topk"]
 
     def step_fns(lo, hi):
         return [(lambda s=s, name=name: ops[name](s)) for s in sets[lo:hi] for name in order]
@@ -413,6 +414,7 @@ KERNEL_SOURCES = {          # kernel-name prefix -> the source it is compiled fr
     "logits_prefill_kernel": "logits_prefill.hip",
     "topk_kernel": "topk.hip",
     "mxfp4_rows_kernel": "insert.hip",
+    "insert_quantize_kernel": "insert.hip",
     "gather_kernel": "gather.hip",
 }
 
@@ -530,15 +532,14 @@ def main():
 
     B, H, L = len(case["context_lens"]), case["H"], int(case["context_lens"][0])
     alg_bytes = {
-        "insert": B * (256 + 8 + 68),
-        "quantize": B * H * (256 + 68),
+        "insert_quantize": B * (256 + 8 + 68) + B * H * (256 + 68),
         "logits_paged": scored * (68 + 4) + B * H * (68 + 4),
         "topk": scored * 4 + B * case["topk"] * 4,
     }
     dominant = max(per_kernel, key=per_kernel.get)
     achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-6) / 1e9
-    dom_kernel = {"insert": "mxfp4_rows_kernel<Bf16In, true>", "quantize": "mxfp4_rows_kernel<Bf16In, false>",
-                  "logits_paged": "logits_paged_kernel", "topk": "topk_kernel"}[dominant]
+    dom_kernel = {"insert_quantize": "insert_quantize_kernel", "logits_paged": "logits_paged_kernel",
+                  "topk": "topk_kernel"}[dominant]
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic("decode", dom_kernel),
@@ -592,7 +593,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": case["name"], "batch": B, "context": L, "heads": H,
                    "head_dim": 128, "page_size": 64, "next_n": 1, "topk": case["topk"],
-                   "step": "insert(16 new tokens)+quantize(q)+logits_paged+topk",
+                   "step": "insert_quantize(16 new tokens' K, 512 q rows; one launch)+logits_paged+topk",
                    "rotating_sets": args.sets, "hip_graph": True, "parallelism": "none"},
         "roofline": roofline,
         "kernels": kernels,

@@ -123,6 +123,23 @@ int idx_insert(const void* k, int dtype, int64_t num_tokens, int64_t k_row_strid
                const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
                int page_size, hipStream_t stream);
 
+/* idx_insert_quantize -- idx_insert and idx_quantize in one launch: the new
+ * tokens' K rows into their cache slots and the query rows into contiguous
+ * MXFP4, the two encodes of a decode step (P1 "Changes": K quant-and-cache;
+ * P3 "forward_cuda": FP4 q).  For callers whose decode step is launch-bound.
+ *   k, k_dtype, num_tokens, k_row_stride, slot_mapping, cache, num_pages,
+ *   page_size: as for idx_insert (num_tokens may be 0).
+ *   q, q_dtype, q_rows, q_row_stride, q_values, q_scales: as x, dtype, rows,
+ *   row_stride, values, scales of idx_quantize (q_rows may be 0).
+ * Every argument is checked as the two calls check it; the outputs are
+ * byte-identical to idx_insert followed by idx_quantize.  The query output must
+ * not overlap the cache. */
+int idx_insert_quantize(const void* k, int k_dtype, int64_t num_tokens, int64_t k_row_stride,
+                        const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
+                        int page_size, const void* q, int q_dtype, int64_t q_rows,
+                        int64_t q_row_stride, uint8_t* q_values, uint8_t* q_scales,
+                        hipStream_t stream);
+
 /* idx_gather -- paged cache -> contiguous MXFP4 K (the cp_gather that P1's
  * live-validation comment names as sharing the cache layout).
  *   block_table:    [batch, bt_row_stride] int32 page ids.

@@ -14,7 +14,7 @@ import os
 
 __all__ = [
     "MxidxError", "lib", "lib_path", "version", "init",
-    "quantize", "insert", "gather", "logits_prefill", "logits_paged", "topk",
+    "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged", "topk",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
 ]
 
@@ -42,6 +42,8 @@ EXPORTS = {
     "idx_init": (_int, [_int]),
     "idx_quantize": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "idx_insert": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int, _c_void_p]),
+    "idx_insert_quantize": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int,
+                                   _c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "idx_gather": (_int, [_c_void_p, _i64, _int, _c_void_p, _i64, _c_void_p, _c_void_p, _int, _i64,
                           _i64, _c_void_p, _c_void_p, _c_void_p]),
     "idx_logits_prefill": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -122,14 +124,16 @@ def _rows_view(x, name):
     """[..., 128] tensor with unit inner stride -> (rows, row_stride, dtype code)."""
     torch = _torch()
     _dev(x, name)
-    if x.shape[-1] != HEAD_DIM or x.stride(-1) != 1:
-        raise MxidxError(f"{name} must be [..., 128] with a contiguous last dim")
     if x.dtype == torch.bfloat16:
         code = IDX_BF16
     elif x.dtype == torch.float32:
         code = IDX_F32
     else:
         raise MxidxError(f"{name} must be bfloat16 or float32")
+    if x.dim() >= 1 and x.shape[-1] == HEAD_DIM and x.numel() == 0:
+        return 0, HEAD_DIM, code                   # no rows: strides are irrelevant
+    if x.shape[-1] != HEAD_DIM or x.stride(-1) != 1:
+        raise MxidxError(f"{name} must be [..., 128] with a contiguous last dim")
     rows = x.numel() // HEAD_DIM
     if x.dim() == 1:
         stride = HEAD_DIM
@@ -174,6 +178,35 @@ def insert(k, slot_mapping, cache, stream=None):
     _check(lib().idx_insert(_ptr(k), code, rows, stride, _ptr(slot_mapping), _ptr(cache), num_pages,
                             PAGE_SIZE, _stream(stream)), "idx_insert")
     return cache
+
+
+def insert_quantize(k, slot_mapping, cache, q, q_values=None, q_scales=None, stream=None):
+    """insert(k, slot_mapping, cache) and quantize(q) in one launch; returns (q_values, q_scales)."""
+    torch = _torch()
+    rows, stride, code = _rows_view(k, "k")
+    q_rows, q_stride, q_code = _rows_view(q, "q")
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(cache, "cache", torch.uint8)
+    if slot_mapping.numel() != rows or not slot_mapping.is_contiguous():
+        raise MxidxError("slot_mapping must be a contiguous int64 [N]")
+    if not cache.is_contiguous() or cache.numel() % (PAGE_SIZE * ROW_BYTES) != 0:
+        raise MxidxError("cache must be a contiguous uint8 [num_pages, 64*68]")
+    lead = tuple(q.shape[:-1])
+    if q_values is None:
+        q_values = torch.empty(lead + (CODE_BYTES,), dtype=torch.uint8, device=q.device)
+    if q_scales is None:
+        q_scales = torch.empty(lead + (SCALE_BYTES,), dtype=torch.uint8, device=q.device)
+    _dev(q_values, "q_values", torch.uint8)
+    _dev(q_scales, "q_scales", torch.uint8)
+    if q_values.numel() != q_rows * CODE_BYTES or q_scales.numel() != q_rows * SCALE_BYTES or \
+            not q_values.is_contiguous() or not q_scales.is_contiguous():
+        raise MxidxError("q_values/q_scales must be contiguous [rows, 64] / [rows, 4]")
+    num_pages = cache.numel() // (PAGE_SIZE * ROW_BYTES)
+    _check(lib().idx_insert_quantize(_ptr(k), code, rows, stride, _ptr(slot_mapping), _ptr(cache),
+                                     num_pages, PAGE_SIZE, _ptr(q), q_code, q_rows, q_stride,
+                                     _ptr(q_values), _ptr(q_scales), _stream(stream)),
+           "idx_insert_quantize")
+    return q_values, q_scales
 
 
 def gather(cache, block_table, seq_lens, cu_seq_offsets, max_seq_len, total_tokens,

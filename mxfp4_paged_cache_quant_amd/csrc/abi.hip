@@ -57,7 +57,7 @@ int check_rows_input(const void* x, int dtype, int64_t rows, int64_t row_stride)
 
 extern "C" {
 
-int idx_version(void) { return 100; }
+int idx_version(void) { return 101; }
 
 const char* idx_strerror(int status) {
   switch (status) {
@@ -99,6 +99,29 @@ int idx_insert(const void* k, int dtype, int64_t num_tokens, int64_t k_row_strid
   if ((st = gate_current()) != IDX_OK) return st;
   return launched(mxidx::launch_insert(k, dtype == IDX_F32, num_tokens, k_row_stride, slot_mapping,
                                        cache, num_pages, stream));
+}
+
+int idx_insert_quantize(const void* k, int k_dtype, int64_t num_tokens, int64_t k_row_stride,
+                        const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
+                        int page_size, const void* q, int q_dtype, int64_t q_rows,
+                        int64_t q_row_stride, uint8_t* q_values, uint8_t* q_scales,
+                        hipStream_t stream) {
+  // exactly the checks of idx_insert and of idx_quantize
+  int st = check_rows_input(k, k_dtype, num_tokens, k_row_stride);
+  if (st != IDX_OK) return st;
+  if ((st = check_rows_input(q, q_dtype, q_rows, q_row_stride)) != IDX_OK) return st;
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0) return IDX_ERR_ARG;
+  if (num_tokens > 0) {
+    if (!slot_mapping || !aligned(slot_mapping, 8)) return IDX_ERR_ARG;
+    if (num_pages > 0 && (!cache || !aligned(cache, 4))) return IDX_ERR_ARG;
+  }
+  if (q_rows > 0 && (!q_values || !q_scales || !aligned(q_values, 4))) return IDX_ERR_ARG;
+  if (num_tokens == 0 && q_rows == 0) return IDX_OK;
+  if ((st = gate_current()) != IDX_OK) return st;
+  return launched(mxidx::launch_insert_quantize(k, k_dtype == IDX_F32, num_tokens, k_row_stride,
+                                                slot_mapping, cache, num_pages, q,
+                                                q_dtype == IDX_F32, q_rows, q_row_stride, q_values,
+                                                q_scales, stream));
 }
 
 int idx_gather(const uint8_t* cache, int64_t num_pages, int page_size, const int32_t* block_table,

@@ -91,9 +91,41 @@ struct F32In {
 
 constexpr int kRowsPerBlock = 16;   // 256 threads, 16 lanes per row
 
+// Encode row `row` of x (16 lanes, lane `sub` takes elements 8*sub..8*sub+7)
+// into 64 code bytes at cdst and 4 scale bytes at sdst.
+template <typename In>
+__device__ __forceinline__ void encode_row(const void* __restrict__ x, int64_t row, int64_t stride,
+                                           int sub, uint8_t* cdst, uint8_t* sdst) {
+  In in;
+  in.load(x, row, stride, sub);
+  uint32_t a = in.amax_bits();
+  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 2));
+  const int E = block_exponent(a);
+  // An all-zero block needs no division (its codes are the sign bits alone);
+  // dividing by 1 keeps the subnormal scale out of the common case.
+  const float scale = (a == 0u) ? 1.0f : pow2f(E);
+  const uint32_t codes = in.encode(scale);
+  *reinterpret_cast<uint32_t*>(cdst + 4 * sub) = codes;
+  if ((sub & 3) == 0) sdst[sub >> 2] = (uint8_t)(E + 127);
+}
+
+// Paged destination of a slot: codes at page*4352 + off*64, scales at
+// page*4352 + 4096 + off*4.  False (write nothing) unless 0 <= slot < num_slots.
+__device__ __forceinline__ bool slot_dst(const int64_t* __restrict__ slot_mapping, int64_t row,
+                                         int64_t num_slots, uint8_t* cache, uint8_t*& cdst,
+                                         uint8_t*& sdst) {
+  const int64_t slot = slot_mapping[row];
+  if (slot < 0 || slot >= num_slots) return false;
+  const int64_t page = slot / kPage;
+  const int64_t off = slot % kPage;
+  cdst = cache + page * kPageBytes + off * kCodeBytes;
+  sdst = cache + page * kPageBytes + kPageCodeBytes + off * kScaleBytes;
+  return true;
+}
+
 // kPaged = false: row r -> values[r*64], scales[r*4].
-// kPaged = true:  row r -> slot = slot_mapping[r] (skipped unless 0 <= slot < num_slots),
-//                 codes at page*4352 + off*64, scales at page*4352 + 4096 + off*4.
+// kPaged = true:  row r -> the paged slot slot_mapping[r] (see slot_dst).
 template <typename In, bool kPaged>
 __global__ __launch_bounds__(256) void mxfp4_rows_kernel(const void* __restrict__ x, int64_t rows,
                                                           int64_t stride,
@@ -107,28 +139,40 @@ __global__ __launch_bounds__(256) void mxfp4_rows_kernel(const void* __restrict_
     uint8_t* cdst;
     uint8_t* sdst;
     if constexpr (kPaged) {
-      const int64_t slot = slot_mapping[row];
-      if (slot < 0 || slot >= num_slots) continue;   // same decision for all 16 lanes of the row
-      const int64_t page = slot / kPage;
-      const int64_t off = slot % kPage;
-      cdst = dst_codes + page * kPageBytes + off * kCodeBytes;
-      sdst = dst_codes + page * kPageBytes + kPageCodeBytes + off * kScaleBytes;
+      // same decision for all 16 lanes of the row
+      if (!slot_dst(slot_mapping, row, num_slots, dst_codes, cdst, sdst)) continue;
     } else {
       cdst = dst_codes + row * kCodeBytes;
       sdst = dst_scales + row * kScaleBytes;
     }
-    In in;
-    in.load(x, row, stride, sub);
-    uint32_t a = in.amax_bits();
-    a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-    a = max(a, (uint32_t)__shfl_xor((int)a, 2));
-    const int E = block_exponent(a);
-    // An all-zero block needs no division (its codes are the sign bits alone);
-    // dividing by 1 keeps the subnormal scale out of the common case.
-    const float scale = (a == 0u) ? 1.0f : pow2f(E);
-    const uint32_t codes = in.encode(scale);
-    *reinterpret_cast<uint32_t*>(cdst + 4 * sub) = codes;
-    if ((sub & 3) == 0) sdst[sub >> 2] = (uint8_t)(E + 127);
+    encode_row<In>(x, row, stride, sub, cdst, sdst);
+  }
+}
+
+// Both encodes of a decode step in one launch: workgroups [0, k_blocks) put
+// the K rows into their cache slots, the others write the query rows
+// contiguously.  Each part is a grid-stride loop over its own workgroups.
+template <typename KIn, typename QIn>
+__global__ __launch_bounds__(256) void insert_quantize_kernel(
+    const void* __restrict__ k, int64_t k_rows, int64_t k_stride,
+    const int64_t* __restrict__ slot_mapping, int64_t num_slots, uint8_t* __restrict__ cache,
+    int k_blocks, const void* __restrict__ q, int64_t q_rows, int64_t q_stride,
+    uint8_t* __restrict__ q_values, uint8_t* __restrict__ q_scales) {
+  const int sub = threadIdx.x & 15;
+  if ((int)blockIdx.x < k_blocks) {
+    for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4); row < k_rows;
+         row += (int64_t)k_blocks * kRowsPerBlock) {
+      uint8_t* cdst;
+      uint8_t* sdst;
+      if (!slot_dst(slot_mapping, row, num_slots, cache, cdst, sdst)) continue;
+      encode_row<KIn>(k, row, k_stride, sub, cdst, sdst);
+    }
+  } else {
+    const int64_t qb = (int64_t)blockIdx.x - k_blocks;
+    const int64_t q_blocks = (int64_t)gridDim.x - k_blocks;
+    for (int64_t row = qb * kRowsPerBlock + (threadIdx.x >> 4); row < q_rows;
+         row += q_blocks * kRowsPerBlock)
+      encode_row<QIn>(q, row, q_stride, sub, q_values + row * kCodeBytes, q_scales + row * kScaleBytes);
   }
 }
 
@@ -136,6 +180,18 @@ int grid_for_rows(int64_t rows) {
   const int64_t blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t cap = 256 * 32;   // grid-stride beyond ~32 resident blocks per CU
   return (int)(blocks < cap ? blocks : cap);
+}
+
+template <typename KIn, typename QIn>
+hipError_t launch_iq(const void* k, int64_t num_tokens, int64_t k_stride, const int64_t* slots,
+                     uint8_t* cache, int64_t num_pages, const void* q, int64_t q_rows,
+                     int64_t q_stride, uint8_t* q_values, uint8_t* q_scales, hipStream_t stream) {
+  const int kb = grid_for_rows(num_tokens);
+  const int qb = grid_for_rows(q_rows);
+  hipLaunchKernelGGL((insert_quantize_kernel<KIn, QIn>), dim3(kb + qb), dim3(256), 0, stream, k,
+                     num_tokens, k_stride, slots, num_pages * kPage, cache, kb, q, q_rows, q_stride,
+                     q_values, q_scales);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -164,6 +220,24 @@ hipError_t launch_insert(const void* k, bool f32, int64_t num_tokens, int64_t ro
     hipLaunchKernelGGL((mxfp4_rows_kernel<Bf16In, true>), dim3(grid), dim3(256), 0, stream, k,
                        num_tokens, row_stride, slot_mapping, num_slots, cache, nullptr);
   return hipGetLastError();
+}
+
+hipError_t launch_insert_quantize(const void* k, bool k_f32, int64_t num_tokens,
+                                  int64_t k_row_stride, const int64_t* slot_mapping,
+                                  uint8_t* cache, int64_t num_pages, const void* q, bool q_f32,
+                                  int64_t q_rows, int64_t q_row_stride, uint8_t* q_values,
+                                  uint8_t* q_scales, hipStream_t stream) {
+  if (k_f32 && q_f32)
+    return launch_iq<F32In, F32In>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
+                                   q_rows, q_row_stride, q_values, q_scales, stream);
+  if (k_f32)
+    return launch_iq<F32In, Bf16In>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
+                                    q_rows, q_row_stride, q_values, q_scales, stream);
+  if (q_f32)
+    return launch_iq<Bf16In, F32In>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
+                                    q_rows, q_row_stride, q_values, q_scales, stream);
+  return launch_iq<Bf16In, Bf16In>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
+                                   q_rows, q_row_stride, q_values, q_scales, stream);
 }
 
 }  // namespace mxidx

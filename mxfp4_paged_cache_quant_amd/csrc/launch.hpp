@@ -15,6 +15,12 @@ hipError_t launch_insert(const void* k, bool f32, int64_t num_tokens, int64_t ro
                          const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
                          hipStream_t stream);
 
+hipError_t launch_insert_quantize(const void* k, bool k_f32, int64_t num_tokens,
+                                  int64_t k_row_stride, const int64_t* slot_mapping,
+                                  uint8_t* cache, int64_t num_pages, const void* q, bool q_f32,
+                                  int64_t q_rows, int64_t q_row_stride, uint8_t* q_values,
+                                  uint8_t* q_scales, hipStream_t stream);
+
 hipError_t launch_gather(const uint8_t* cache, int64_t num_pages, const int32_t* block_table,
                          int64_t bt_row_stride, const int32_t* seq_lens,
                          const int64_t* cu_seq_offsets, int batch, int64_t max_seq_len,

@@ -45,7 +45,7 @@ def test_header_declarations_are_exported(L):
 
 
 def test_version_and_strerror(L):
-    assert L.idx_version() == 100
+    assert L.idx_version() == 101
     for st in range(5):
         assert L.idx_strerror(st)
     assert L.idx_strerror(99) == b"unknown status"
@@ -69,6 +69,19 @@ def test_insert_argument_validation(L):
     assert L.idx_insert(P, 0, 4, 128, P, None, 4, 64, None) == ERR_ARG    # null cache
     assert L.idx_insert(P, 0, 4, 128, P, P2, -1, 64, None) == ERR_ARG     # negative pages
     assert L.idx_insert(None, 0, 0, 128, None, None, 0, 64, None) == OK
+
+
+def test_insert_quantize_argument_validation(L):
+    f = L.idx_insert_quantize
+    assert f(P, 0, 4, 128, P, P2, 4, 32, P, 0, 8, 128, P, P2, None) == ERR_ARG   # page size != 64
+    assert f(P, 2, 4, 128, P, P2, 4, 64, P, 0, 8, 128, P, P2, None) == ERR_ARG   # bad K dtype
+    assert f(P, 0, 4, 128, P, P2, 4, 64, P, 2, 8, 128, P, P2, None) == ERR_ARG   # bad q dtype
+    assert f(P, 0, 4, 128, None, P2, 4, 64, P, 0, 8, 128, P, P2, None) == ERR_ARG  # null slots
+    assert f(P, 0, 4, 128, P, P2, 4, 64, P, 0, 8, 100, P, P2, None) == ERR_ARG   # q stride < 128
+    assert f(P, 0, 4, 128, P, P2, 4, 64, MIS, 0, 8, 128, P, P2, None) == ERR_ARG  # misaligned q
+    assert f(P, 0, 4, 128, P, P2, 4, 64, P, 0, 8, 128, None, P2, None) == ERR_ARG  # null q out
+    assert f(P, 0, 4, 128, P, P2, -1, 64, P, 0, 8, 128, P, P2, None) == ERR_ARG  # negative pages
+    assert f(None, 0, 0, 128, None, None, 0, 64, None, 0, 0, 128, None, None, None) == OK  # empty
 
 
 def test_gather_argument_validation(L):

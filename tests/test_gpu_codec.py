@@ -166,3 +166,35 @@ def test_gather_prefill_chunk_bit_exact():
     torch.cuda.synchronize()
     qc, qs = omx.quantize_rows(exact(case, "k"))
     assert np.array_equal(host(kv), qc) and np.array_equal(host(ksc), qs)
+
+
+@pytest.mark.parametrize("k_dtype,q_dtype,n_tok,q_rows", [("bf16", "bf16", 16, 512), ("f32", "bf16", 40, 3),
+                                                          ("bf16", "f32", 1, 700), ("f32", "f32", 300, 64),
+                                                          ("bf16", "bf16", 0, 33), ("bf16", "bf16", 50, 0)])
+def test_insert_quantize_matches_separate_calls_and_oracle(k_dtype, q_dtype, n_tok, q_rows):
+    rng = np.random.default_rng(n_tok * 7 + q_rows)
+
+    def draw(rows, dt):
+        x = (rng.standard_normal((rows, 128)) * 2.0 ** rng.integers(-20, 20, (rows, 1))).astype(np.float32)
+        return workloads.bf16_bits(x) if dt == "bf16" else x
+
+    def f64(a):
+        return omx.bf16_bits_to_f64(a) if a.dtype == np.uint16 else omx.f32_to_f64(a)
+
+    k, q = draw(n_tok, k_dtype), draw(q_rows, q_dtype)
+    slots = rng.permutation(5 * 64)[:n_tok].astype(np.int64)
+    if n_tok > 3:
+        slots[[1, 2]] = [-1, 5 * 64 + 9]              # no write; out of range (skipped)
+    fused = new_cache(5)
+    qv, qs = mx.insert_quantize(dev(k), dev(slots), fused, dev(q))
+    sep = new_cache(5)
+    mx.insert(dev(k), dev(slots), sep)
+    qv2, qs2 = mx.quantize(dev(q))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(fused), host(sep))
+    assert np.array_equal(host(qv), host(qv2)) and np.array_equal(host(qs), host(qs2))
+    ok = np.where(slots >= 5 * 64, -1, slots)
+    ref = opc.insert(np.full((5, 64 * 68), CANARY, np.uint8), f64(k), ok)
+    assert np.array_equal(host(fused), ref)
+    rc, rs = omx.quantize_rows(f64(q))
+    assert np.array_equal(host(qv), rc) and np.array_equal(host(qs), rs)
