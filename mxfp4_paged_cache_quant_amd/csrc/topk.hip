@@ -141,6 +141,54 @@ __device__ __forceinline__ int load_keys(const float* __restrict__ src, int64_t 
   return nv;
 }
 
+// Keys c0 + E*t + e of a chunk that lies wholly inside a 16-byte aligned row:
+// E/4 vector loads, no branch.
+template <int E>
+__device__ __forceinline__ void load_full(const float* __restrict__ src, int64_t c0,
+                                          uint32_t (&key)[E]) {
+  const float* p = src + c0 + (int64_t)E * threadIdx.x;
+  uint4 v[E / 4];
+#pragma unroll
+  for (int q = 0; q < E / 4; ++q) v[q] = *reinterpret_cast<const uint4*>(p + 4 * q);
+#pragma unroll
+  for (int q = 0; q < E / 4; ++q) {
+    key[4 * q + 0] = f32_key(v[q].x);
+    key[4 * q + 1] = f32_key(v[q].y);
+    key[4 * q + 2] = f32_key(v[q].z);
+    key[4 * q + 3] = f32_key(v[q].w);
+  }
+}
+
+// Runs body(c0, key, nv) over the chunks of C = NT*E keys of src[0, n) in
+// order.  The full chunks of an aligned row are double-buffered: the next
+// chunk's loads are issued before a chunk is processed (the refill is
+// unconditional -- past the last full chunk it re-reads that chunk -- so the
+// waits on it are exact); a partial last chunk, and every chunk of an
+// unaligned row, use the generic loader.
+template <int NT, int E, typename Body>
+__device__ __forceinline__ void for_chunks(const float* __restrict__ src, int64_t n, bool vec,
+                                           Body&& body) {
+  constexpr int64_t C = (int64_t)NT * E;
+  const int64_t nfull = vec ? n / C : 0;
+  if (nfull > 0) {
+    uint32_t ka[E], kb[E];
+    load_full<E>(src, 0, ka);
+    int64_t i = 0;
+    for (; i + 1 < nfull; i += 2) {
+      load_full<E>(src, (i + 1) * C, kb);
+      body(i * C, ka, E);
+      load_full<E>(src, min(i + 2, nfull - 1) * C, ka);
+      body((i + 1) * C, kb, E);
+    }
+    if (i < nfull) body(i * C, ka, E);
+  }
+  for (int64_t c0 = nfull * C; c0 < n; c0 += C) {
+    uint32_t key[E];
+    const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+    body(c0, key, nv);
+  }
+}
+
 // One radix level over register-held keys: u = key - kmin; candidates have
 // u >> shift == prefix (all when shift >= 32); digit = bits shift-1 .. nsh.
 template <int E, int BINS>
@@ -165,8 +213,8 @@ constexpr int digit_bits() {
 // entry).  Returns u_t (the exact threshold, as key - kmin) and how many keys
 // equal to it to take.
 template <int NT, int BINS, int E>
-__device__ void refine_regs(Shared<BINS>& s, const uint32_t (&key)[E], int nv, uint32_t kmin,
-                            int shift, uint32_t prefix, uint32_t need, int& parity, uint32_t& u_t,
+__device__ __forceinline__ void refine_regs(Shared<BINS>& s, const uint32_t (&key)[E], int nv,
+                                            uint32_t kmin, int shift, uint32_t prefix, uint32_t need, int& parity, uint32_t& u_t,
                             uint32_t& need_ties) {
   constexpr int D = digit_bits<BINS>();
   while (shift > 0) {
@@ -191,7 +239,7 @@ __device__ void refine_regs(Shared<BINS>& s, const uint32_t (&key)[E], int nv, u
 // whole workgroup -- instead of histogramming the remaining digits.  Returns
 // u_t and the number of keys equal to it to take, as refine_regs does.
 template <int NT, int BINS, int E>
-__device__ void resolve_few(Shared<BINS>& s, const uint32_t (&key)[E], int nv, uint32_t col0,
+__device__ __forceinline__ void resolve_few(Shared<BINS>& s, const uint32_t (&key)[E], int nv, uint32_t col0,
                             uint32_t kmin, int shift, uint32_t prefix, uint32_t need,
                             uint32_t& u_t, uint32_t& need_ties) {
   constexpr int kPerCand = NT / kFewCand;        // threads per candidate
@@ -376,13 +424,11 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
     for (int i = lane; i < kWaveHistBins; i += kWave) wh[i] = 0;
   clear_hist<NT>(s);
   __syncthreads();
-  for (int64_t c0 = 0; c0 < n; c0 += C) {
-    uint32_t key[E];
-    const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+  for_chunks<NT, E>(src, n, vec, [&](int64_t, const uint32_t (&key)[E], int nv) {
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (e < nv) atomicAdd(&wh[key[e] >> S1], 1u);
-  }
+  });
   __syncthreads();
   if (kWaveHist) {
     for (int b = threadIdx.x; b < kWaveHistBins; b += NT) {
@@ -404,9 +450,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
     // Pass 2: keys above bin1 go straight out; bin1's keys become candidates
     // (stored while they fit; their count decides the path afterwards).
     uint32_t gbase = 0, cbase = 0;
-    for (int64_t c0 = 0; c0 < n; c0 += C) {
-      uint32_t key[E];
-      const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+    for_chunks<NT, E>(src, n, vec, [&](int64_t c0, const uint32_t (&key)[E], int nv) {
       uint32_t cg = 0, cq = 0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -435,7 +479,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       }
       gbase += total & 0xffffu;
       cbase += total >> 16;
-    }
+    });
     m = cbase;
     __syncthreads();
   }
