@@ -288,6 +288,18 @@ def bench_long_decode():
     t_lgc = None if EAGER else time_fn(lg_clean, 10, 4)
     t_lg = time_fn(lg, 10, 4)
     t_tk = time_fn(tk, 10, 4)
+    # multi-token decode (next_n = 2): the same cache, two query rows per sequence
+    # (seeded N(0,1) bf16 q drawn on the device); rows see L-1 and L tokens
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20)
+    q2 = torch.randn((2 * B, H, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    w2 = torch.rand((2 * B, H), generator=gen, device="cuda")
+    qv2, qs2 = mx.quantize(q2)
+    logits2 = torch.empty((2 * B, W), dtype=torch.float32, device="cuda")
+    lg2 = lambda: mx.logits_paged(qv2, qs2, w2, cache, bt, ctx, 2, W, logits=logits2, clean=False)  # noqa: E731
+    lg2()
+    torch.cuda.synchronize()
+    t_lg2 = None if EAGER else time_fn(lg2, 10, 4)
     b_ins = N * (256 + 8 + 68)
     b_lg = N * 72 + B * H * 72
     b_tk = N * 4 + B * case["topk"] * 4
@@ -297,6 +309,8 @@ def bench_long_decode():
         "logits_paged_us": round(t_lg, 1), "logits_paged_gbs": round(b_lg / t_lg / 1e3, 1),
         "logits_paged_frac_hbm": round(b_lg / t_lg / 1e3 / HBM_PEAK_GBS, 4),
         "logits_paged_clean_us": None if t_lgc is None else round(t_lgc, 1),
+        "mtp2_logits_paged_us": None if t_lg2 is None else round(t_lg2, 1),
+        "mtp2_scored_pairs_per_s": None if t_lg2 is None else round((2 * N - B) / (t_lg2 * 1e-6), 1),
         "topk_us": round(t_tk, 1), "topk_gbs": round(b_tk / t_tk / 1e3, 1),
         "decode_step_us": round(t_lg + t_tk, 1),
         "scored_tokens_per_s": round(N / ((t_lg + t_tk) * 1e-6), 1),

@@ -29,8 +29,10 @@
 //    xor-shuffles combine the four lane groups' partial sums, after which
 //    lane l owns token l of the page and the wave stores 64 consecutive floats.
 //  * Vector memory counters retire in issue order, so a wait for a load also
-//    waits for every store issued before it: for single-row decode the logit
-//    stores are issued after the wave's last load.
+//    waits for every store issued before it: for up to NN query rows per
+//    sequence (NN * heads/16 <= 8) every row's query is loaded up front and
+//    all logit stores are issued after the wave's last load; more rows take a
+//    general loop (one row at a time).
 #include "common.hpp"
 #include "launch.hpp"
 #include "logits_reduce.hpp"
@@ -95,7 +97,9 @@ __device__ __forceinline__ float page_score(const PageRegs& pg, const QueryRegs<
   return reduce_tiles(acc);
 }
 
-template <int NH, bool kOneRow>
+// NN > 0: exactly NN query rows per sequence, all held in registers;
+// NN == 0: any next_n, one row at a time.
+template <int NH, int NN>
 __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     const uint8_t* __restrict__ q_values, const uint8_t* __restrict__ q_scales,
     const float* __restrict__ weights, const uint8_t* __restrict__ cache, int64_t num_pages,
@@ -122,8 +126,11 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::"v"(bt_lane));   // keeps the table load here, not sunk past the branch below
   const int64_t ctx = (int32_t)__builtin_amdgcn_readfirstlane(ctx_raw);
-  QueryRegs<NH> q0;
-  if (kOneRow) q0 = load_query<NH>(q_values, q_scales, weights, row0, g, n);
+  constexpr int kRowsHeld = NN > 0 ? NN : 1;
+  QueryRegs<NH> qr[kRowsHeld];
+  if (NN > 0)
+#pragma unroll
+    for (int i = 0; i < kRowsHeld; ++i) qr[i] = load_query<NH>(q_values, q_scales, weights, row0 + i, g, n);
   // context lengths beyond the row width are a precondition violation; clamp so
   // that no store leaves the row
   const int64_t L = min(ctx, width);
@@ -170,13 +177,17 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
   }
   __builtin_amdgcn_sched_barrier(0);   // every page load issues before any compute
 
-  if (kOneRow) {
-    float out[kPagesPerWave];
+  if (NN > 0) {
+    float out[kRowsHeld][kPagesPerWave];
 #pragma unroll
-    for (int p = 0; p < kPagesPerWave; ++p) out[p] = page_score<NH>(pg[p], q0, lane);
+    for (int i = 0; i < kRowsHeld; ++i)
 #pragma unroll
-    for (int p = 0; p < kPagesPerWave; ++p)
-      if (page_ok[p]) store(row0, (lp0 + p) * kPage, L, out[p]);
+      for (int p = 0; p < kPagesPerWave; ++p) out[i][p] = page_score<NH>(pg[p], qr[i], lane);
+#pragma unroll
+    for (int i = 0; i < kRowsHeld; ++i)
+#pragma unroll
+      for (int p = 0; p < kPagesPerWave; ++p)
+        if (page_ok[p]) store(row0 + i, (lp0 + p) * kPage, L - NN + i + 1, out[i][p]);
   } else {
     for (int i = 0; i < next_n; ++i) {
       const int64_t r = row0 + i;
@@ -196,12 +207,31 @@ hipError_t launch_nh(const uint8_t* qv, const uint8_t* qs, const float* w, const
                      hipStream_t stream) {
   const int64_t pages = (width + kPage - 1) / kPage;
   const dim3 grid((unsigned)((pages + kPagesPerWave - 1) / kPagesPerWave), (unsigned)B);
-  if (next_n == 1)
-    hipLaunchKernelGGL((logits_paged_kernel<NH, true>), grid, dim3(kWave), 0, stream, qv, qs, w,
-                       cache, num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean);
-  else
-    hipLaunchKernelGGL((logits_paged_kernel<NH, false>), grid, dim3(kWave), 0, stream, qv, qs, w,
-                       cache, num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean);
+#define MXIDX_PAGED_ROWS(nn)                                                                     \
+  hipLaunchKernelGGL((logits_paged_kernel<NH, nn>), grid, dim3(kWave), 0, stream, qv, qs, w, cache, \
+                     num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean)
+  // rows held in registers while rows * NH <= 8 (the query operands of 8 head groups)
+  bool held = true;
+  if (next_n == 1) {
+    MXIDX_PAGED_ROWS(1);
+  } else if constexpr (NH <= 4) {
+    if (next_n == 2) {
+      MXIDX_PAGED_ROWS(2);
+    } else if constexpr (NH <= 2) {
+      if (next_n == 3)
+        MXIDX_PAGED_ROWS(3);
+      else if (next_n == 4)
+        MXIDX_PAGED_ROWS(4);
+      else
+        held = false;
+    } else {
+      held = false;
+    }
+  } else {
+    held = false;
+  }
+  if (!held) MXIDX_PAGED_ROWS(0);
+#undef MXIDX_PAGED_ROWS
   return hipGetLastError();
 }
 

@@ -45,7 +45,11 @@ def test_paged_tiny():
                                            (128, 2, [100, 17]),
                                            (48, 16, [40, 200]),
                                            (32, 1, [0, 5, 0, 700, 64, 0, 1]),
-                                           (32, 2, list(np.random.default_rng(5).integers(0, 1500, 300)))])
+                                           (32, 2, list(np.random.default_rng(5).integers(0, 1500, 300))),
+                                           (16, 3, [3, 64, 130, 1, 2, 700]),
+                                           (64, 2, [2, 65, 129, 1000]),
+                                           (48, 2, [127, 128, 1]),
+                                           (32, 4, [4, 3, 0, 64, 67, 300])])
 def test_paged_ragged_heads_and_next_n(H, next_n, lens):
     case = workloads.decode_case(H * 7 + next_n, seq_lens=lens, H=H, next_n=next_n, spare_pages=2,
                                  width=max(lens) + 37)
