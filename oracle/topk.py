@@ -47,3 +47,51 @@ def kth_value(logits_row, ks, ke, k):
     if len(vals) == 0:
         return None
     return vals[min(k, len(vals)) - 1]
+
+
+def shard_to_global(local, rank, world, interleave):
+    """Global position of local position ``local`` on context-parallel rank
+    ``rank`` of ``world``: the sequence's tokens are dealt to the ranks
+    round-robin in runs of ``interleave`` consecutive positions (the
+    decode-context-parallel layout named by P3 "SparseAttnIndexerKpool":
+    dcp_rank, dcp_world_size, cp_kv_cache_interleave_size; the formula is the
+    reading taken here).  Run j of rank r covers global positions
+    (j*world + r)*interleave .. +interleave-1."""
+    local = np.asarray(local, dtype=np.int64)
+    return (local // interleave) * (interleave * world) + rank * interleave + local % interleave
+
+
+def global_to_shard(pos, world, interleave):
+    """Inverse of shard_to_global: (rank, local position) of global positions."""
+    pos = np.asarray(pos, dtype=np.int64)
+    run = pos // interleave
+    return run % world, (run // world) * interleave + pos % interleave
+
+
+def merge_shard_topk(values, indices, world_interleave, k):
+    """Merge per-rank top-k lists into the sequence's top-k (the exchange step
+    of context-parallel decode: every rank selects over its own share of the
+    positions, the lists are gathered and merged).
+
+    values [R, rows, kin] float32, indices [R, rows, kin] int32: rank s's
+    candidates for row r, as local positions (-1 = empty slot).
+    world_interleave: the interleave size (R is values.shape[0]).
+    Returns [rows, k] int32 global positions of the k best candidates, ranked
+    by value descending then global position ascending (-0.0 == +0.0), in
+    rank order, then -1 padding."""
+    values = np.asarray(values, dtype=np.float32)
+    indices = np.asarray(indices, dtype=np.int64)
+    R, rows, _ = values.shape
+    out = np.full((rows, k), -1, dtype=np.int32)
+    for r in range(rows):
+        v, c = [], []
+        for s in range(R):
+            ok = indices[s, r] >= 0
+            v.append(values[s, r][ok].astype(np.float64))
+            c.append(shard_to_global(indices[s, r][ok], s, R, world_interleave))
+        v = np.concatenate(v)
+        c = np.concatenate(c)
+        order = np.lexsort((c, -v))
+        n = min(k, len(order))
+        out[r, :n] = c[order[:n]]
+    return out
