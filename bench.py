@@ -300,6 +300,17 @@ def bench_long_decode():
     lg2()
     torch.cuda.synchronize()
     t_lg2 = None if EAGER else time_fn(lg2, 10, 4)
+    # context-parallel merge: 4 ranks' top-2048 lists per sequence -> global top-2048
+    # (seeded candidates on the device; local positions distinct per rank)
+    world = 4
+    mvals = torch.randn((world, B, case["topk"]), generator=gen, device="cuda")
+    mpos = torch.argsort(torch.rand((world, B, 32768), generator=gen, device="cuda"), dim=-1)
+    midx = mpos[:, :, :case["topk"]].to(torch.int32).contiguous()
+    mout = torch.empty((B, case["topk"]), dtype=torch.int32, device="cuda")
+    mg = lambda: mx.topk_merge(mvals, midx, 64, case["topk"], out=mout)  # noqa: E731
+    mg()
+    torch.cuda.synchronize()
+    t_mg = None if EAGER else time_fn(mg, 10, 4)
     b_ins = N * (256 + 8 + 68)
     b_lg = N * 72 + B * H * 72
     b_tk = N * 4 + B * case["topk"] * 4
@@ -311,6 +322,7 @@ def bench_long_decode():
         "logits_paged_clean_us": None if t_lgc is None else round(t_lgc, 1),
         "mtp2_logits_paged_us": None if t_lg2 is None else round(t_lg2, 1),
         "mtp2_scored_pairs_per_s": None if t_lg2 is None else round((2 * N - B) / (t_lg2 * 1e-6), 1),
+        "dcp4_merge_us": None if t_mg is None else round(t_mg, 1),
         "topk_us": round(t_tk, 1), "topk_gbs": round(b_tk / t_tk / 1e3, 1),
         "decode_step_us": round(t_lg + t_tk, 1),
         "scored_tokens_per_s": round(N / ((t_lg + t_tk) * 1e-6), 1),

@@ -84,6 +84,7 @@ typedef enum { IDX_BF16 = 0, IDX_F32 = 1 } idx_dtype;
 #define IDX_MAX_HEADS 128
 #define IDX_TOPK_MAX 2048
 #define IDX_MAX_DECODE_SEQS 65535
+#define IDX_MERGE_MAX_CANDIDATES 8192
 
 /* Version of this ABI (major * 100 + minor). */
 int idx_version(void);
@@ -211,6 +212,25 @@ int idx_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
 int idx_topk(const float* logits, int64_t rows, int64_t logits_row_stride,
              const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
              hipStream_t stream);
+
+/* idx_topk_merge -- merge per-rank top-k lists into a sequence's top-k: the
+ * exchange step of decode with the context split over `world` ranks (P3
+ * "SparseAttnIndexerKpool": dcp_rank, dcp_world_size,
+ * cp_kv_cache_interleave_size).  Rank s holds the sequence's positions in runs
+ * of `interleave` consecutive positions dealt round-robin, so its local
+ * position l is global position (l / interleave) * interleave * world +
+ * s * interleave + l % interleave.
+ *   values  [world, rows, k_in] fp32 (finite): rank s's candidate values for row r;
+ *   indices [world, rows, k_in] int32: their local positions, -1 = empty slot;
+ *   out_idx [rows, k] int32 out: the global positions of the min(k, valid)
+ *   best candidates, ranked by value then by lower global position
+ *   (-0.0 == +0.0), then -1.  The set is exact (with each rank's exact
+ *   top-k as input it is the unsharded top-k); the order is deterministic but
+ *   not part of the contract.
+ * 1 <= world, 1 <= k_in, world * k_in <= IDX_MERGE_MAX_CANDIDATES,
+ * 1 <= k <= 2048, interleave >= 1; global positions must be < 2^31. */
+int idx_topk_merge(const float* values, const int32_t* indices, int world, int64_t rows,
+                   int k_in, int interleave, int k, int32_t* out_idx, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,7 @@ import os
 __all__ = [
     "MxidxError", "lib", "lib_path", "version", "init",
     "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged", "topk",
+    "topk_merge",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
 ]
 
@@ -52,6 +53,8 @@ EXPORTS = {
                                 _i64, _c_void_p, _int, _int, _int, _i64, _c_void_p, _i64, _int,
                                 _c_void_p]),
     "idx_topk": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p]),
+    "idx_topk_merge": (_int, [_c_void_p, _c_void_p, _int, _i64, _int, _int, _int, _c_void_p,
+                              _c_void_p]),
 }
 
 
@@ -333,4 +336,25 @@ def topk(logits, ks, ke, k, out=None, stream=None):
         raise MxidxError("out must be a contiguous int32 [rows, k]")
     _check(lib().idx_topk(_ptr(logits), rows, logits.stride(0), _ptr(ks), _ptr(ke), k, _ptr(out),
                           _stream(stream)), "idx_topk")
+    return out
+
+
+def topk_merge(values, indices, interleave, k, out=None, stream=None):
+    """Merge per-rank top-k lists (values f32 / indices i32 [world, rows, k_in], local
+    positions, -1 empty) into global top-k positions [rows, k] (-1 padded)."""
+    torch = _torch()
+    _dev(values, "values", torch.float32)
+    _dev(indices, "indices", torch.int32)
+    if values.dim() != 3 or values.shape != indices.shape:
+        raise MxidxError("values and indices must both be [world, rows, k_in]")
+    if not values.is_contiguous() or not indices.is_contiguous():
+        raise MxidxError("values and indices must be contiguous")
+    world, rows, k_in = values.shape
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=values.device)
+    _dev(out, "out", torch.int32)
+    if out.shape != (rows, k) or not out.is_contiguous():
+        raise MxidxError("out must be a contiguous int32 [rows, k]")
+    _check(lib().idx_topk_merge(_ptr(values), _ptr(indices), world, rows, k_in, interleave, k,
+                                _ptr(out), _stream(stream)), "idx_topk_merge")
     return out

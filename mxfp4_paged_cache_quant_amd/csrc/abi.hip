@@ -57,7 +57,7 @@ int check_rows_input(const void* x, int dtype, int64_t rows, int64_t row_stride)
 
 extern "C" {
 
-int idx_version(void) { return 101; }
+int idx_version(void) { return 102; }
 
 const char* idx_strerror(int status) {
   switch (status) {
@@ -188,6 +188,19 @@ int idx_logits_paged(const uint8_t* q_values, const uint8_t* q_scales, const flo
                                              block_table, bt_row_stride, context_lens, B, next_n,
                                              H, max_context_len, logits, logits_row_stride, clean,
                                              stream));
+}
+
+int idx_topk_merge(const float* values, const int32_t* indices, int world, int64_t rows, int k_in,
+                   int interleave, int k, int32_t* out_idx, hipStream_t stream) {
+  if (world < 1 || rows < 0 || k_in < 1 || interleave < 1 || k < 1 || k > IDX_TOPK_MAX ||
+      (int64_t)world * k_in > IDX_MERGE_MAX_CANDIDATES || rows > 0x7fffffffLL)
+    return IDX_ERR_ARG;
+  if (rows == 0) return IDX_OK;
+  if (!values || !aligned(values, 4) || !indices || !aligned(indices, 4) || !out_idx) return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_topk_merge(values, indices, world, k_in, rows, interleave, k,
+                                           out_idx, stream));
 }
 
 int idx_topk(const float* logits, int64_t rows, int64_t logits_row_stride, const int32_t* ks,

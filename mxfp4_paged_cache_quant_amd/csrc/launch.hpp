@@ -40,6 +40,10 @@ hipError_t launch_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
                                int64_t max_context_len, float* logits, int64_t ld, int clean,
                                hipStream_t stream);
 
+hipError_t launch_topk_merge(const float* values, const int32_t* indices, int world, int k_in,
+                             int64_t rows, int interleave, int k, int32_t* out_idx,
+                             hipStream_t stream);
+
 hipError_t launch_topk(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                        const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream);
 

@@ -48,7 +48,7 @@ struct Shared {
   // few-candidate resolve (zeroed at kernel start)
   uint32_t ccount;
   uint32_t ckey[kFewCand], ccol[kFewCand], crank[kFewCand], cgt[kFewCand];
-  uint32_t res[2];
+  uint32_t res[3];
 };
 
 // Exclusive prefix sum over the workgroup in thread order; also returns the
@@ -237,11 +237,14 @@ __device__ __forceinline__ void refine_regs(Shared<BINS>& s, const uint32_t (&ke
 // bin's (key, column) pairs and rank them directly -- rank = number of bin
 // keys before it in (key desc, column asc) order, counted pairwise by the
 // whole workgroup -- instead of histogramming the remaining digits.  Returns
-// u_t and the number of keys equal to it to take, as refine_regs does.
-template <int NT, int BINS, int E>
-__device__ __forceinline__ void resolve_few(Shared<BINS>& s, const uint32_t (&key)[E], int nv, uint32_t col0,
-                            uint32_t kmin, int shift, uint32_t prefix, uint32_t need,
-                            uint32_t& u_t, uint32_t& need_ties) {
+// u_t and the number of keys equal to it to take, as refine_regs does, and
+// the threshold key's column in s.res[2].  Columns are col0 + e, or cols[e]
+// when kCols.
+template <int NT, bool kCols, int BINS, int E>
+__device__ __forceinline__ void resolve_few(Shared<BINS>& s, const uint32_t (&key)[E],
+                                            const uint32_t (&cols)[E], int nv, uint32_t col0,
+                                            uint32_t kmin, int shift, uint32_t prefix,
+                                            uint32_t need, uint32_t& u_t, uint32_t& need_ties) {
   constexpr int kPerCand = NT / kFewCand;        // threads per candidate
   constexpr int kJ = kFewCand / kPerCand;        // comparisons per thread
 #pragma unroll
@@ -250,7 +253,7 @@ __device__ __forceinline__ void resolve_few(Shared<BINS>& s, const uint32_t (&ke
     if (e < nv && (u >> shift) == prefix) {
       const uint32_t slot = atomicAdd(&s.ccount, 1u);
       s.ckey[slot] = key[e];
-      s.ccol[slot] = col0 + (uint32_t)e;
+      s.ccol[slot] = kCols ? cols[e] : col0 + (uint32_t)e;
     }
   }
   __syncthreads();
@@ -276,6 +279,7 @@ __device__ __forceinline__ void resolve_few(Shared<BINS>& s, const uint32_t (&ke
   if (threadIdx.x < cnt && s.crank[threadIdx.x] == need - 1) {   // exactly one candidate
     s.res[0] = s.ckey[threadIdx.x] - kmin;
     s.res[1] = need - s.cgt[threadIdx.x];
+    s.res[2] = s.ccol[threadIdx.x];
   }
   __syncthreads();
   u_t = s.res[0];
@@ -400,8 +404,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
         u_t = bin;
         need_ties = need;
       } else if (s.sel[2] <= (uint32_t)kFewCand) {
-        resolve_few<NT>(s, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x), kmin, nsh, bin, need,
-                        u_t, need_ties);
+        resolve_few<NT, false>(s, key, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x), kmin,
+                               nsh, bin, need, u_t, need_ties);
       } else {
         refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
       }
@@ -530,6 +534,161 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of per-rank top-k lists (the exchange step of context-parallel
+// decode, P3 "SparseAttnIndexerKpool": dcp_rank / dcp_world_size /
+// cp_kv_cache_interleave_size).  Rank s holds the sequence's positions in
+// runs of `interleave`, dealt round-robin; its local position l is global
+// position (l / I) * I * R + s * I + l % I.  Row r's candidates are the
+// R * k_in (value, local position) entries of all ranks (position -1 = empty
+// slot); the result is the k best by value descending, then global position
+// ascending -- the same set the unsharded top-k would give.
+//
+// One workgroup per row, E candidates per thread in rank-major order.  Empty
+// slots become (the smallest valid key, column 0xffffffff): they rank below
+// every real candidate and are never needed when at least k are valid.  The
+// threshold is found as an exact (key, column) pair: either the few-candidate
+// ranking of the first radix level's bin, or the key radix select followed by
+// a radix select over the columns of the keys tied at the threshold (lowest
+// first); the output takes every candidate at or above that pair, in
+// candidate order (deterministic).
+template <int NT, int E>
+__global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict__ values,
+                                                        const int32_t* __restrict__ indices,
+                                                        int world, int k_in, int64_t rows,
+                                                        int interleave, int k,
+                                                        int32_t* __restrict__ out_idx) {
+  constexpr int kWaves = NT / kWave;
+  constexpr int BINS = 2048;
+  __shared__ Shared<BINS> s;
+  const int64_t r = blockIdx.x;
+  int32_t* out = out_idx + r * k;
+  const int ncand = world * k_in;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  int parity = 0;
+  if (threadIdx.x < kFewCand) {                 // read only after later barriers
+    s.crank[threadIdx.x] = 0;
+    s.cgt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) s.ccount = 0;
+  }
+  clear_hist<NT>(s);                            // first read after the barriers below
+
+  // candidates c = E*t + e: rank c / k_in, slot c % k_in
+  const int first = E * (int)threadIdx.x;
+  const int nv = max(0, min(E, ncand - first));
+  uint32_t key[E], col[E];
+  uint32_t okmask = 0;
+  {
+    int sh = first / k_in, j = first - sh * k_in;
+    const int64_t span = (int64_t)interleave * world;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      key[e] = 0;
+      col[e] = 0xffffffffu;
+      if (e < nv) {
+        const int64_t off = ((int64_t)sh * rows + r) * k_in + j;
+        const int li = indices[off];
+        if (li >= 0) {
+          okmask |= 1u << e;
+          key[e] = f32_key(__float_as_uint(values[off]));
+          col[e] = (uint32_t)((li / interleave) * span + (int64_t)sh * interleave + li % interleave);
+        }
+      }
+      if (++j == k_in) {
+        j = 0;
+        ++sh;
+      }
+    }
+  }
+  // valid count and key range over the valid candidates
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((okmask >> e) & 1u) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+    }
+  for (int d = 32; d >= 1; d >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
+  }
+  if (lane == 0) {
+    s.wave_tot[1][wid] = kmin;
+    s.wave_tot[1][kMaxWaves + wid] = kmax;
+  }
+  uint32_t total_valid;
+  (void)block_scan<NT>((uint32_t)__popc(okmask), s, parity, total_valid);   // one barrier
+  parity ^= 1;
+  for (int w = 0; w < kWaves; ++w) {
+    kmin = min(kmin, s.wave_tot[1][w]);
+    kmax = max(kmax, s.wave_tot[1][kMaxWaves + w]);
+  }
+  __syncthreads();                              // the next scan rewrites wave_tot[1]
+
+  if (total_valid <= (uint32_t)k) {             // every valid candidate, then -1
+    uint32_t tot;
+    uint32_t pos = block_scan<NT>((uint32_t)__popc(okmask), s, parity, tot);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((okmask >> e) & 1u) out[pos++] = (int32_t)col[e];
+    for (uint32_t i = tot + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (!((okmask >> e) & 1u)) key[e] = kmin;   // empty: (kmin, 0xffffffff), below every valid one
+
+  uint32_t key_t, col_t;
+  bool col_known = false;
+  uint32_t u_t = 0, need_ties = (uint32_t)k;
+  const uint32_t range = kmax - kmin;
+  const int L = range ? 32 - __clz(range) : 0;
+  if (L > 0) {
+    constexpr int D = digit_bits<BINS>();
+    const int nsh = L > D ? L - D : 0;
+    hist_level(s, key, nv, kmin, L, 0u, nsh, (1u << (L - nsh)) - 1u);
+    __syncthreads();
+    select_bin<NT>(s, (uint32_t)k, parity);
+    parity ^= 1;
+    const uint32_t need = (uint32_t)k - s.sel[1];
+    const uint32_t bin = s.sel[0];
+    if (nsh == 0) {
+      u_t = bin;
+      need_ties = need;
+    } else if (s.sel[2] <= (uint32_t)kFewCand) {
+      resolve_few<NT, true>(s, key, col, nv, 0u, kmin, nsh, bin, need, u_t, need_ties);
+      col_t = s.res[2];
+      col_known = true;
+    } else {
+      refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
+    }
+  }
+  key_t = kmin + u_t;
+  if (!col_known) {
+    // the need_ties lowest columns among the keys equal to key_t: largest ~column
+    uint32_t key2[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) key2[e] = (e < nv && key[e] == key_t) ? ~col[e] : 0u;
+    uint32_t u2, n2;
+    refine_regs<NT>(s, key2, nv, 0u, 32, 0u, need_ties, parity, u2, n2);
+    col_t = ~u2;
+  }
+  // ordered output of every candidate at or above (key_t, col_t)
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    cnt += (e < nv && (key[e] > key_t || (key[e] == key_t && col[e] <= col_t))) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t pos = block_scan<NT>(cnt, s, parity, tot);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e < nv && (key[e] > key_t || (key[e] == key_t && col[e] <= col_t))) {
+      if (pos < (uint32_t)k) out[pos] = (int32_t)col[e];
+      ++pos;
+    }
+}
+
 template <int NT, int E, int BINS>
 hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                       const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {
@@ -537,11 +696,17 @@ hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32
   // 64 KB: candidate pairs, or first the per-wave histograms (<= 8 x 8 KB)
   const size_t dyn = long_rows ? (size_t)kCandPairs * 2 * sizeof(uint32_t) : 0;
   if (long_rows) {
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<NT, E, BINS>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-      attr_set = true;
+    // once per device (setting it twice from racing threads is harmless)
+    constexpr int kMaxDevices = 64;
+    static bool attr_set[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<NT, E, BINS>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+      if (e != hipSuccess) return e;
+      if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
     }
   }
   hipLaunchKernelGGL((topk_kernel<NT, E, BINS>), dim3((unsigned)rows), dim3(NT), dyn, stream, logits,
@@ -550,6 +715,23 @@ hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32
 }
 
 }  // namespace
+
+hipError_t launch_topk_merge(const float* values, const int32_t* indices, int world, int k_in,
+                             int64_t rows, int interleave, int k, int32_t* out_idx,
+                             hipStream_t stream) {
+  const int ncand = world * k_in;
+#define MXIDX_MERGE(e)                                                                         \
+  hipLaunchKernelGGL((topk_merge_kernel<1024, e>), dim3((unsigned)rows), dim3(1024), 0, stream, \
+                     values, indices, world, k_in, rows, interleave, k, out_idx)
+  // at most 8192 candidates per row (checked by the ABI): 8 per thread keeps the
+  // candidates, their columns and the tie keys in registers
+  if (ncand <= 4 * 1024)
+    MXIDX_MERGE(4);
+  else
+    MXIDX_MERGE(8);
+#undef MXIDX_MERGE
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                        const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {

@@ -45,7 +45,7 @@ def test_header_declarations_are_exported(L):
 
 
 def test_version_and_strerror(L):
-    assert L.idx_version() == 101
+    assert L.idx_version() == 102
     for st in range(5):
         assert L.idx_strerror(st)
     assert L.idx_strerror(99) == b"unknown status"
@@ -82,6 +82,21 @@ def test_insert_quantize_argument_validation(L):
     assert f(P, 0, 4, 128, P, P2, 4, 64, P, 0, 8, 128, None, P2, None) == ERR_ARG  # null q out
     assert f(P, 0, 4, 128, P, P2, -1, 64, P, 0, 8, 128, P, P2, None) == ERR_ARG  # negative pages
     assert f(None, 0, 0, 128, None, None, 0, 64, None, 0, 0, 128, None, None, None) == OK  # empty
+
+
+def test_topk_merge_argument_validation(L):
+    f = L.idx_topk_merge
+    assert f(P, P2, 0, 4, 64, 1, 16, P, None) == ERR_ARG          # world < 1
+    assert f(P, P2, 2, 4, 0, 1, 16, P, None) == ERR_ARG           # k_in < 1
+    assert f(P, P2, 2, 4, 64, 0, 16, P, None) == ERR_ARG          # interleave < 1
+    assert f(P, P2, 2, 4, 64, 1, 0, P, None) == ERR_ARG           # k < 1
+    assert f(P, P2, 2, 4, 64, 1, 2049, P, None) == ERR_ARG        # k > 2048
+    assert f(P, P2, 5, 4, 2048, 1, 16, P, None) == ERR_ARG        # more than 8192 candidates
+    assert f(P, P2, 2, -1, 64, 1, 16, P, None) == ERR_ARG         # negative rows
+    assert f(MIS, P2, 2, 4, 64, 1, 16, P, None) == ERR_ARG        # misaligned values
+    assert f(P, None, 2, 4, 64, 1, 16, P, None) == ERR_ARG        # null indices
+    assert f(P, P2, 2, 4, 64, 1, 16, None, None) == ERR_ARG       # null output
+    assert f(None, None, 2, 0, 64, 1, 16, None, None) == OK       # no rows
 
 
 def test_gather_argument_validation(L):
