@@ -38,7 +38,12 @@ constexpr int kMaxWaves = kMaxThreads / kWave;
 constexpr int kCandPairs = 8192;   // (key, column) pairs in dynamic LDS (64 KB), long rows only
 constexpr int kWaveHistBins = 2048;
 
-constexpr int kFewCand = 64;       // threshold bins this small are resolved by ranking
+// Threshold bins this small are resolved by ranking their keys pairwise
+// (quadratic, so the cutoff is per kernel): the row top-k uses 64, the merge
+// of rank lists -- whose first-level bins are larger -- uses 256.
+constexpr int kFewCand = 256;      // LDS capacity for the ranked keys
+constexpr int kFewTopk = 64;
+constexpr int kFewMerge = 256;
 
 template <int BINS>
 struct Shared {
@@ -240,13 +245,14 @@ __device__ __forceinline__ void refine_regs(Shared<BINS>& s, const uint32_t (&ke
 // u_t and the number of keys equal to it to take, as refine_regs does, and
 // the threshold key's column in s.res[2].  Columns are col0 + e, or cols[e]
 // when kCols.
-template <int NT, bool kCols, int BINS, int E>
+template <int NT, int FEW, bool kCols, int BINS, int E>
 __device__ __forceinline__ void resolve_few(Shared<BINS>& s, const uint32_t (&key)[E],
                                             const uint32_t (&cols)[E], int nv, uint32_t col0,
                                             uint32_t kmin, int shift, uint32_t prefix,
                                             uint32_t need, uint32_t& u_t, uint32_t& need_ties) {
-  constexpr int kPerCand = NT / kFewCand;        // threads per candidate
-  constexpr int kJ = kFewCand / kPerCand;        // comparisons per thread
+  static_assert(FEW <= kFewCand && NT % FEW == 0, "ranked keys: LDS capacity, threads");
+  constexpr int kPerCand = NT / FEW;             // threads per candidate
+  constexpr int kJ = FEW / kPerCand;             // comparisons per thread
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const uint32_t u = key[e] - kmin;
@@ -403,9 +409,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       if (nsh == 0) {
         u_t = bin;
         need_ties = need;
-      } else if (s.sel[2] <= (uint32_t)kFewCand) {
-        resolve_few<NT, false>(s, key, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x), kmin,
-                               nsh, bin, need, u_t, need_ties);
+      } else if (s.sel[2] <= (uint32_t)kFewTopk) {
+        resolve_few<NT, kFewTopk, false>(s, key, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x),
+                                         kmin, nsh, bin, need, u_t, need_ties);
       } else {
         refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
       }
@@ -656,12 +662,18 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
     if (nsh == 0) {
       u_t = bin;
       need_ties = need;
-    } else if (s.sel[2] <= (uint32_t)kFewCand) {
-      resolve_few<NT, true>(s, key, col, nv, 0u, kmin, nsh, bin, need, u_t, need_ties);
+    } else if (s.sel[2] <= (uint32_t)kFewMerge) {
+      resolve_few<NT, kFewMerge, true>(s, key, col, nv, 0u, kmin, nsh, bin, need, u_t, need_ties);
       col_t = s.res[2];
       col_known = true;
     } else {
       refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
+    }
+    // the last radix level's bin holds exactly the keys equal to the threshold:
+    // when all of them are taken, no column select is needed
+    if (!col_known && s.sel[2] == need_ties) {
+      col_t = 0xfffffffeu;                      // every valid column (empty slots are 0xffffffff)
+      col_known = true;
     }
   }
   key_t = kmin + u_t;
