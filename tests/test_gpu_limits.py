@@ -1,0 +1,73 @@
+"""GPU parity at the size limits of the ABI: the largest decode batch (65535
+sequences, the grid's y extent) and a cache whose pages lie beyond 2 GiB of
+byte offset (64-bit page addressing in insert, gather and paged logits)."""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_paged_cache_quant_amd as mx
+import workloads
+from oracle import logits as olog, mxfp4 as omx, paged_cache as opc, topk as otk
+from tests.gpu_helpers import check_logits, dev, exact, host, oracle_q
+
+pytestmark = pytest.mark.gpu
+
+
+def test_max_decode_batch_65535_sequences():
+    B, H = 65535, 16
+    rng = np.random.default_rng(65535)
+    lens = rng.integers(0, 70, B).astype(np.int32)          # empty, partial and two-page contexts
+    case = workloads.decode_case(65535, seq_lens=lens, H=H, next_n=1, spare_pages=1, width=70, topk=8)
+    cache = torch.zeros((case["num_pages"], 64 * 68), dtype=torch.uint8, device="cuda")
+    mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
+    qv, qs = mx.quantize(dev(case["q"]))
+    out = mx.logits_paged(qv, qs, dev(case["w"]), cache, dev(case["block_table"]),
+                          dev(case["context_lens"]), 1, case["width"], clean=True)
+    idx = mx.topk(out, None, dev(case["context_lens"]), 8)
+    torch.cuda.synchronize()
+    g, gi = host(out), host(idx)
+    # sampled sequences against the oracle (first, last, and some in between)
+    seqs = np.unique(np.concatenate([[0, 1, B - 2, B - 1], rng.choice(B, 60, replace=False)]))
+    qc = np.zeros((B, H, 64), np.uint8)              # the oracle's q, for the sampled rows only
+    qsc = np.zeros((B, H, 4), np.uint8)
+    c, sc = omx.quantize_rows(omx.bf16_bits_to_f64(case["q"][seqs]))
+    qc[seqs], qsc[seqs] = c.reshape(-1, H, 64), sc.reshape(-1, H, 4)
+    ref, bound = olog.paged_mqa_logits(qc, qsc, case["w"], host(cache), case["block_table"],
+                                       case["context_lens"], 1, case["width"], seqs=seqs,
+                                       with_bound=True)
+    check_logits(g[seqs], ref[seqs], bound[seqs], "65535 sequences")
+    tk = otk.top_k_per_row(g[seqs], np.zeros(len(seqs), int), lens[seqs], 8)
+    for j, b in enumerate(seqs):
+        m = int((tk[j] >= 0).sum())
+        assert sorted(gi[b, :m].tolist()) == sorted(tk[j, :m].tolist()), b
+        assert np.all(gi[b, m:] == -1), b
+
+
+def test_pages_beyond_2gib_offsets():
+    # 600,000 pages of 4352 B = 2.6 GB: the sequence's pages are taken from the top
+    num_pages = 600_000
+    lens = np.array([200, 130], np.int32)
+    case = workloads.decode_case(77, seq_lens=lens, H=32, next_n=2, spare_pages=0, width=200)
+    pages_used = case["num_pages"]
+    high = num_pages - pages_used                            # page p -> p + high (offset > 2^31 B)
+    bt = (case["block_table"] + high).astype(np.int32)
+    slots = case["slot_mapping"] + np.int64(high) * 64
+    cache = torch.zeros((num_pages, 64 * 68), dtype=torch.uint8, device="cuda")
+    mx.insert(dev(case["k"]), dev(slots), cache)
+    qv, qs = mx.quantize(dev(case["q"]))
+    out = mx.logits_paged(qv, qs, dev(case["w"]), cache, dev(bt), dev(case["context_lens"]), 2,
+                          case["width"], clean=True)
+    kv, ksc = mx.gather(cache, dev(bt), dev(case["context_lens"]),
+                        dev(np.array([0, 200], np.int64)), 200, 330)
+    torch.cuda.synchronize()
+    top = host(cache[high:])                                 # the written pages only
+    ref_pages = opc.insert(np.zeros((pages_used, 64 * 68), np.uint8), exact(case, "k"),
+                           case["slot_mapping"])
+    assert np.array_equal(top, ref_pages)
+    assert not torch.any(cache[:high].view(-1)[:: 4099]).item()   # sampled untouched low pages
+    kc, ks_ = omx.quantize_rows(exact(case, "k"))
+    assert np.array_equal(host(kv), kc) and np.array_equal(host(ksc), ks_)
+    ref, bound = olog.paged_mqa_logits(*oracle_q(case), case["w"], ref_pages, case["block_table"],
+                                       case["context_lens"], 2, case["width"], with_bound=True)
+    check_logits(host(out), ref, bound, "pages beyond 2 GiB")
