@@ -57,3 +57,52 @@ def test_decode_step_graph_replays_match_eager():
         assert np.array_equal(got_logits, host(logits)), rep
         assert np.array_equal(got_idx, host(idx)), rep
         assert np.array_equal(got_cache, host(cache)), rep
+
+
+def test_fused_step_and_merge_graph_replays_match_eager():
+    # the decode step as the bench runs it (one-launch insert + quantize,
+    # next_n 2), followed by a context-parallel merge of two lists
+    case = workloads.decode_case(51, seq_lens=[3000, 700, 2100], H=32, next_n=2, topk=256)
+    B, W = 3, case["width"]
+    cache = new_cache(case["num_pages"], fill=0)
+    mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
+    last = np.cumsum(case["context_lens"]) - 1
+    k_new, slot_new = dev(case["k"][last]), dev(case["slot_mapping"][last])
+    q, w = dev(case["q"]), dev(case["w"])
+    bt, ctx = dev(case["block_table"]), dev(case["context_lens"])
+    ke = dev(olog.decode_visible_end(case["context_lens"], 2).astype(np.int32))
+    qv = torch.empty((2 * B, 32, 64), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((2 * B, 32, 4), dtype=torch.uint8, device="cuda")
+    logits = torch.empty((2 * B, W), dtype=torch.float32, device="cuda")
+    idx = torch.empty((2 * B, 256), dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(4)
+    mv = dev(rng.standard_normal((2, 2 * B, 256)).astype(np.float32))
+    mi = dev(np.stack([np.stack([rng.permutation(4000)[:256] for _ in range(2 * B)]) for _ in range(2)])
+             .astype(np.int32))
+    mout = torch.empty((2 * B, 256), dtype=torch.int32, device="cuda")
+
+    def step():
+        mx.insert_quantize(k_new, slot_new, cache, q, qv, qs)
+        mx.logits_paged(qv, qs, w, cache, bt, ctx, 2, W, logits=logits, clean=False)
+        mx.topk(logits, None, ke, 256, out=idx)
+        mx.topk_merge(mv, mi, 16, 256, out=mout)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        q.copy_(dev(workloads.bf16_bits(rng.standard_normal(case["q"].shape).astype(np.float32))))
+        mv.copy_(dev(rng.standard_normal((2, 2 * B, 256)).astype(np.float32)))
+        g.replay()
+        torch.cuda.synchronize()
+        got = [host(t).copy() for t in (idx, cache, mout)]
+        got_vis = [host(logits)[r, :int(host(ke)[r])].copy() for r in range(2 * B)]
+        _ = torch.randn(1000, device="cuda").sum().item()
+        step()
+        torch.cuda.synchronize()
+        for a, t in zip(got, (idx, cache, mout)):
+            assert np.array_equal(a, host(t)), rep
+        for r in range(2 * B):
+            assert np.array_equal(got_vis[r], host(logits)[r, :int(host(ke)[r])]), (rep, r)
