@@ -2,7 +2,10 @@
 // "SparseAttnIndexerKpool"; exact sets, as P2 "Validation" tests them).
 //
 // Ranking: value descending, then column ascending; -0.0 == +0.0.  The output
-// holds the min(k, n) selected columns, in column order, followed by -1.
+// holds the min(k, n) selected columns followed by -1, in a deterministic
+// order: column order, except where the first level's threshold bin is ranked
+// directly -- then the keys above that bin come first, in column order, and
+// the bin's selected keys follow in rank order.
 //
 // Radix select on order-preserving 32-bit keys with 11-bit digits and one
 // workgroup per row (1024 threads for small batches, 512 threads when there
@@ -10,9 +13,10 @@
 // the candidate keys in LDS and finds the bin where the running count from
 // the top crosses the number still needed; when the digits are exhausted the
 // exact k-th key T is known, and a final ordered pass takes every key > T plus
-// the lowest-column keys == T.  Ordered writes come from one workgroup prefix
-// sum of per-thread counts (no atomics), so the output is deterministic.  A
-// level costs three barriers: histogram complete, scan totals, selection.
+// the lowest-column keys == T.  Output positions come from workgroup prefix
+// sums of per-thread counts or from ranks (no atomics), so the output is
+// deterministic.  A level costs three barriers: histogram complete, scan
+// totals, selection.
 //
 // The row is held in registers, E keys per thread, with every load of a
 // thread issued before any is used (the passes are latency-bound otherwise):
@@ -21,8 +25,8 @@
 //     bit of kmax - kmin, so the first histogram spreads the row over the bins
 //     (fixed top-bit digits would pile similar logits into a few bins).  When
 //     the first level's threshold bin holds at most 64 keys (the usual case:
-//     2048 bins over the row's own range), those keys are ranked directly
-//     instead of histogramming the remaining digits;
+//     2048 bins over the row's own range), those keys are ranked directly and
+//     written at their rank, instead of histogramming the remaining digits;
 //   * longer rows, in chunks of threads*E: a first read histograms the top
 //     digit of the keys, a second read writes the keys above the threshold bin
 //     directly and compacts the bin's (key, column) pairs into LDS (up to
@@ -52,9 +56,52 @@ struct Shared {
   uint32_t sel[3];                      // selected bin, count strictly above it, count in it
   // few-candidate resolve (zeroed at kernel start)
   uint32_t ccount;
-  uint32_t ckey[kFewCand], ccol[kFewCand], crank[kFewCand], cgt[kFewCand];
-  uint32_t res[3];
+  uint32_t ckey[kFewCand], ccol[kFewCand];
 };
+
+// Cross-lane steps use DPP row shifts (lane i reads lane i - d of its 16-lane
+// row; a source outside the row reads as 0) and lane reads into scalars, not
+// LDS permutes: each step is a few VALU cycles instead of an LDS round trip.
+// Callers run them with every lane of the wave active.
+__device__ __forceinline__ uint32_t row_shr(uint32_t x, int d) {
+  switch (d) {
+    case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);
+    case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);
+    case 4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);
+    default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);
+  }
+}
+
+// Sum over each aligned group of SPAN lanes (SPAN a power of two <= 16),
+// complete in the group's last lane.
+template <int SPAN>
+__device__ __forceinline__ uint32_t group_sum(uint32_t x) {
+  static_assert(SPAN >= 1 && SPAN <= 16 && (SPAN & (SPAN - 1)) == 0, "groups within a DPP row");
+#pragma unroll
+  for (int d = 1; d < SPAN; d <<= 1) x += row_shr(x, d);
+  return x;
+}
+
+// Inclusive prefix sum over the wave in lane order.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x = group_sum<16>(x);                          // inclusive within each row
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)x, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)x, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)x, 47);
+  const int lane = threadIdx.x & 63;
+  return x + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+}
+
+// Maximum over the wave (uniform result).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+#pragma unroll
+  for (int d = 1; d < 16; d <<= 1) x = max(x, row_shr(x, d));   // 0 from outside a row is neutral
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)x, 15),
+                         (uint32_t)__builtin_amdgcn_readlane((int)x, 31));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)x, 47),
+                         (uint32_t)__builtin_amdgcn_readlane((int)x, 63));
+  return max(a, b);
+}
 
 // Exclusive prefix sum over the workgroup in thread order; also returns the
 // total.  One barrier; consecutive calls must alternate `parity`.
@@ -64,12 +111,7 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, Shared<BINS>& s, int 
   constexpr int kWaves = NT / kWave;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_up((int)x, d);
-    if (lane >= d) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   uint32_t* wt = s.wave_tot[parity];
   if (lane == 63) wt[wid] = x;
   __syncthreads();
@@ -237,59 +279,60 @@ __device__ __forceinline__ void refine_regs(Shared<BINS>& s, const uint32_t (&ke
   need_ties = need;
 }
 
-// The threshold bin (keys with u >> shift == prefix) holds at most kFewCand
-// keys and the `need`-th largest of them is the k-th of the row: gather the
-// bin's (key, column) pairs and rank them directly -- rank = number of bin
-// keys before it in (key desc, column asc) order, counted pairwise by the
-// whole workgroup -- instead of histogramming the remaining digits.  Returns
-// u_t and the number of keys equal to it to take, as refine_regs does, and
-// the threshold key's column in s.res[2].  Columns are col0 + e, or cols[e]
-// when kCols.
+// Output of the row when the threshold bin (keys with u >> shift == prefix)
+// holds at most FEW keys and the `need`-th largest of them is the k-th of the
+// row.  Keys in higher bins (`above` of them) go to out[0, above) in thread
+// order, from one prefix sum whose barrier also publishes the bin's gathered
+// (key, column) pairs; each bin key is then ranked directly -- rank = number
+// of bin keys before it in (key desc, column asc) order, counted pairwise by
+// kPerCand threads and summed over their DPP row -- and written to
+// out[above + rank] when rank < need.  Two barriers, no remaining digits and
+// no further pass.  Columns are col0 + e, or cols[e] when kCols.
 template <int NT, int FEW, bool kCols, int BINS, int E>
-__device__ __forceinline__ void resolve_few(Shared<BINS>& s, const uint32_t (&key)[E],
-                                            const uint32_t (&cols)[E], int nv, uint32_t col0,
-                                            uint32_t kmin, int shift, uint32_t prefix,
-                                            uint32_t need, uint32_t& u_t, uint32_t& need_ties) {
+__device__ __forceinline__ void select_few(Shared<BINS>& s, const uint32_t (&key)[E],
+                                           const uint32_t (&cols)[E], int nv, uint32_t col0,
+                                           uint32_t kmin, int shift, uint32_t prefix,
+                                           uint32_t need, uint32_t above,
+                                           int32_t* __restrict__ out, int parity) {
   static_assert(FEW <= kFewCand && NT % FEW == 0, "ranked keys: LDS capacity, threads");
   constexpr int kPerCand = NT / FEW;             // threads per candidate
   constexpr int kJ = FEW / kPerCand;             // comparisons per thread
+  uint32_t ca = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t u = key[e] - kmin;
-    if (e < nv && (u >> shift) == prefix) {
+    const uint32_t d = (key[e] - kmin) >> shift;
+    if (e < nv && d > prefix) ++ca;
+    if (e < nv && d == prefix) {
       const uint32_t slot = atomicAdd(&s.ccount, 1u);
       s.ckey[slot] = key[e];
       s.ccol[slot] = kCols ? cols[e] : col0 + (uint32_t)e;
     }
   }
-  __syncthreads();
+  uint32_t total;
+  uint32_t pos = block_scan<NT>(ca, s, parity, total);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e < nv && ((key[e] - kmin) >> shift) > prefix)
+      out[pos++] = (int32_t)(kCols ? cols[e] : col0 + (uint32_t)e);
   const uint32_t cnt = s.ccount;
   const uint32_t i = threadIdx.x / kPerCand;
   const uint32_t j0 = (threadIdx.x % kPerCand) * kJ;
+  uint32_t ki = 0, ci = 0, before = 0;
   if (i < cnt) {
-    const uint32_t ki = s.ckey[i], ci = s.ccol[i];
-    uint32_t before = 0, greater = 0;
+    ki = s.ckey[i];
+    ci = s.ccol[i];
 #pragma unroll
     for (int jj = 0; jj < kJ; ++jj) {
       const uint32_t j = j0 + jj;
       if (j < cnt) {
         const uint32_t kj = s.ckey[j], cj = s.ccol[j];
         before += (kj > ki || (kj == ki && cj < ci)) ? 1u : 0u;
-        greater += kj > ki ? 1u : 0u;
       }
     }
-    if (before) atomicAdd(&s.crank[i], before);
-    if (greater) atomicAdd(&s.cgt[i], greater);
   }
-  __syncthreads();
-  if (threadIdx.x < cnt && s.crank[threadIdx.x] == need - 1) {   // exactly one candidate
-    s.res[0] = s.ckey[threadIdx.x] - kmin;
-    s.res[1] = need - s.cgt[threadIdx.x];
-    s.res[2] = s.ccol[threadIdx.x];
-  }
-  __syncthreads();
-  u_t = s.res[0];
-  need_ties = s.res[1];
+  before = group_sum<kPerCand>(before);          // a candidate's threads share a DPP row
+  if (i < cnt && threadIdx.x % kPerCand == kPerCand - 1 && before < need)
+    out[above + before] = (int32_t)ci;
 }
 
 // Ordered output of register-held candidates (thread t holds consecutive
@@ -360,11 +403,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   int parity = 0;
-  if (threadIdx.x < kFewCand) {                 // read only after later barriers
-    s.crank[threadIdx.x] = 0;
-    s.cgt[threadIdx.x] = 0;
-    if (threadIdx.x == 0) s.ccount = 0;
-  }
+  if (threadIdx.x == 0) s.ccount = 0;           // read only after later barriers
 
   if (n <= C) {
     // ---- the whole row in registers: one read ----
@@ -378,10 +417,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
         kmin = min(kmin, key[e]);
         kmax = max(kmax, key[e]);
       }
-    for (int d = 32; d >= 1; d >>= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
-    }
+    kmin = ~wave_umax(~kmin);
+    kmax = wave_umax(kmax);
     if (lane == 0) {
       s.wave_tot[1][wid] = kmin;
       s.wave_tot[1][kMaxWaves + wid] = kmax;
@@ -410,8 +447,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
         u_t = bin;
         need_ties = need;
       } else if (s.sel[2] <= (uint32_t)kFewTopk) {
-        resolve_few<NT, kFewTopk, false>(s, key, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x),
-                                         kmin, nsh, bin, need, u_t, need_ties);
+        select_few<NT, kFewTopk, false>(s, key, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x),
+                                        kmin, nsh, bin, need, (uint32_t)k - need, out, parity);
+        return;
       } else {
         refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
       }
@@ -573,11 +611,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   int parity = 0;
-  if (threadIdx.x < kFewCand) {                 // read only after later barriers
-    s.crank[threadIdx.x] = 0;
-    s.cgt[threadIdx.x] = 0;
-    if (threadIdx.x == 0) s.ccount = 0;
-  }
+  if (threadIdx.x == 0) s.ccount = 0;           // read only after later barriers
   clear_hist<NT>(s);                            // first read after the barriers below
 
   // candidates c = E*t + e: rank c / k_in, slot c % k_in
@@ -615,10 +649,8 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
       kmin = min(kmin, key[e]);
       kmax = max(kmax, key[e]);
     }
-  for (int d = 32; d >= 1; d >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
-  }
+  kmin = ~wave_umax(~kmin);
+  kmax = wave_umax(kmax);
   if (lane == 0) {
     s.wave_tot[1][wid] = kmin;
     s.wave_tot[1][kMaxWaves + wid] = kmax;
@@ -663,9 +695,9 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
       u_t = bin;
       need_ties = need;
     } else if (s.sel[2] <= (uint32_t)kFewMerge) {
-      resolve_few<NT, kFewMerge, true>(s, key, col, nv, 0u, kmin, nsh, bin, need, u_t, need_ties);
-      col_t = s.res[2];
-      col_known = true;
+      select_few<NT, kFewMerge, true>(s, key, col, nv, 0u, kmin, nsh, bin, need,
+                                      (uint32_t)k - need, out, parity);
+      return;
     } else {
       refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
     }
