@@ -7,10 +7,12 @@
 // of the block-split MXFP4 cache (P1 live-validation comment).
 //
 // Design (HBM-bound: 68 bytes of K per scored token, 4 bytes of logit out):
-//  * grid = (logical pages / 2, sequences), one wave per workgroup, so the
-//    dispatcher balances ragged sequence lengths at the finest grain; each
-//    wave owns two consecutive pages of one sequence and has both pages'
-//    loads in flight before it computes either.
+//  * grid = (logical pages / 3, sequences), one wave per workgroup, so the
+//    dispatcher balances ragged sequence lengths at a fine grain; each wave
+//    owns three consecutive pages of one sequence (13 KB of cache) and has
+//    every page's loads in flight before it computes any.  Three measured
+//    faster than two (more bytes in flight per wave) and than four (fewer
+//    waves) on long contexts.
 //  * A page's base address is wave-uniform: it goes into a buffer descriptor
 //    in scalar registers and every lane keeps one fixed offset, so a page
 //    costs no vector address arithmetic.  A missing page (past the context,
@@ -25,9 +27,10 @@
 //    block and lane) per token tile gives the exact scaled head dots.  An
 //    output column depends on its own token only, so tokens past the context
 //    need no masking of operands, only of stores.
-//  * ReLU and the head weights are applied on the fp32 MFMA output; two
-//    xor-shuffles combine the four lane groups' partial sums, after which
-//    lane l owns token l of the page and the wave stores 64 consecutive floats.
+//  * ReLU and the head weights are applied on the fp32 MFMA output; lane-pair
+//    swaps across the wave halves and quarters combine the four lane groups'
+//    partial sums, after which lane l owns token l of the page and the wave
+//    stores 64 consecutive floats.
 //  * Vector memory counters retire in issue order, so a wait for a load also
 //    waits for every store issued before it: for up to NN query rows per
 //    sequence (NN * heads/16 <= 8) every row's query is loaded up front and
@@ -40,7 +43,7 @@
 namespace mxidx {
 namespace {
 
-constexpr int kPagesPerWave = 2;
+constexpr int kPagesPerWave = 3;
 // Dword 3 of a raw buffer descriptor: data format 32 (bits 18:15 = 4); raw
 // loads and stores move bytes and ignore the format otherwise.
 constexpr int kBufferFormat = 0x00020000;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
 
   // Context length and the wave's block-table entries in one round trip: both
   // as vector loads (a scalar load of the length would have to retire before
-  // the table load could issue).  Lane p < 2 reads the entry of page lp0 + p;
+  // the table load could issue).  Lane p < kPagesPerWave reads the entry of page lp0 + p;
   // the other lanes fall outside the descriptor and read 0 without an access.
   const int bt_count = (int)min((int64_t)kPagesPerWave, wpages - lp0);
   const int bt_lane = (int)__builtin_amdgcn_raw_buffer_load_b32(
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
                                           keep ? 4u * lane : kDropOffset, 0, kNonTemporal);
   };
 
-  if (lp0 * kPage >= L) {        // both pages lie past the context: -inf fill only
+  if (lp0 * kPage >= L) {        // every page lies past the context: -inf fill only
     if (clean)
       for (int i = 0; i < next_n; ++i)
 #pragma unroll
