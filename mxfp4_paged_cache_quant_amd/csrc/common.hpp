@@ -38,6 +38,18 @@ __device__ __forceinline__ uint32_t f32_key(uint32_t u) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Raw buffer descriptors over a wave-uniform base (kept in scalar registers):
+// a load outside [0, bytes) reads 0 and a store there is dropped, with no
+// memory access.  Dword 3 holds data format 32 (bits 18:15 = 4); raw loads and
+// stores move bytes and ignore the format otherwise.
+constexpr int kBufferFormat = 0x00020000;
+constexpr int kNonTemporal = 2;                 // cache-policy bits of buffer ops: nt
+constexpr uint32_t kDropOffset = 0x40000000u;   // beyond any descriptor: the access is dropped
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFormat);
+}
+
 __device__ __forceinline__ float neg_inf() { return __uint_as_float(0xff800000u); }
 
 }  // namespace mxidx

@@ -44,16 +44,6 @@ namespace mxidx {
 namespace {
 
 constexpr int kPagesPerWave = 3;
-// Dword 3 of a raw buffer descriptor: data format 32 (bits 18:15 = 4); raw
-// loads and stores move bytes and ignore the format otherwise.
-constexpr int kBufferFormat = 0x00020000;
-constexpr int kNonTemporal = 2;                 // cache-policy bits of buffer ops: nt
-constexpr uint32_t kDropOffset = 0x40000000u;   // beyond any descriptor: the store is dropped
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFormat);
-}
-
 struct PageRegs {
   uint4 code[4];      // tile j: block g of token 16*j + n
   uint32_t scale[4];  // tile j: the 4 scale bytes of token 16*j + n

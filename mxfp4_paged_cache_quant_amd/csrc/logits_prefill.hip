@@ -42,16 +42,6 @@ namespace {
 
 constexpr int kKeyChunk = 1024;
 
-// Dword 3 of a raw buffer descriptor: data format 32 (bits 18:15 = 4); raw
-// loads and stores move bytes and ignore the format otherwise.
-constexpr int kBufferFormat = 0x00020000;
-constexpr int kNonTemporal = 2;                 // cache-policy bits of buffer ops: nt
-constexpr uint32_t kDropOffset = 0x40000000u;   // beyond any descriptor: the store is dropped
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufferFormat);
-}
-
 // B operands of 64 consecutive keys c0..c0+63: lane (g, n) takes the 16 code
 // bytes of block g of key c0 + 16*j + n for each tile j, and that key's 4
 // scale bytes (the block's byte is extracted when the tile is used).  Keys at

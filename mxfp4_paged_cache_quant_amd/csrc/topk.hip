@@ -109,20 +109,17 @@ template <int NT, int BINS>
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, Shared<BINS>& s, int parity,
                                                uint32_t& total) {
   constexpr int kWaves = NT / kWave;
+  static_assert(kWaves <= 16, "the wave totals are scanned in one DPP row");
   const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t x = wave_incl_scan(v);
   uint32_t* wt = s.wave_tot[parity];
   if (lane == 63) wt[wid] = x;
   __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
-    const uint32_t w = wt[i];
-    before += (i < wid) ? w : 0u;
-    tot += w;
-  }
-  total = tot;
+  // lane i < kWaves takes wave i's total; their running sums give each wave its base
+  const uint32_t w = group_sum<16>(lane < kWaves ? wt[lane & 15] : 0u);
+  const uint32_t before = wid ? (uint32_t)__builtin_amdgcn_readlane((int)w, wid - 1) : 0u;
+  total = (uint32_t)__builtin_amdgcn_readlane((int)w, kWaves - 1);
   return before + x - v;
 }
 
@@ -247,6 +244,16 @@ __device__ __forceinline__ void hist_level(Shared<BINS>& s, const uint32_t (&key
     const uint32_t u = key[e] - kmin;
     if (e < nv && (shift >= 32 || (u >> shift) == prefix)) atomicAdd(&s.hist[(u >> nsh) & dmask], 1u);
   }
+}
+
+// First level over the key range: u = key - kmin < 2^(nsh + digit bits), so
+// every valid key counts and its digit is u >> nsh.
+template <int E, int BINS>
+__device__ __forceinline__ void hist_first(Shared<BINS>& s, const uint32_t (&key)[E], int nv,
+                                           uint32_t kmin, int nsh) {
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e < nv) atomicAdd(&s.hist[(key[e] - kmin) >> nsh], 1u);
 }
 
 template <int BINS>
@@ -424,10 +431,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       s.wave_tot[1][kMaxWaves + wid] = kmax;
     }
     __syncthreads();
-    for (int w = 0; w < kWaves; ++w) {
-      kmin = min(kmin, s.wave_tot[1][w]);
-      kmax = max(kmax, s.wave_tot[1][kMaxWaves + w]);
-    }
+    kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
+    kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
     // wave_tot[1] is next written by the second scan, after at least one more barrier
     const uint32_t range = kmax - kmin;
     const int L = range ? 32 - __clz(range) : 0;     // bit length of the key range
@@ -437,7 +442,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       // small threshold bin or the remaining digits
       constexpr int D = digit_bits<BINS>();
       const int nsh = L > D ? L - D : 0;
-      hist_level(s, key, nv, kmin, L, 0u, nsh, (1u << (L - nsh)) - 1u);
+      hist_first(s, key, nv, kmin, nsh);
       __syncthreads();
       select_bin<NT>(s, (uint32_t)k, parity);
       parity ^= 1;
@@ -658,10 +663,8 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
   uint32_t total_valid;
   (void)block_scan<NT>((uint32_t)__popc(okmask), s, parity, total_valid);   // one barrier
   parity ^= 1;
-  for (int w = 0; w < kWaves; ++w) {
-    kmin = min(kmin, s.wave_tot[1][w]);
-    kmax = max(kmax, s.wave_tot[1][kMaxWaves + w]);
-  }
+  kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
+  kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
   __syncthreads();                              // the next scan rewrites wave_tot[1]
 
   if (total_valid <= (uint32_t)k) {             // every valid candidate, then -1
@@ -685,7 +688,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
   if (L > 0) {
     constexpr int D = digit_bits<BINS>();
     const int nsh = L > D ? L - D : 0;
-    hist_level(s, key, nv, kmin, L, 0u, nsh, (1u << (L - nsh)) - 1u);
+    hist_first(s, key, nv, kmin, nsh);
     __syncthreads();
     select_bin<NT>(s, (uint32_t)k, parity);
     parity ^= 1;
