@@ -3,11 +3,12 @@
 
 Decode step (the headline): batch 16, one query token each, 8192-token
 contexts, 32 index heads, head_dim 128, MXFP4 cache (page 64, permuted block
-table), top-2048.  One step = insert of the 16 new tokens' K (quantize +
-scatter) and MXFP4 quantization of the 16x32 query rows (one launch,
-idx_insert_quantize) -> paged logits over all 131072 cached tokens ->
-top-2048 per row.  Metric: scored cache tokens per
-second = sum over rows of the visible context / step time.
+table), top-2048.  One step = one launch of idx_logits_paged_insert (insert of
+the 16 new tokens' K -- quantize + scatter --, MXFP4 quantization of the 16x32
+query rows, paged logits over all 131072 cached tokens) -> top-2048 per row.
+Metric: scored cache tokens per second = sum over rows of the visible context /
+step time.  The same step as three calls (idx_insert_quantize, idx_logits_paged,
+idx_topk) is timed beside it.
 
 Timing: the step is captured in HIP graphs; W untimed warm-up steps, then
 exactly K steps between two device synchronizations.  The steps rotate over
@@ -109,11 +110,16 @@ def build_decode_sets(case, n_sets):
 
 
 def decode_ops(case):
-    """The four calls of one decode step, each as f(set)."""
+    """The calls of a decode step, each as f(set)."""
     import mxfp4_paged_cache_quant_amd as mx
     W, K = case["width"], case["topk"]
     return {
-        # the new tokens' K into the cache and the query rows to MXFP4, one launch
+        # the new tokens' K into the cache, the query rows to MXFP4 and the paged
+        # logits, one launch
+        "logits_paged_insert": lambda s: mx.logits_paged_insert(s.q, s.k_new, s.w, s.cache, s.bt,
+                                                                s.ctx, 1, W, logits=s.logits,
+                                                                clean=False),
+        # the same as two launches: the encodes, then the logits
         "insert_quantize": lambda s: mx.insert_quantize(s.k_new, s.slot_new, s.cache, s.q, s.qv, s.qs),
         # clean=False: the top-k reads each row only up to its visible end
         "logits_paged": lambda s: mx.logits_paged(s.qv, s.qs, s.w, s.cache, s.bt, s.ctx, 1, W,
@@ -160,11 +166,9 @@ def time_graph(g, reps):
     return start.elapsed_time(stop) / reps
 
 
-def bench_decode(args, case):
+def bench_decode(args, case, sets, order):
     import torch
-    sets = build_decode_sets(case, args.sets)
     ops = decode_ops(case)
-    order = ["insert_quantize", "logits_paged", "topk"]
 
     def step_fns(lo, hi):
         return [(lambda s=s, name=name: ops[name](s)) for s in sets[lo:hi] for name in order]
@@ -451,7 +455,7 @@ def _source_hash(kernel):
         if kernel.startswith(prefix):
             path = os.path.join(ROOT, "mxfp4_paged_cache_quant_amd", "csrc", src)
             h = hashlib.sha256(open(path, "rb").read())
-            for common in ("common.hpp", "logits_reduce.hpp"):
+            for common in ("common.hpp", "logits_reduce.hpp", "mxfp4_encode.hpp"):
                 h.update(open(os.path.join(os.path.dirname(path), common), "rb").read())
             return h.hexdigest()[:16]
     return None
@@ -550,7 +554,10 @@ def main():
             return
     case = workloads.paged_decode()
     log(f"[bench] decode workload {case['name']}: building {args.sets} rotating sets")
-    elapsed, per_kernel = bench_decode(args, case)
+    sets = build_decode_sets(case, args.sets)
+    elapsed, per_kernel = bench_decode(args, case, sets, ["logits_paged_insert", "topk"])
+    sep_elapsed, sep_kernel = bench_decode(args, case, sets, ["insert_quantize", "logits_paged", "topk"])
+    del sets
     ms_per_step = elapsed / args.steps * 1e3
     scored = int(np.sum(case["context_lens"]))
     value = scored * args.steps / elapsed
@@ -558,13 +565,16 @@ def main():
 
     B, H, L = len(case["context_lens"]), case["H"], int(case["context_lens"][0])
     alg_bytes = {
+        # cache read + logits written, bf16 q and fp32 weights read, new K read + written
+        "logits_paged_insert": scored * (68 + 4) + B * H * (256 + 4) + B * (256 + 68),
         "insert_quantize": B * (256 + 8 + 68) + B * H * (256 + 68),
         "logits_paged": scored * (68 + 4) + B * H * (68 + 4),
         "topk": scored * 4 + B * case["topk"] * 4,
     }
     dominant = max(per_kernel, key=per_kernel.get)
     achieved = alg_bytes[dominant] / (per_kernel[dominant] * 1e-6) / 1e9
-    dom_kernel = {"insert_quantize": "insert_quantize_kernel", "logits_paged": "logits_paged_kernel",
+    dom_kernel = {"logits_paged_insert": "logits_paged_kernel",
+                  "insert_quantize": "insert_quantize_kernel", "logits_paged": "logits_paged_kernel",
                   "topk": "topk_kernel"}[dominant]
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -573,10 +583,14 @@ def main():
                 "avg_launch_us": round(per_kernel[dominant], 3)}
     kernels = {k: {"avg_us": round(v, 3), "alg_bytes": alg_bytes[k],
                    "gbs": round(alg_bytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in per_kernel.items()}
+    separate = {"step": "insert_quantize+logits_paged+topk",
+                "us_per_step": round(sep_elapsed / args.steps * 1e6, 3),
+                "kernels_us": {k: round(v, 3) for k, v in sep_kernel.items()}}
+    log(f"[bench] decode as three calls: {separate}")
 
     if args.only == "decode":
         print(json.dumps({"section": "decode", "us_per_step": round(ms_per_step * 1e3, 3),
-                          "kernels_us": per_kernel}), flush=True)
+                          "kernels_us": per_kernel, "separate": separate}), flush=True)
         return
 
     prefill = None
@@ -619,10 +633,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": case["name"], "batch": B, "context": L, "heads": H,
                    "head_dim": 128, "page_size": 64, "next_n": 1, "topk": case["topk"],
-                   "step": "insert_quantize(16 new tokens' K, 512 q rows; one launch)+logits_paged+topk",
+                   "step": "logits_paged_insert(16 new tokens' K, 512 q rows, paged logits; one launch)+topk",
                    "rotating_sets": args.sets, "hip_graph": True, "parallelism": "none"},
         "roofline": roofline,
         "kernels": kernels,
+        "decode_separate_calls": separate,
         "prefill": prefill,
         "long_decode": long_decode,
         "long_prefill": long_prefill,

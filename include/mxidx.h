@@ -200,6 +200,32 @@ int idx_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
                      int64_t max_context_len, float* logits, int64_t logits_row_stride,
                      int clean, hipStream_t stream);
 
+/* idx_logits_paged_insert -- a decode step's two encodes and its paged logits in
+ * one launch: equal, byte for byte and bit for bit, to idx_insert of the new
+ * tokens into their block-table slots, idx_quantize of q, then
+ * idx_logits_paged (the indexer K quant-and-cache of P1 "Changes", the FP4 q of
+ * P3 "forward_cuda" and the paged_mqa_logits of P3 "SparseAttnIndexerKpool").
+ * For decode steps bound by launch count.
+ *   q:      [B*next_n, H, 128] bf16 (dtype IDX_BF16) or fp32 (IDX_F32),
+ *           contiguous, 16-byte aligned: the query rows, encoded in the kernel.
+ *   k_new:  [B*next_n, 128] in the same dtype, contiguous, 16-byte aligned:
+ *           row b*next_n + i is the K row of sequence b's token at position
+ *           context_lens[b] - next_n + i (the sequence's last next_n tokens);
+ *           it is written to page block_table[b, pos / 64], offset pos % 64.
+ *           Positions < 0, pages whose table entry is outside [0, num_pages)
+ *           and pages past max_context_len are not written.
+ *   cache:  updated in place (the new tokens' 68 bytes only), and read.
+ *   All other arguments, the logits and the error behaviour are those of
+ *   idx_logits_paged.  The new tokens' pages must not appear in another
+ *   sequence's block table: they are written while the other sequences' pages
+ *   are read. */
+int idx_logits_paged_insert(const void* q, const void* k_new, int dtype, const float* weights,
+                            uint8_t* cache, int64_t num_pages, int page_size,
+                            const int32_t* block_table, int64_t bt_row_stride,
+                            const int32_t* context_lens, int B, int next_n, int H,
+                            int64_t max_context_len, float* logits, int64_t logits_row_stride,
+                            int clean, hipStream_t stream);
+
 /* idx_topk -- per-row top-k column indices (top_k_per_row, P3
  * "SparseAttnIndexerKpool"; exact sets as tested in P2 "Validation").
  *   logits [rows, logits_row_stride] fp32 (finite in [ks, ke));

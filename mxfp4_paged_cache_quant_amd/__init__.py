@@ -14,8 +14,8 @@ import os
 
 __all__ = [
     "MxidxError", "lib", "lib_path", "version", "init",
-    "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged", "topk",
-    "topk_merge",
+    "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged",
+    "logits_paged_insert", "topk", "topk_merge",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
 ]
 
@@ -52,6 +52,9 @@ EXPORTS = {
     "idx_logits_paged": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _int, _c_void_p,
                                 _i64, _c_void_p, _int, _int, _int, _i64, _c_void_p, _i64, _int,
                                 _c_void_p]),
+    "idx_logits_paged_insert": (_int, [_c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _i64, _int,
+                                       _c_void_p, _i64, _c_void_p, _int, _int, _int, _i64,
+                                       _c_void_p, _i64, _int, _c_void_p]),
     "idx_topk": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p]),
     "idx_topk_merge": (_int, [_c_void_p, _c_void_p, _int, _i64, _int, _int, _int, _c_void_p,
                               _c_void_p]),
@@ -313,6 +316,60 @@ def logits_paged(q_values, q_scales, weights, cache, block_table, context_lens, 
                                   _ptr(context_lens), B, next_n, H, int(max_context_len),
                                   _ptr(logits), logits.stride(0), 1 if clean else 0, _stream(stream)),
            "idx_logits_paged")
+    return logits
+
+
+def logits_paged_insert(q, k_new, weights, cache, block_table, context_lens, next_n,
+                        max_context_len, logits=None, clean=True, stream=None):
+    """One decode step in one launch: the new tokens' K (k_new [B*next_n, 128], the
+    last next_n positions of each sequence) into their block-table slots, q
+    [B*next_n, H, 128] encoded to MXFP4, and the decode logits [B*next_n,
+    max_context_len] of the updated cache (as insert + quantize + logits_paged)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k_new", k_new)):
+        _dev(t, name)
+        if t.dtype not in (torch.bfloat16, torch.float32):
+            raise MxidxError(f"{name} must be bfloat16 or float32")
+        if not t.is_contiguous():
+            raise MxidxError(f"{name} must be contiguous")
+    if k_new.dtype != q.dtype:
+        raise MxidxError("q and k_new must have one dtype")
+    code = IDX_BF16 if q.dtype == torch.bfloat16 else IDX_F32
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise MxidxError("q must be [rows, heads, 128]")
+    R, H = q.shape[0], q.shape[1]
+    B = context_lens.numel()
+    if R != B * next_n:
+        raise MxidxError("q rows must be batch * next_n")
+    if tuple(k_new.shape) != (R, HEAD_DIM):
+        raise MxidxError("k_new must be [batch * next_n, 128]")
+    for name, t, dt in (("weights", weights, torch.float32), ("cache", cache, torch.uint8),
+                        ("block_table", block_table, torch.int32),
+                        ("context_lens", context_lens, torch.int32)):
+        _dev(t, name, dt)
+    for name, t in (("weights", weights), ("cache", cache), ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise MxidxError(f"{name} must be contiguous")
+    if tuple(weights.shape) != (R, H):
+        raise MxidxError("weights must be [rows, heads]")
+    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.shape[0] != B:
+        raise MxidxError("block_table must be [batch, pages] with unit inner stride")
+    if block_table.shape[1] * PAGE_SIZE < max_context_len:
+        raise MxidxError("block_table has fewer pages than max_context_len needs")
+    if logits is None:
+        fill = float("-inf") if clean else 0.0
+        logits = torch.full((R, max_context_len), fill, dtype=torch.float32, device=q.device)
+    _dev(logits, "logits", torch.float32)
+    if logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] < R or \
+            logits.shape[1] < max_context_len:
+        raise MxidxError("logits must be [>=rows, >=max_context_len] with contiguous rows")
+    num_pages = cache.numel() // (PAGE_SIZE * ROW_BYTES)
+    _check(lib().idx_logits_paged_insert(_ptr(q), _ptr(k_new), code, _ptr(weights), _ptr(cache),
+                                         num_pages, PAGE_SIZE, _ptr(block_table),
+                                         block_table.stride(0), _ptr(context_lens), B, next_n, H,
+                                         int(max_context_len), _ptr(logits), logits.stride(0),
+                                         1 if clean else 0, _stream(stream)),
+           "idx_logits_paged_insert")
     return logits
 
 

@@ -17,26 +17,10 @@
 // one coalesced 64-byte segment); lanes 0,4,8,12 of a row store the 4 scale bytes.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mxfp4_encode.hpp"
 
 namespace mxidx {
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// Smallest E with amax <= 6 * 2^E, clamped to [-127, 127], from the bits of a
-// non-negative finite fp32 amax = 1.f * 2^e:  E = e - 2 when f <= 0.5, else
-// e - 1.  Exponent fields 0 and 1 (amax < 2^-125) always clamp to -127.
-__device__ __forceinline__ int block_exponent(uint32_t a) {
-  const uint32_t ex = a >> 23;
-  if (ex <= 1u) return -127;
-  const int e = (int)ex - 127;
-  return ((a & 0x7fffffu) <= 0x400000u) ? e - 2 : e - 1;
-}
-
-// 2^E as an fp32 value (E in [-127, 126]; 2^-127 is the subnormal 0x00400000).
-__device__ __forceinline__ float pow2f(int E) {
-  return __uint_as_float(E >= -126 ? (uint32_t)(E + 127) << 23 : 0x00400000u);
-}
 
 struct Bf16In {
   uint4 v;
@@ -102,9 +86,7 @@ __device__ __forceinline__ void encode_row(const void* __restrict__ x, int64_t r
   a = max(a, (uint32_t)__shfl_xor((int)a, 1));
   a = max(a, (uint32_t)__shfl_xor((int)a, 2));
   const int E = block_exponent(a);
-  // An all-zero block needs no division (its codes are the sign bits alone);
-  // dividing by 1 keeps the subnormal scale out of the common case.
-  const float scale = (a == 0u) ? 1.0f : pow2f(E);
+  const float scale = block_divisor(a, E);
   const uint32_t codes = in.encode(scale);
   *reinterpret_cast<uint32_t*>(cdst + 4 * sub) = codes;
   if ((sub & 3) == 0) sdst[sub >> 2] = (uint8_t)(E + 127);

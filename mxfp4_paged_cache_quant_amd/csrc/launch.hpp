@@ -40,6 +40,15 @@ hipError_t launch_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
                                int64_t max_context_len, float* logits, int64_t ld, int clean,
                                hipStream_t stream);
 
+// The decode step's encodes fused into the paged logits: q rows and the new
+// tokens' K rows in bf16 (f32 = false) or fp32, encoded in the kernel.
+hipError_t launch_logits_paged_insert(const void* q, const void* k_new, bool f32,
+                                      const float* weights, uint8_t* cache, int64_t num_pages,
+                                      const int32_t* block_table, int64_t bt_row_stride,
+                                      const int32_t* context_lens, int B, int next_n, int H,
+                                      int64_t max_context_len, float* logits, int64_t ld,
+                                      int clean, hipStream_t stream);
+
 hipError_t launch_topk_merge(const float* values, const int32_t* indices, int world, int k_in,
                              int64_t rows, int interleave, int k, int32_t* out_idx,
                              hipStream_t stream);

@@ -31,6 +31,12 @@
 //    swaps across the wave halves and quarters combine the four lane groups'
 //    partial sums, after which lane l owns token l of the page and the wave
 //    stores 64 consecutive floats.
+//  * The fused decode step (query source RawQuery) takes q and the new
+//    tokens' K in bf16 / fp32: each wave encodes its query rows itself, and
+//    the wave whose pages hold a new token encodes it, writes it to the cache
+//    and patches its page registers, so one launch does insert, quantize and
+//    logits.  Only the sequence's own pages are written, and no other wave
+//    reads them.
 //  * Vector memory counters retire in issue order, so a wait for a load also
 //    waits for every store issued before it: for up to NN query rows per
 //    sequence (NN * heads/16 <= 8) every row's query is loaded up front and
@@ -39,6 +45,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "logits_reduce.hpp"
+#include "mxfp4_encode.hpp"
 
 namespace mxidx {
 namespace {
@@ -73,6 +80,94 @@ __device__ __forceinline__ QueryRegs<NH> load_query(const uint8_t* __restrict__ 
   return q;
 }
 
+// Query source of the paged kernel: MXFP4 rows encoded beforehand.  fetch()
+// issues the loads, finish() turns fetched registers into MFMA operands.
+struct PackedQuery {
+  const uint8_t* q_values;
+  const uint8_t* q_scales;
+  const float* weights;
+  static constexpr bool kInsert = false;
+  template <int NH>
+  using Fetched = QueryRegs<NH>;
+  template <int NH>
+  __device__ __forceinline__ QueryRegs<NH> fetch(int64_t r, int g, int n) const {
+    return load_query<NH>(q_values, q_scales, weights, r, g, n);
+  }
+  template <int NH>
+  __device__ __forceinline__ QueryRegs<NH> finish(const QueryRegs<NH>& f) const {
+    return f;
+  }
+};
+
+// Query source of the fused decode step: q rows in bf16 / fp32 (Blk), encoded
+// to MXFP4 in the wave -- lane (g, n) encodes block g of head 16*grp + n, the
+// block it supplies to the MFMA -- with the rule and conversion of the row
+// encoders, so the operands equal those of the separate encode.  The new
+// tokens' K rows come with it (kInsert).
+template <typename Blk>
+struct RawQuery {
+  const void* q;          // [rows, H, 128]
+  const void* k_new;      // [rows, 128]: row b*next_n + i is token L_b - next_n + i
+  const float* weights;
+  static constexpr bool kInsert = true;
+  using Block = Blk;
+  template <int NH>
+  struct Fetched {
+    Blk blk[NH];
+    float4 w[NH];
+  };
+  template <int NH>
+  __device__ __forceinline__ Fetched<NH> fetch(int64_t r, int g, int n) const {
+    constexpr int H = 16 * NH;
+    constexpr int kRow = kHeadDim * Blk::kElemBytes;
+    Fetched<NH> f;
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(static_cast<const uint8_t*>(q) + r * H * kRow, H * kRow);
+#pragma unroll
+    for (int grp = 0; grp < NH; ++grp) {
+      f.blk[grp].load(rs, (uint32_t)((16 * grp + n) * kRow + g * kBlock * Blk::kElemBytes));
+      f.w[grp] = *reinterpret_cast<const float4*>(weights + r * H + 16 * grp + 4 * g);
+    }
+    return f;
+  }
+  template <int NH>
+  __device__ __forceinline__ void pin_fetched(const Fetched<NH>& f) const {
+#pragma unroll
+    for (int grp = 0; grp < NH; ++grp) {
+      f.blk[grp].pin();
+      pin(f.w[grp]);
+    }
+  }
+  template <int NH>
+  __device__ __forceinline__ QueryRegs<NH> finish(const Fetched<NH>& f) const {
+    QueryRegs<NH> q;
+#pragma unroll
+    for (int grp = 0; grp < NH; ++grp) {
+      const uint32_t a = f.blk[grp].amax_bits();
+      const int E = block_exponent(a);
+      q.a[grp] = f.blk[grp].encode(block_divisor(a, E));
+      q.sa[grp] = E + 127;
+      q.w[grp] = f.w[grp];
+    }
+    return q;
+  }
+};
+
+// The new token's K block a wave preloads with its table entries: one bf16
+// row (64 bytes per lane) for a single held row; more would cost registers
+// that the fp32 and multi-row kernels do not have.  An empty stand-in
+// otherwise (those load the K row when they insert).
+template <typename QS, int NN, bool = QS::kInsert>
+struct NewRows {
+  static constexpr bool kPreload = false;
+  struct type {};
+};
+template <typename QS, int NN>
+struct NewRows<QS, NN, true> {
+  static constexpr bool kPreload = NN > 0 && NN * QS::Block::kElemBytes <= 2;
+  using type = typename QS::Block;
+};
+
 // Weighted ReLU head sum for the 64 tokens of one page; lane l returns token l.
 template <int NH>
 __device__ __forceinline__ float page_score(const PageRegs& pg, const QueryRegs<NH>& q, int lane) {
@@ -91,11 +186,12 @@ __device__ __forceinline__ float page_score(const PageRegs& pg, const QueryRegs<
 }
 
 // NN > 0: exactly NN query rows per sequence, all held in registers;
-// NN == 0: any next_n, one row at a time.
-template <int NH, int NN>
+// NN == 0: any next_n, one row at a time.  QS: the query source; with
+// QS::kInsert the wave holding a new token's page also encodes that token,
+// writes it to its cache slot and scores the page with it.
+template <int NH, int NN, typename QS>
 __global__ __launch_bounds__(kWave) void logits_paged_kernel(
-    const uint8_t* __restrict__ q_values, const uint8_t* __restrict__ q_scales,
-    const float* __restrict__ weights, const uint8_t* __restrict__ cache, int64_t num_pages,
+    QS qs, const uint8_t* __restrict__ cache, int64_t num_pages,
     const int32_t* __restrict__ block_table, int64_t bt_row_stride,
     const int32_t* __restrict__ context_lens, int next_n, int64_t width,
     float* __restrict__ logits, int64_t ld, int clean) {
@@ -116,14 +212,41 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
       buffer_rsrc(block_table + (int64_t)b * bt_row_stride + lp0, 4 * bt_count), 4u * lane, 0, 0);
   const uint32_t ctx_raw =
       __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(context_lens + b, 4), 0, 0, 0);
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::"v"(bt_lane));   // keeps the table load here, not sunk past the branch below
-  const int64_t ctx = (int32_t)__builtin_amdgcn_readfirstlane(ctx_raw);
+  // Raw held query rows and the new token's K row are fetched with the table
+  // and waited for with it, so they are encoded while the pages load (left to
+  // itself the compiler issues these loads after the page loads, and the
+  // encode would wait for the pages).
   constexpr int kRowsHeld = NN > 0 ? NN : 1;
-  QueryRegs<NH> qr[kRowsHeld];
-  if (NN > 0)
+  typename QS::template Fetched<NH> qf[kRowsHeld];
+  if (QS::kInsert && NN > 0)
 #pragma unroll
-    for (int i = 0; i < kRowsHeld; ++i) qr[i] = load_query<NH>(q_values, q_scales, weights, row0 + i, g, n);
+    for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n);
+  constexpr int kNewHeld = NN > 0 ? NN : 1;
+  constexpr bool kPreload = NewRows<QS, NN>::kPreload;
+  typename NewRows<QS, NN>::type kpre[kNewHeld];
+  if constexpr (kPreload) {
+    constexpr int kRow = kHeadDim * QS::Block::kElemBytes;
+#pragma unroll
+    for (int i = 0; i < NN; ++i)
+      kpre[i].load(buffer_rsrc(static_cast<const uint8_t*>(qs.k_new) + (row0 + i) * kRow, kRow),
+                   (uint32_t)(g * kBlock * QS::Block::kElemBytes));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  pin(bt_lane);                      // keeps the table load here, not sunk past the branch below
+  if constexpr (QS::kInsert) {
+    if (NN > 0)
+#pragma unroll
+      for (int i = 0; i < kRowsHeld; ++i) qs.template pin_fetched<NH>(qf[i]);
+  } else if (NN > 0) {
+    // encoded operands: fetched after the table wait (measured faster than
+    // waiting for them with it; the compiler issues them behind the pages)
+#pragma unroll
+    for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n);
+  }
+  if constexpr (kPreload)
+#pragma unroll
+    for (int i = 0; i < NN; ++i) kpre[i].pin();
+  const int64_t ctx = (int32_t)__builtin_amdgcn_readfirstlane(ctx_raw);
   // context lengths beyond the row width are a precondition violation; clamp so
   // that no store leaves the row
   const int64_t L = min(ctx, width);
@@ -148,8 +271,11 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
   }
   const int np = (int)min((int64_t)kPagesPerWave, (L - lp0 * kPage + kPage - 1) / kPage);
 
+
   PageRegs pg[kPagesPerWave];
   bool page_ok[kPagesPerWave];   // false: invalid block-table entry, the page is skipped
+  bool page_live[kPagesPerWave];
+  int64_t page_id[kPagesPerWave];
   const uint32_t off_code = 64u * n + 16u * g;
   const uint32_t off_scale = kPageCodeBytes + 4u * n;
 #pragma unroll
@@ -159,16 +285,109 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     page_ok[p] = p >= np || valid;
     const int live = __builtin_amdgcn_readfirstlane((p < np && valid) ? 1 : 0);
     const int64_t page = __builtin_amdgcn_readfirstlane(live ? pid : 0);
+    page_live[p] = live != 0;
+    page_id[p] = page;
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(cache + page * kPageBytes, live ? kPageBytes : 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
       const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, off_code + 1024u * j, 0, kNonTemporal);
       pg[p].code[j] = make_uint4(c.x, c.y, c.z, c.w);
       pg[p].scale[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_scale + 64u * j, 0, kNonTemporal);
     }
   }
   __builtin_amdgcn_sched_barrier(0);   // every page load issues before any compute
+
+  // held rows' operands first: a raw query is encoded while the pages load
+  // (pinned, or the compiler defers the encode into the scoring code, behind
+  // the waits for the pages)
+  QueryRegs<NH> qr[kRowsHeld];
+  if (NN > 0)
+#pragma unroll
+    for (int i = 0; i < kRowsHeld; ++i) {
+      qr[i] = qs.template finish<NH>(qf[i]);
+      if constexpr (QS::kInsert)
+#pragma unroll
+        for (int grp = 0; grp < NH; ++grp) {
+          pin(qr[i].a[grp]);
+          pin(qr[i].sa[grp]);
+        }
+    }
+
+  if constexpr (QS::kInsert) {
+    // New token i sits at position P = context_len - next_n + i.  Its page,
+    // when it is one of this wave's live pages, gets the token's 68 bytes both
+    // in the registers about to be scored and in the cache.  Every lane
+    // encodes block g of the row, so lane (g, n) holds the operand it
+    // supplies.  Pages past the row width belong to no wave: tokens there are
+    // not written.
+    using Blk = typename QS::Block;
+    constexpr int kRow = kHeadDim * Blk::kElemBytes;
+    // pre: the preloaded row (then branch-free: every wave encodes it and
+    // only the wave holding the token keeps it, so the scoring code stays in
+    // one block with the page loads), or null (the wave loads it if needed)
+    auto insert_one = [&](int i, const Blk* pre) {
+      const int64_t P = ctx - next_n + i;
+      const int64_t wp = P - lp0 * kPage;        // position within the wave's pages
+      const bool in_wave = P >= 0 && wp >= 0 && wp < (int64_t)np * kPage;   // uniform
+      if (!pre && !in_wave) return;
+      const int p_t = in_wave ? (int)(wp / kPage) : -1, off = in_wave ? (int)(wp % kPage) : 0;
+      const int j_t = off / 16, n_t = off % 16;
+      Blk kb;
+      if (pre)
+        kb = *pre;
+      else
+        kb.load(buffer_rsrc(static_cast<const uint8_t*>(qs.k_new) + (row0 + i) * kRow, kRow),
+                (uint32_t)(g * kBlock * Blk::kElemBytes));
+      const uint32_t a = kb.amax_bits();
+      const int E = block_exponent(a);
+      const uint4 code = kb.encode(block_divisor(a, E));
+      // the row's 4 scale bytes, one per lane group (all lanes of a group agree)
+      const uint32_t sword = (uint32_t)(E + 127) & 0xffu;
+      const uint32_t srow = (uint32_t)__builtin_amdgcn_readlane((int)sword, 0) |
+                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 16) << 8) |
+                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 32) << 16) |
+                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 48) << 24);
+      pin(code);                                   // encoded before the wait for the pages
+      pin((int)srow);
+      int64_t dst = 0;                             // the token's page (when live)
+      bool live = false;
+#pragma unroll
+      for (int p = 0; p < kPagesPerWave; ++p) {
+        const bool on = p == p_t && page_live[p];   // uniform
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool hit = on && j == j_t && n == n_t;
+          // component-wise: a select of whole structs would go through memory
+          const uint4 c = pg[p].code[j];
+          pg[p].code[j] = make_uint4(hit ? code.x : c.x, hit ? code.y : c.y, hit ? code.z : c.z,
+                                     hit ? code.w : c.w);
+          pg[p].scale[j] = hit ? srow : pg[p].scale[j];
+        }
+        dst = on ? page_id[p] : dst;
+        live = live || on;
+      }
+      // uniform by construction; readfirstlane keeps the descriptor in scalars
+      const int64_t dst_u = __builtin_amdgcn_readfirstlane((int)dst);
+      const int live_u = __builtin_amdgcn_readfirstlane(live ? 1 : 0);
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc(const_cast<uint8_t*>(cache) + dst_u * kPageBytes, live_u ? kPageBytes : 0);
+      const u32x4 cv = {code.x, code.y, code.z, code.w};
+      __builtin_amdgcn_raw_buffer_store_b128(
+          cv, rs, n == n_t ? (uint32_t)(off * kCodeBytes + 16 * g) : kDropOffset, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(
+          srow, rs, lane == n_t ? (uint32_t)(kPageCodeBytes + off * kScaleBytes) : kDropOffset,
+          0, 0);
+    };
+    if constexpr (kPreload) {
+#pragma unroll
+      for (int i = 0; i < NN; ++i) insert_one(i, &kpre[i]);
+    } else if constexpr (NN > 0) {
+#pragma unroll
+      for (int i = 0; i < NN; ++i) insert_one(i, nullptr);
+    } else {
+      for (int i = 0; i < next_n; ++i) insert_one(i, nullptr);
+    }
+  }
 
   if (NN > 0) {
     float out[kRowsHeld][kPagesPerWave];
@@ -185,7 +404,7 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     for (int i = 0; i < next_n; ++i) {
       const int64_t r = row0 + i;
       const int64_t ke = L - next_n + i + 1;
-      const QueryRegs<NH> q = load_query<NH>(q_values, q_scales, weights, r, g, n);
+      const QueryRegs<NH> q = qs.template finish<NH>(qs.template fetch<NH>(r, g, n));
 #pragma unroll
       for (int p = 0; p < kPagesPerWave; ++p)
         if (page_ok[p]) store(r, (lp0 + p) * kPage, ke, page_score<NH>(pg[p], q, lane));
@@ -193,15 +412,14 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
   }
 }
 
-template <int NH>
-hipError_t launch_nh(const uint8_t* qv, const uint8_t* qs, const float* w, const uint8_t* cache,
-                     int64_t num_pages, const int32_t* bt, int64_t bt_stride, const int32_t* ctx,
-                     int B, int next_n, int64_t width, float* logits, int64_t ld, int clean,
-                     hipStream_t stream) {
+template <int NH, typename QS>
+hipError_t launch_nh(QS qs, const uint8_t* cache, int64_t num_pages, const int32_t* bt,
+                     int64_t bt_stride, const int32_t* ctx, int B, int next_n, int64_t width,
+                     float* logits, int64_t ld, int clean, hipStream_t stream) {
   const int64_t pages = (width + kPage - 1) / kPage;
   const dim3 grid((unsigned)((pages + kPagesPerWave - 1) / kPagesPerWave), (unsigned)B);
-#define MXIDX_PAGED_ROWS(nn)                                                                     \
-  hipLaunchKernelGGL((logits_paged_kernel<NH, nn>), grid, dim3(kWave), 0, stream, qv, qs, w, cache, \
+#define MXIDX_PAGED_ROWS(nn)                                                                   \
+  hipLaunchKernelGGL((logits_paged_kernel<NH, nn, QS>), grid, dim3(kWave), 0, stream, qs, cache, \
                      num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean)
   // rows held in registers while rows * NH <= 8 (the query operands of 8 head groups)
   bool held = true;
@@ -228,19 +446,16 @@ hipError_t launch_nh(const uint8_t* qv, const uint8_t* qs, const float* w, const
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
-                               const float* weights, const uint8_t* cache, int64_t num_pages,
-                               const int32_t* block_table, int64_t bt_row_stride,
-                               const int32_t* context_lens, int B, int next_n, int H,
-                               int64_t max_context_len, float* logits, int64_t ld, int clean,
-                               hipStream_t stream) {
+template <typename QS>
+hipError_t launch_source(QS qs, const uint8_t* cache, int64_t num_pages,
+                         const int32_t* block_table, int64_t bt_row_stride,
+                         const int32_t* context_lens, int B, int next_n, int H,
+                         int64_t max_context_len, float* logits, int64_t ld, int clean,
+                         hipStream_t stream) {
 #define MXIDX_PAGED_CASE(nh)                                                                     \
   case nh:                                                                                       \
-    return launch_nh<nh>(q_values, q_scales, weights, cache, num_pages, block_table,             \
-                         bt_row_stride, context_lens, B, next_n, max_context_len, logits, ld,    \
-                         clean, stream);
+    return launch_nh<nh>(qs, cache, num_pages, block_table, bt_row_stride, context_lens, B,     \
+                         next_n, max_context_len, logits, ld, clean, stream);
   switch (H / 16) {
     MXIDX_PAGED_CASE(1)
     MXIDX_PAGED_CASE(2)
@@ -254,6 +469,34 @@ hipError_t launch_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
       return hipErrorInvalidValue;
   }
 #undef MXIDX_PAGED_CASE
+}
+
+}  // namespace
+
+hipError_t launch_logits_paged(const uint8_t* q_values, const uint8_t* q_scales,
+                               const float* weights, const uint8_t* cache, int64_t num_pages,
+                               const int32_t* block_table, int64_t bt_row_stride,
+                               const int32_t* context_lens, int B, int next_n, int H,
+                               int64_t max_context_len, float* logits, int64_t ld, int clean,
+                               hipStream_t stream) {
+  return launch_source(PackedQuery{q_values, q_scales, weights}, cache, num_pages, block_table,
+                       bt_row_stride, context_lens, B, next_n, H, max_context_len, logits, ld,
+                       clean, stream);
+}
+
+hipError_t launch_logits_paged_insert(const void* q, const void* k_new, bool f32,
+                                      const float* weights, uint8_t* cache, int64_t num_pages,
+                                      const int32_t* block_table, int64_t bt_row_stride,
+                                      const int32_t* context_lens, int B, int next_n, int H,
+                                      int64_t max_context_len, float* logits, int64_t ld,
+                                      int clean, hipStream_t stream) {
+  if (f32)
+    return launch_source(RawQuery<F32Block>{q, k_new, weights}, cache, num_pages, block_table,
+                         bt_row_stride, context_lens, B, next_n, H, max_context_len, logits, ld,
+                         clean, stream);
+  return launch_source(RawQuery<Bf16Block>{q, k_new, weights}, cache, num_pages, block_table,
+                       bt_row_stride, context_lens, B, next_n, H, max_context_len, logits, ld,
+                       clean, stream);
 }
 
 }  // namespace mxidx

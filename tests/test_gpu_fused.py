@@ -1,0 +1,119 @@
+"""GPU parity of the one-launch decode step (idx_logits_paged_insert): the cache
+bytes and logits must equal, bit for bit, those of the separate calls --
+idx_insert of the new tokens into their block-table slots, idx_quantize of q,
+idx_logits_paged -- which the other GPU tests hold to the oracle; one small case
+is also checked against the oracle directly."""
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_paged_cache_quant_amd as mx
+import workloads
+from oracle import logits as olog
+from tests.gpu_helpers import check_logits, dev, host, new_cache, oracle_q
+
+pytestmark = pytest.mark.gpu
+
+
+def _split_new_tokens(case, bt):
+    """The cache before the step (every token but the last next_n of each sequence)
+    and the step's new K rows with their slots through block table ``bt`` (-1
+    where the position is < 0 or the table entry is not a page)."""
+    lens = case["context_lens"].astype(np.int64)
+    nn = case["next_n"]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    pre_slots = case["slot_mapping"].copy()
+    B = len(lens)
+    k = case["k"]
+    filler = k[0] if len(k) else np.zeros(128, k.dtype)
+    k_new = np.empty((B * nn, 128), dtype=k.dtype)
+    new_slots = np.full(B * nn, -1, np.int64)
+    for b in range(B):
+        for i in range(nn):
+            pos = lens[b] - nn + i
+            if pos >= 0:
+                k_new[b * nn + i] = k[starts[b] + pos]
+                page = int(bt[b, pos // 64])
+                if 0 <= page < case["num_pages"]:
+                    new_slots[b * nn + i] = page * 64 + pos % 64
+                pre_slots[starts[b] + pos] = -1
+            else:
+                k_new[b * nn + i] = filler
+    return pre_slots, k_new, new_slots
+
+
+def _both(case, clean=True, block_table=None):
+    bt_np = case["block_table"] if block_table is None else block_table
+    pre_slots, k_new, new_slots = _split_new_tokens(case, bt_np)
+    bt = dev(bt_np)
+    ctx, w, q = dev(case["context_lens"]), dev(case["w"]), dev(case["q"])
+    cache_a = new_cache(case["num_pages"])
+    mx.insert(dev(case["k"]), dev(pre_slots), cache_a)
+    cache_b = cache_a.clone()
+    R, W = case["q"].shape[0], case["width"]
+    poison = float("nan")
+    la = torch.full((R, W), poison, dtype=torch.float32, device="cuda")
+    lb = la.clone()
+    # separate calls
+    mx.insert(dev(k_new), dev(new_slots), cache_a)
+    qv, qs = mx.quantize(q)
+    mx.logits_paged(qv, qs, w, cache_a, bt, ctx, case["next_n"], W, logits=la, clean=clean)
+    # one launch
+    mx.logits_paged_insert(q, dev(k_new), w, cache_b, bt, ctx, case["next_n"], W, logits=lb,
+                           clean=clean)
+    torch.cuda.synchronize()
+    return cache_a, cache_b, la, lb
+
+
+def _assert_same(case, clean=True, block_table=None, what=""):
+    cache_a, cache_b, la, lb = _both(case, clean, block_table)
+    ca, cb = host(cache_a), host(cache_b)
+    assert np.array_equal(ca, cb), f"{what}: cache bytes differ at {np.argwhere(ca != cb)[:4].tolist()}"
+    a, b = host(la).view(np.uint32), host(lb).view(np.uint32)
+    assert np.array_equal(a, b), f"{what}: logits differ at {np.argwhere(a != b)[:4].tolist()}"
+    return cache_b, lb
+
+
+def test_fused_tiny_against_oracle():
+    case = workloads.decode_case(11, seq_lens=[1, 63, 64, 65, 300, 0], H=32, next_n=1,
+                                 dtype="f32", width=337)
+    cache, logits = _assert_same(case, what="tiny")
+    qc, qs = oracle_q(case)
+    ref, bound = olog.paged_mqa_logits(qc, qs, case["w"], host(cache), case["block_table"],
+                                       case["context_lens"], 1, case["width"], with_bound=True)
+    check_logits(host(logits), ref, bound, "fused tiny vs oracle")
+
+
+@pytest.mark.parametrize("dtype,H,next_n,lens", [
+    ("bf16", 32, 1, [1, 63, 64, 65, 300, 0, 191, 192, 193]),
+    ("f32", 64, 3, [2, 5, 64, 129, 250, 191, 192, 193]),     # 2 < next_n: position -1 skipped
+    ("bf16", 16, 2, [192, 193, 384, 385, 1, 2]),              # new tokens across wave boundaries
+    ("bf16", 32, 4, [4, 3, 0, 64, 67, 300]),
+    ("bf16", 32, 5, [5, 64, 130, 700, 2]),                     # rows not held in registers
+    ("f32", 128, 1, [100, 17, 1000]),
+    ("bf16", 48, 2, [127, 128, 1, 640]),
+    ("bf16", 64, 16, [40, 200, 16]),
+])
+def test_fused_equals_separate_calls(dtype, H, next_n, lens):
+    case = workloads.decode_case(H * 13 + next_n, seq_lens=lens, H=H, next_n=next_n, dtype=dtype,
+                                 spare_pages=3, width=max(lens) + 45)
+    _assert_same(case, what=f"{dtype} H={H} next_n={next_n}")
+
+
+def test_fused_clean_false():
+    case = workloads.decode_case(7, seq_lens=[65, 700, 3, 129], H=32, next_n=2, width=800)
+    _assert_same(case, clean=False, what="clean=False")
+
+
+def test_fused_invalid_table_entries_skip_the_page():
+    case = workloads.decode_case(8, seq_lens=[130, 300, 64, 65], H=32, next_n=1, width=320)
+    bt = case["block_table"].copy()
+    bt[0, 2] = -1                          # the page of sequence 0's new token (position 129)
+    bt[1, 4] = case["num_pages"] + 5       # the page of sequence 1's new token (position 299)
+    _assert_same(case, block_table=bt, what="invalid entries")
+
+
+def test_fused_paged_decode_16x8192():
+    case = workloads.paged_decode()
+    _assert_same(case, clean=False, what="16x8192")
