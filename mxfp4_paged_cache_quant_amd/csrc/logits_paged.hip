@@ -131,14 +131,6 @@ struct RawQuery {
     return f;
   }
   template <int NH>
-  __device__ __forceinline__ void pin_fetched(const Fetched<NH>& f) const {
-#pragma unroll
-    for (int grp = 0; grp < NH; ++grp) {
-      f.blk[grp].pin();
-      pin(f.w[grp]);
-    }
-  }
-  template <int NH>
   __device__ __forceinline__ QueryRegs<NH> finish(const Fetched<NH>& f) const {
     QueryRegs<NH> q;
 #pragma unroll
@@ -191,7 +183,7 @@ __device__ __forceinline__ float page_score(const PageRegs& pg, const QueryRegs<
 // writes it to its cache slot and scores the page with it.
 template <int NH, int NN, typename QS>
 __global__ __launch_bounds__(kWave) void logits_paged_kernel(
-    QS qs, const uint8_t* __restrict__ cache, int64_t num_pages,
+    QS qs, const uint8_t* cache, int64_t num_pages,   // written when inserting: no restrict
     const int32_t* __restrict__ block_table, int64_t bt_row_stride,
     const int32_t* __restrict__ context_lens, int next_n, int64_t width,
     float* __restrict__ logits, int64_t ld, int clean) {
@@ -212,15 +204,12 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
       buffer_rsrc(block_table + (int64_t)b * bt_row_stride + lp0, 4 * bt_count), 4u * lane, 0, 0);
   const uint32_t ctx_raw =
       __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(context_lens + b, 4), 0, 0, 0);
-  // Raw held query rows and the new token's K row are fetched with the table
-  // and waited for with it, so they are encoded while the pages load (left to
-  // itself the compiler issues these loads after the page loads, and the
-  // encode would wait for the pages).
+  // The new token's K row is issued right behind the table loads.  The asm
+  // below waits for the table only (counters retire in order, later loads stay
+  // in flight) and, clobbering memory when inserting, keeps every load on its
+  // side.
   constexpr int kRowsHeld = NN > 0 ? NN : 1;
   typename QS::template Fetched<NH> qf[kRowsHeld];
-  if (QS::kInsert && NN > 0)
-#pragma unroll
-    for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n);
   constexpr int kNewHeld = NN > 0 ? NN : 1;
   constexpr bool kPreload = NewRows<QS, NN>::kPreload;
   typename NewRows<QS, NN>::type kpre[kNewHeld];
@@ -231,21 +220,24 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
       kpre[i].load(buffer_rsrc(static_cast<const uint8_t*>(qs.k_new) + (row0 + i) * kRow, kRow),
                    (uint32_t)(g * kBlock * QS::Block::kElemBytes));
   }
-  __builtin_amdgcn_sched_barrier(0);
-  pin(bt_lane);                      // keeps the table load here, not sunk past the branch below
+  // Raw held query rows: fetched after the table wait and pinned ahead of the
+  // page loads by a second memory clobber (left alone, the compiler issues
+  // them behind the pages, and their encode would wait for the pages; issued
+  // with the table, their 8 KB per wave slow the table loads).  Encoded rows
+  // are fetched after the table wait with no clobbers: the compiler's order
+  // (behind the weights, ahead of the pages) measured fastest for them.
   if constexpr (QS::kInsert) {
+    asm volatile("" ::"v"(bt_lane) : "memory");
     if (NN > 0)
 #pragma unroll
-      for (int i = 0; i < kRowsHeld; ++i) qs.template pin_fetched<NH>(qf[i]);
-  } else if (NN > 0) {
-    // encoded operands: fetched after the table wait (measured faster than
-    // waiting for them with it; the compiler issues them behind the pages)
+      for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n);
+    asm volatile("" ::: "memory");
+  } else {
+    asm volatile("" ::"v"(bt_lane));   // keeps the table load here, not sunk past the branch below
+    if (NN > 0)
 #pragma unroll
-    for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n);
+      for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n);
   }
-  if constexpr (kPreload)
-#pragma unroll
-    for (int i = 0; i < NN; ++i) kpre[i].pin();
   const int64_t ctx = (int32_t)__builtin_amdgcn_readfirstlane(ctx_raw);
   // context lengths beyond the row width are a precondition violation; clamp so
   // that no store leaves the row
@@ -271,11 +263,59 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
   }
   const int np = (int)min((int64_t)kPagesPerWave, (L - lp0 * kPage + kPage - 1) / kPage);
 
+  if constexpr (QS::kInsert) {
+    // New token i sits at position P = context_len - next_n + i.  The wave
+    // whose live pages hold it encodes it -- every lane block g of the row --
+    // and writes its 68 bytes to the cache before loading the pages: lane
+    // (g, n) later loads exactly the 16 code bytes it stores here, and every
+    // lane of the token's column stores the 4 scale bytes it later loads, so
+    // the page loads see the new token (program order of one lane, one
+    // address).  Pages past the row width belong to no wave: tokens there are
+    // not written.
+    using Blk = typename QS::Block;
+    constexpr int kRow = kHeadDim * Blk::kElemBytes;
+    auto insert_one = [&](int i, const Blk* pre) {   // pre: the preloaded row, or null
+      const int64_t P = ctx - next_n + i;
+      const int64_t wp = P - lp0 * kPage;        // position within the wave's pages
+      if (P < 0 || wp < 0 || wp >= (int64_t)np * kPage) return;   // uniform
+      const int p_t = (int)(wp / kPage), off = (int)(wp % kPage);
+      const int n_t = off % 16;
+      const int64_t dst = __builtin_amdgcn_readlane(bt_lane, p_t);
+      if (dst < 0 || dst >= num_pages) return;    // invalid table entry: not written
+      Blk kb;
+      if (pre)
+        kb = *pre;
+      else
+        kb.load(buffer_rsrc(static_cast<const uint8_t*>(qs.k_new) + (row0 + i) * kRow, kRow),
+                (uint32_t)(g * kBlock * Blk::kElemBytes));
+      const uint32_t a = kb.amax_bits();
+      const int E = block_exponent(a);
+      const uint4 code = kb.encode(block_divisor(a, E));
+      // the row's 4 scale bytes, one per lane group (all lanes of a group agree)
+      const uint32_t sword = (uint32_t)(E + 127) & 0xffu;
+      const uint32_t srow = (uint32_t)__builtin_amdgcn_readlane((int)sword, 0) |
+                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 16) << 8) |
+                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 32) << 16) |
+                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 48) << 24);
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc(const_cast<uint8_t*>(cache) + dst * kPageBytes, kPageBytes);
+      const u32x4 cv = {code.x, code.y, code.z, code.w};
+      __builtin_amdgcn_raw_buffer_store_b128(
+          cv, rs, n == n_t ? (uint32_t)(off * kCodeBytes + 16 * g) : kDropOffset, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(
+          srow, rs, n == n_t ? (uint32_t)(kPageCodeBytes + off * kScaleBytes) : kDropOffset, 0,
+          0);
+    };
+    if constexpr (kPreload) {
+#pragma unroll
+      for (int i = 0; i < NN; ++i) insert_one(i, &kpre[i]);
+    } else {
+      for (int i = 0; i < next_n; ++i) insert_one(i, nullptr);
+    }
+  }
 
   PageRegs pg[kPagesPerWave];
   bool page_ok[kPagesPerWave];   // false: invalid block-table entry, the page is skipped
-  bool page_live[kPagesPerWave];
-  int64_t page_id[kPagesPerWave];
   const uint32_t off_code = 64u * n + 16u * g;
   const uint32_t off_scale = kPageCodeBytes + 4u * n;
 #pragma unroll
@@ -285,8 +325,6 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     page_ok[p] = p >= np || valid;
     const int live = __builtin_amdgcn_readfirstlane((p < np && valid) ? 1 : 0);
     const int64_t page = __builtin_amdgcn_readfirstlane(live ? pid : 0);
-    page_live[p] = live != 0;
-    page_id[p] = page;
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(cache + page * kPageBytes, live ? kPageBytes : 0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -295,6 +333,12 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
       pg[p].scale[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_scale + 64u * j, 0, kNonTemporal);
     }
   }
+  // Keep the preloaded K rows live until here in every wave: a wave without a
+  // new token would otherwise reuse their registers while the loads are in
+  // flight, which waits for every load before the page loads can issue.
+  if constexpr (kPreload)
+#pragma unroll
+    for (int i = 0; i < NN; ++i) kpre[i].pin();
   __builtin_amdgcn_sched_barrier(0);   // every page load issues before any compute
 
   // held rows' operands first: a raw query is encoded while the pages load
@@ -312,82 +356,6 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
           pin(qr[i].sa[grp]);
         }
     }
-
-  if constexpr (QS::kInsert) {
-    // New token i sits at position P = context_len - next_n + i.  Its page,
-    // when it is one of this wave's live pages, gets the token's 68 bytes both
-    // in the registers about to be scored and in the cache.  Every lane
-    // encodes block g of the row, so lane (g, n) holds the operand it
-    // supplies.  Pages past the row width belong to no wave: tokens there are
-    // not written.
-    using Blk = typename QS::Block;
-    constexpr int kRow = kHeadDim * Blk::kElemBytes;
-    // pre: the preloaded row (then branch-free: every wave encodes it and
-    // only the wave holding the token keeps it, so the scoring code stays in
-    // one block with the page loads), or null (the wave loads it if needed)
-    auto insert_one = [&](int i, const Blk* pre) {
-      const int64_t P = ctx - next_n + i;
-      const int64_t wp = P - lp0 * kPage;        // position within the wave's pages
-      const bool in_wave = P >= 0 && wp >= 0 && wp < (int64_t)np * kPage;   // uniform
-      if (!pre && !in_wave) return;
-      const int p_t = in_wave ? (int)(wp / kPage) : -1, off = in_wave ? (int)(wp % kPage) : 0;
-      const int j_t = off / 16, n_t = off % 16;
-      Blk kb;
-      if (pre)
-        kb = *pre;
-      else
-        kb.load(buffer_rsrc(static_cast<const uint8_t*>(qs.k_new) + (row0 + i) * kRow, kRow),
-                (uint32_t)(g * kBlock * Blk::kElemBytes));
-      const uint32_t a = kb.amax_bits();
-      const int E = block_exponent(a);
-      const uint4 code = kb.encode(block_divisor(a, E));
-      // the row's 4 scale bytes, one per lane group (all lanes of a group agree)
-      const uint32_t sword = (uint32_t)(E + 127) & 0xffu;
-      const uint32_t srow = (uint32_t)__builtin_amdgcn_readlane((int)sword, 0) |
-                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 16) << 8) |
-                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 32) << 16) |
-                            ((uint32_t)__builtin_amdgcn_readlane((int)sword, 48) << 24);
-      pin(code);                                   // encoded before the wait for the pages
-      pin((int)srow);
-      int64_t dst = 0;                             // the token's page (when live)
-      bool live = false;
-#pragma unroll
-      for (int p = 0; p < kPagesPerWave; ++p) {
-        const bool on = p == p_t && page_live[p];   // uniform
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool hit = on && j == j_t && n == n_t;
-          // component-wise: a select of whole structs would go through memory
-          const uint4 c = pg[p].code[j];
-          pg[p].code[j] = make_uint4(hit ? code.x : c.x, hit ? code.y : c.y, hit ? code.z : c.z,
-                                     hit ? code.w : c.w);
-          pg[p].scale[j] = hit ? srow : pg[p].scale[j];
-        }
-        dst = on ? page_id[p] : dst;
-        live = live || on;
-      }
-      // uniform by construction; readfirstlane keeps the descriptor in scalars
-      const int64_t dst_u = __builtin_amdgcn_readfirstlane((int)dst);
-      const int live_u = __builtin_amdgcn_readfirstlane(live ? 1 : 0);
-      const __amdgpu_buffer_rsrc_t rs =
-          buffer_rsrc(const_cast<uint8_t*>(cache) + dst_u * kPageBytes, live_u ? kPageBytes : 0);
-      const u32x4 cv = {code.x, code.y, code.z, code.w};
-      __builtin_amdgcn_raw_buffer_store_b128(
-          cv, rs, n == n_t ? (uint32_t)(off * kCodeBytes + 16 * g) : kDropOffset, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b32(
-          srow, rs, lane == n_t ? (uint32_t)(kPageCodeBytes + off * kScaleBytes) : kDropOffset,
-          0, 0);
-    };
-    if constexpr (kPreload) {
-#pragma unroll
-      for (int i = 0; i < NN; ++i) insert_one(i, &kpre[i]);
-    } else if constexpr (NN > 0) {
-#pragma unroll
-      for (int i = 0; i < NN; ++i) insert_one(i, nullptr);
-    } else {
-      for (int i = 0; i < next_n; ++i) insert_one(i, nullptr);
-    }
-  }
 
   if (NN > 0) {
     float out[kRowsHeld][kPagesPerWave];

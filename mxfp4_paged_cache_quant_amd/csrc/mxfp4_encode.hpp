@@ -40,12 +40,9 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t rs, uint32_t off)
   return make_uint4(c.x, c.y, c.z, c.w);
 }
 
-// An empty asm that reads x: the loads behind x must have returned here, and
-// they cannot be moved past this point.
+// An empty asm that reads x: x is computed here (its loads have returned) and
+// is not deferred past this point.
 __device__ __forceinline__ void pin(const uint4& x) {
-  asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
-}
-__device__ __forceinline__ void pin(const float4& x) {
   asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
 }
 __device__ __forceinline__ void pin(int x) { asm volatile("" ::"v"(x)); }
