@@ -106,3 +106,43 @@ def test_fused_step_and_merge_graph_replays_match_eager():
             assert np.array_equal(a, host(t)), rep
         for r in range(2 * B):
             assert np.array_equal(got_vis[r], host(logits)[r, :int(host(ke)[r])]), (rep, r)
+
+
+def test_one_launch_decode_step_graph_replays_match_eager():
+    # idx_logits_paged_insert + idx_topk captured; new K rows and queries change between replays
+    case = workloads.decode_case(52, seq_lens=[1000, 4000, 64, 2500, 193], H=32, next_n=1, topk=512)
+    B, W = 5, case["width"]
+    cache = new_cache(case["num_pages"], fill=0)
+    mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
+    last = np.cumsum(case["context_lens"]) - 1
+    k_new = dev(case["k"][last])
+    q = dev(case["q"])
+    w = dev(case["w"])
+    bt = dev(case["block_table"])
+    ctx = dev(case["context_lens"])
+    ke = dev(olog.decode_visible_end(case["context_lens"], 1).astype(np.int32))
+    logits = torch.empty((B, W), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda")
+
+    def step():
+        mx.logits_paged_insert(q, k_new, w, cache, bt, ctx, 1, W, logits=logits, clean=True)
+        mx.topk(logits, None, ke, 512, out=idx)
+
+    step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    rng = np.random.default_rng(3)
+    for rep in range(3):
+        q.copy_(dev(workloads.bf16_bits(rng.standard_normal(case["q"].shape).astype(np.float32))))
+        k_new.copy_(dev(workloads.bf16_bits(rng.standard_normal((B, 128)).astype(np.float32))))
+        g.replay()
+        torch.cuda.synchronize()
+        got_logits, got_idx, got_cache = host(logits).copy(), host(idx).copy(), host(cache).copy()
+        _ = torch.randn(1000, device="cuda").sum().item()
+        step()
+        torch.cuda.synchronize()
+        assert np.array_equal(got_logits, host(logits)), rep
+        assert np.array_equal(got_idx, host(idx)), rep
+        assert np.array_equal(got_cache, host(cache)), rep
