@@ -385,7 +385,112 @@ __device__ __forceinline__ void emit_regs(Shared<BINS>& s, const uint32_t (&key)
   tie_run += total >> 16;
 }
 
-template <int NT, int E, int BINS>
+// Top-k of register-held (key, column) pairs: slots e < nv of each thread, of
+// which those with okmask bit e set are valid (the others take part as
+// (kmin, 0xffffffff), below every valid pair).  Ranking: key descending, then
+// column ascending.  Writes the min(k, valid) selected columns to out[0, k),
+// then -1; the order is deterministic.  Starts with the histogram cleared and
+// ccount zero.
+template <int NT, int FEW, int BINS, int E>
+__device__ __forceinline__ void select_pairs(Shared<BINS>& s, uint32_t (&key)[E],
+                                             const uint32_t (&col)[E], uint32_t okmask, int nv,
+                                             int k, int32_t* __restrict__ out, int parity) {
+  constexpr int kWaves = NT / kWave;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  // valid count and key range over the valid candidates
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((okmask >> e) & 1u) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+    }
+  kmin = ~wave_umax(~kmin);
+  kmax = wave_umax(kmax);
+  if (lane == 0) {
+    s.wave_tot[1][wid] = kmin;
+    s.wave_tot[1][kMaxWaves + wid] = kmax;
+  }
+  uint32_t total_valid;
+  (void)block_scan<NT>((uint32_t)__popc(okmask), s, parity, total_valid);   // one barrier
+  parity ^= 1;
+  kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
+  kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
+  __syncthreads();                              // the next scan rewrites wave_tot[1]
+
+  if (total_valid <= (uint32_t)k) {             // every valid candidate, then -1
+    uint32_t tot;
+    uint32_t pos = block_scan<NT>((uint32_t)__popc(okmask), s, parity, tot);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((okmask >> e) & 1u) out[pos++] = (int32_t)col[e];
+    for (uint32_t i = tot + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (!((okmask >> e) & 1u)) key[e] = kmin;   // empty: (kmin, 0xffffffff), below every valid one
+
+  uint32_t key_t, col_t;
+  bool col_known = false;
+  uint32_t u_t = 0, need_ties = (uint32_t)k;
+  const uint32_t range = kmax - kmin;
+  const int L = range ? 32 - __clz(range) : 0;
+  if (L > 0) {
+    constexpr int D = digit_bits<BINS>();
+    const int nsh = L > D ? L - D : 0;
+    hist_first(s, key, nv, kmin, nsh);
+    __syncthreads();
+    select_bin<NT>(s, (uint32_t)k, parity);
+    parity ^= 1;
+    const uint32_t need = (uint32_t)k - s.sel[1];
+    const uint32_t bin = s.sel[0];
+    if (nsh == 0) {
+      u_t = bin;
+      need_ties = need;
+    } else if (s.sel[2] <= (uint32_t)FEW) {
+      select_few<NT, FEW, true>(s, key, col, nv, 0u, kmin, nsh, bin, need,
+                                      (uint32_t)k - need, out, parity);
+      return;
+    } else {
+      refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
+    }
+    // the last radix level's bin holds exactly the keys equal to the threshold:
+    // when all of them are taken, no column select is needed
+    if (!col_known && s.sel[2] == need_ties) {
+      col_t = 0xfffffffeu;                      // every valid column (empty slots are 0xffffffff)
+      col_known = true;
+    }
+  }
+  key_t = kmin + u_t;
+  if (!col_known) {
+    // the need_ties lowest columns among the keys equal to key_t: largest ~column
+    uint32_t key2[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) key2[e] = (e < nv && key[e] == key_t) ? ~col[e] : 0u;
+    uint32_t u2, n2;
+    refine_regs<NT>(s, key2, nv, 0u, 32, 0u, need_ties, parity, u2, n2);
+    col_t = ~u2;
+  }
+  // ordered output of every candidate at or above (key_t, col_t)
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    cnt += (e < nv && (key[e] > key_t || (key[e] == key_t && col[e] <= col_t))) ? 1u : 0u;
+  uint32_t tot;
+  uint32_t pos = block_scan<NT>(cnt, s, parity, tot);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e < nv && (key[e] > key_t || (key[e] == key_t && col[e] <= col_t))) {
+      if (pos < (uint32_t)k) out[pos] = (int32_t)col[e];
+      ++pos;
+    }
+}
+
+// kLong = false: launched only when every row fits in registers (the long-row
+// code, and its registers, are left out).
+template <int NT, int E, int BINS, bool kLong>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logits, int64_t ld,
                                                   const int32_t* __restrict__ ks,
                                                   const int32_t* __restrict__ ke, int k,
@@ -464,122 +569,211 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
                          false, 0, 0u, out, 0u, k, parity, gr, tr);
     return;
   }
-
-  // ---- long row, chunks of C keys ----
-  // Pass 1: histogram of the top digit.  Workgroups of <= 8 waves keep one
-  // 11-bit histogram per wave (fewer colliding LDS atomics), merged
-  // afterwards; larger workgroups use the shared histogram's full width.
-  constexpr bool kWaveHist = kWaves <= 8;
-  constexpr int D1 = kWaveHist ? 11 : digit_bits<BINS>();
-  constexpr int S1 = 32 - D1;
-  uint32_t* wh = kWaveHist ? dyn + wid * kWaveHistBins : s.hist;
-  if (kWaveHist)
-    for (int i = lane; i < kWaveHistBins; i += kWave) wh[i] = 0;
-  clear_hist<NT>(s);
-  __syncthreads();
-  for_chunks<NT, E>(src, n, vec, [&](int64_t, const uint32_t (&key)[E], int nv) {
+  if constexpr (kLong) {
+    // ---- long row, chunks of C keys ----
+    // One read when an estimate holds: the first chunk gives a key t_est with
+    // about 1.5 k of the row's keys expected at or above it (one histogram level
+    // over the chunk's own range); one pass then keeps every key >= t_est, each
+    // wave appending to its own region of the pair buffer in row order (a ballot
+    // prefix, no atomics, no barriers).  With at least k keys kept and no region
+    // full, the row's top-k is the top-k of the kept pairs.  Otherwise (a row
+    // whose first chunk misrepresents it) the two-pass path below runs.
+    {
+      constexpr int kRegion = kCandPairs / kWaves;  // pairs per wave
+      constexpr int E2 = kRegion / kWave;           // kept pairs per thread afterwards
+      uint32_t* ck = dyn;
+      uint32_t* cc = dyn + kCandPairs;
+      uint32_t t_est;
+      {
+        uint32_t key[E];
+        (void)load_keys<E>(src, n, vec, key);       // n > C: a full chunk
+        clear_hist<NT>(s);
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (e < nv) atomicAdd(&wh[key[e] >> S1], 1u);
-  });
-  __syncthreads();
-  if (kWaveHist) {
-    for (int b = threadIdx.x; b < kWaveHistBins; b += NT) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) c += dyn[w * kWaveHistBins + b];
-      s.hist[b] = c;
-    }
-    __syncthreads();
-  }
-  select_bin<NT>(s, (uint32_t)k, parity);
-  parity ^= 1;
-  const uint32_t bin1 = s.sel[0];
-  const uint32_t above1 = s.sel[1];
-  uint32_t* cand_keys = dyn;                      // the per-wave histograms are dead now
-  uint32_t* cand_cols = dyn + kCandPairs;
-  uint32_t m;                                     // keys in bin1
-  {
-    // Pass 2: keys above bin1 go straight out; bin1's keys become candidates
-    // (stored while they fit; their count decides the path afterwards).
-    uint32_t gbase = 0, cbase = 0;
-    for_chunks<NT, E>(src, n, vec, [&](int64_t c0, const uint32_t (&key)[E], int nv) {
-      uint32_t cg = 0, cq = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        cg += (e < nv && (key[e] >> S1) > bin1) ? 1u : 0u;
-        cq += (e < nv && (key[e] >> S1) == bin1) ? 1u : 0u;
-      }
-      uint32_t total;
-      const uint32_t pre = block_scan<NT>(cg | (cq << 16), s, parity, total);
-      parity ^= 1;
-      uint32_t g = gbase + (pre & 0xffffu), q = cbase + (pre >> 16);
-      const int64_t col0 = lo + c0 + (int64_t)E * threadIdx.x;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (e >= nv) continue;
-        const uint32_t b = key[e] >> S1;
-        if (b > bin1) {
-          if (g < (uint32_t)k) out[g] = (int32_t)(col0 + e);
-          ++g;
-        } else if (b == bin1) {
-          if (q < (uint32_t)kCandPairs) {
-            cand_keys[q] = key[e];
-            cand_cols[q] = (uint32_t)(col0 + e);
-          }
-          ++q;
+        for (int e = 0; e < E; ++e) {
+          kmin = min(kmin, key[e]);
+          kmax = max(kmax, key[e]);
         }
+        kmin = ~wave_umax(~kmin);
+        kmax = wave_umax(kmax);
+        if (lane == 0) {
+          s.wave_tot[1][wid] = kmin;
+          s.wave_tot[1][kMaxWaves + wid] = kmax;
+        }
+        __syncthreads();
+        kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
+        kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
+        const uint32_t range = kmax - kmin;
+        const int L = range ? 32 - __clz(range) : 0;
+        constexpr int D = digit_bits<BINS>();
+        const int nsh = L > D ? L - D : 0;
+        hist_first(s, key, E, kmin, nsh);
+        __syncthreads();
+        const int64_t want = ((int64_t)3 * k * C) / (2 * n) + 32;   // of the chunk's C keys
+        select_bin<NT>(s, (uint32_t)min(want, C), parity);
+        parity ^= 1;
+        t_est = kmin + (s.sel[0] << nsh);           // lower edge of that key's bin
       }
-      gbase += total & 0xffffu;
-      cbase += total >> 16;
-    });
-    m = cbase;
-    __syncthreads();
-  }
-  uint32_t u_t, need_ties;
-  if (m <= (uint32_t)kCandPairs) {
-    // candidates back into registers, consecutive per thread
-    constexpr int E2 = kCandPairs / NT;
-    uint32_t key[E2], cols[E2];
-    const int first = E2 * threadIdx.x;
-    const int nv = max(0, min(E2, (int)m - first));
+      uint32_t kept = 0;                            // this wave's pairs (wave-uniform)
+      uint32_t* wk = ck + wid * kRegion;
+      uint32_t* wc = cc + wid * kRegion;
+      for_chunks<NT, E>(src, n, vec, [&](int64_t c0, const uint32_t (&key)[E], int nv) {
+        const uint32_t col0 = (uint32_t)(lo + c0 + (int64_t)E * threadIdx.x);
 #pragma unroll
-    for (int e = 0; e < E2; ++e) {
-      key[e] = (e < nv) ? cand_keys[first + e] : 0u;
-      cols[e] = (e < nv) ? cand_cols[first + e] : 0u;
+        for (int e = 0; e < E; ++e) {
+          const bool take = e < nv && key[e] >= t_est;
+          const uint64_t m = __ballot(take);
+          if (m) {                                  // wave-uniform
+            const uint32_t pos = kept + __builtin_amdgcn_mbcnt_hi(
+                                            (uint32_t)(m >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (take && pos < (uint32_t)kRegion) {
+              wk[pos] = key[e];
+              wc[pos] = col0 + (uint32_t)e;
+            }
+            kept += (uint32_t)__popcll(m);
+          }
+        }
+      });
+      if (lane == 0) s.wave_tot[0][wid] = kept;
+      __syncthreads();
+      uint32_t total = 0, fullest = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        total += s.wave_tot[0][w];
+        fullest = max(fullest, s.wave_tot[0][w]);
+      }
+      if (total >= (uint32_t)k && fullest <= (uint32_t)kRegion) {
+        uint32_t key[E2], col[E2];
+        uint32_t okmask = 0;
+#pragma unroll
+        for (int e = 0; e < E2; ++e) {
+          const uint32_t i = (uint32_t)(lane * E2 + e);
+          key[e] = wk[i];
+          col[e] = wc[i];
+          okmask |= (i < kept ? 1u : 0u) << e;
+        }
+        __syncthreads();                            // every count read before the next scans
+        select_pairs<NT, kFewMerge>(s, key, col, okmask, E2, k, out, parity);
+        return;
+      }
+      __syncthreads();                              // counts read before the buffers are reused
     }
-    refine_regs<NT>(s, key, nv, 0u, S1, bin1, (uint32_t)k - above1, parity, u_t, need_ties);
+    // Pass 1: histogram of the top digit.  Workgroups of <= 8 waves keep one
+    // 11-bit histogram per wave (fewer colliding LDS atomics), merged
+    // afterwards; larger workgroups use the shared histogram's full width.
+    constexpr bool kWaveHist = kWaves <= 8;
+    constexpr int D1 = kWaveHist ? 11 : digit_bits<BINS>();
+    constexpr int S1 = 32 - D1;
+    uint32_t* wh = kWaveHist ? dyn + wid * kWaveHistBins : s.hist;
+    if (kWaveHist)
+      for (int i = lane; i < kWaveHistBins; i += kWave) wh[i] = 0;
+    clear_hist<NT>(s);
+    __syncthreads();
+    for_chunks<NT, E>(src, n, vec, [&](int64_t, const uint32_t (&key)[E], int nv) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (e < nv) atomicAdd(&wh[key[e] >> S1], 1u);
+    });
+    __syncthreads();
+    if (kWaveHist) {
+      for (int b = threadIdx.x; b < kWaveHistBins; b += NT) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c += dyn[w * kWaveHistBins + b];
+        s.hist[b] = c;
+      }
+      __syncthreads();
+    }
+    select_bin<NT>(s, (uint32_t)k, parity);
+    parity ^= 1;
+    const uint32_t bin1 = s.sel[0];
+    const uint32_t above1 = s.sel[1];
+    uint32_t* cand_keys = dyn;                      // the per-wave histograms are dead now
+    uint32_t* cand_cols = dyn + kCandPairs;
+    uint32_t m;                                     // keys in bin1
+    {
+      // Pass 2: keys above bin1 go straight out; bin1's keys become candidates
+      // (stored while they fit; their count decides the path afterwards).
+      uint32_t gbase = 0, cbase = 0;
+      for_chunks<NT, E>(src, n, vec, [&](int64_t c0, const uint32_t (&key)[E], int nv) {
+        uint32_t cg = 0, cq = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          cg += (e < nv && (key[e] >> S1) > bin1) ? 1u : 0u;
+          cq += (e < nv && (key[e] >> S1) == bin1) ? 1u : 0u;
+        }
+        uint32_t total;
+        const uint32_t pre = block_scan<NT>(cg | (cq << 16), s, parity, total);
+        parity ^= 1;
+        uint32_t g = gbase + (pre & 0xffffu), q = cbase + (pre >> 16);
+        const int64_t col0 = lo + c0 + (int64_t)E * threadIdx.x;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e >= nv) continue;
+          const uint32_t b = key[e] >> S1;
+          if (b > bin1) {
+            if (g < (uint32_t)k) out[g] = (int32_t)(col0 + e);
+            ++g;
+          } else if (b == bin1) {
+            if (q < (uint32_t)kCandPairs) {
+              cand_keys[q] = key[e];
+              cand_cols[q] = (uint32_t)(col0 + e);
+            }
+            ++q;
+          }
+        }
+        gbase += total & 0xffffu;
+        cbase += total >> 16;
+      });
+      m = cbase;
+      __syncthreads();
+    }
+    uint32_t u_t, need_ties;
+    if (m <= (uint32_t)kCandPairs) {
+      // candidates back into registers, consecutive per thread
+      constexpr int E2 = kCandPairs / NT;
+      uint32_t key[E2], cols[E2];
+      const int first = E2 * threadIdx.x;
+      const int nv = max(0, min(E2, (int)m - first));
+#pragma unroll
+      for (int e = 0; e < E2; ++e) {
+        key[e] = (e < nv) ? cand_keys[first + e] : 0u;
+        cols[e] = (e < nv) ? cand_cols[first + e] : 0u;
+      }
+      refine_regs<NT>(s, key, nv, 0u, S1, bin1, (uint32_t)k - above1, parity, u_t, need_ties);
+      uint32_t gr = 0, tr = 0;
+      emit_regs<NT, true>(s, key, cols, 0, nv, 0u, u_t, need_ties, false, S1, bin1, out, above1, k,
+                          parity, gr, tr);
+      return;
+    }
+    // more than 8192 keys in the threshold bin: the remaining levels re-read the row
+    constexpr int D = digit_bits<BINS>();
+    uint32_t need = (uint32_t)k - above1, prefix = bin1;
+    for (int shift = S1; shift > 0;) {
+      const int nsh = shift > D ? shift - D : 0;
+      const uint32_t dmask = (1u << (shift - nsh)) - 1u;
+      for (int64_t c0 = 0; c0 < n; c0 += C) {
+        uint32_t key[E];
+        const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+        hist_level(s, key, nv, 0u, shift, prefix, nsh, dmask);
+      }
+      __syncthreads();
+      select_bin<NT>(s, need, parity);
+      parity ^= 1;
+      need -= s.sel[1];
+      prefix = (prefix << (shift - nsh)) | s.sel[0];
+      shift = nsh;
+    }
+    u_t = prefix;
+    need_ties = need;
     uint32_t gr = 0, tr = 0;
-    emit_regs<NT, true>(s, key, cols, 0, nv, 0u, u_t, need_ties, false, S1, bin1, out, above1, k,
-                        parity, gr, tr);
-    return;
-  }
-  // more than 8192 keys in the threshold bin: the remaining levels re-read the row
-  constexpr int D = digit_bits<BINS>();
-  uint32_t need = (uint32_t)k - above1, prefix = bin1;
-  for (int shift = S1; shift > 0;) {
-    const int nsh = shift > D ? shift - D : 0;
-    const uint32_t dmask = (1u << (shift - nsh)) - 1u;
     for (int64_t c0 = 0; c0 < n; c0 += C) {
       uint32_t key[E];
       const int nv = load_keys<E>(src + c0, n - c0, vec, key);
-      hist_level(s, key, nv, 0u, shift, prefix, nsh, dmask);
+      emit_regs<NT, false>(s, key, key, lo + c0 + (int64_t)E * threadIdx.x, nv, 0u, u_t, need_ties,
+                           true, S1, bin1, out, above1, k, parity, gr, tr);
     }
-    __syncthreads();
-    select_bin<NT>(s, need, parity);
-    parity ^= 1;
-    need -= s.sel[1];
-    prefix = (prefix << (shift - nsh)) | s.sel[0];
-    shift = nsh;
-  }
-  u_t = prefix;
-  need_ties = need;
-  uint32_t gr = 0, tr = 0;
-  for (int64_t c0 = 0; c0 < n; c0 += C) {
-    uint32_t key[E];
-    const int nv = load_keys<E>(src + c0, n - c0, vec, key);
-    emit_regs<NT, false>(s, key, key, lo + c0 + (int64_t)E * threadIdx.x, nv, 0u, u_t, need_ties,
-                         true, S1, bin1, out, above1, k, parity, gr, tr);
   }
 }
 
@@ -607,15 +801,12 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
                                                         int world, int k_in, int64_t rows,
                                                         int interleave, int k,
                                                         int32_t* __restrict__ out_idx) {
-  constexpr int kWaves = NT / kWave;
   constexpr int BINS = 2048;
   __shared__ Shared<BINS> s;
   const int64_t r = blockIdx.x;
   int32_t* out = out_idx + r * k;
   const int ncand = world * k_in;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  int parity = 0;
+  const int parity = 0;
   if (threadIdx.x == 0) s.ccount = 0;           // read only after later barriers
   clear_hist<NT>(s);                            // first read after the barriers below
 
@@ -646,94 +837,7 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
       }
     }
   }
-  // valid count and key range over the valid candidates
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if ((okmask >> e) & 1u) {
-      kmin = min(kmin, key[e]);
-      kmax = max(kmax, key[e]);
-    }
-  kmin = ~wave_umax(~kmin);
-  kmax = wave_umax(kmax);
-  if (lane == 0) {
-    s.wave_tot[1][wid] = kmin;
-    s.wave_tot[1][kMaxWaves + wid] = kmax;
-  }
-  uint32_t total_valid;
-  (void)block_scan<NT>((uint32_t)__popc(okmask), s, parity, total_valid);   // one barrier
-  parity ^= 1;
-  kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
-  kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
-  __syncthreads();                              // the next scan rewrites wave_tot[1]
-
-  if (total_valid <= (uint32_t)k) {             // every valid candidate, then -1
-    uint32_t tot;
-    uint32_t pos = block_scan<NT>((uint32_t)__popc(okmask), s, parity, tot);
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if ((okmask >> e) & 1u) out[pos++] = (int32_t)col[e];
-    for (uint32_t i = tot + threadIdx.x; i < (uint32_t)k; i += NT) out[i] = -1;
-    return;
-  }
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (!((okmask >> e) & 1u)) key[e] = kmin;   // empty: (kmin, 0xffffffff), below every valid one
-
-  uint32_t key_t, col_t;
-  bool col_known = false;
-  uint32_t u_t = 0, need_ties = (uint32_t)k;
-  const uint32_t range = kmax - kmin;
-  const int L = range ? 32 - __clz(range) : 0;
-  if (L > 0) {
-    constexpr int D = digit_bits<BINS>();
-    const int nsh = L > D ? L - D : 0;
-    hist_first(s, key, nv, kmin, nsh);
-    __syncthreads();
-    select_bin<NT>(s, (uint32_t)k, parity);
-    parity ^= 1;
-    const uint32_t need = (uint32_t)k - s.sel[1];
-    const uint32_t bin = s.sel[0];
-    if (nsh == 0) {
-      u_t = bin;
-      need_ties = need;
-    } else if (s.sel[2] <= (uint32_t)kFewMerge) {
-      select_few<NT, kFewMerge, true>(s, key, col, nv, 0u, kmin, nsh, bin, need,
-                                      (uint32_t)k - need, out, parity);
-      return;
-    } else {
-      refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
-    }
-    // the last radix level's bin holds exactly the keys equal to the threshold:
-    // when all of them are taken, no column select is needed
-    if (!col_known && s.sel[2] == need_ties) {
-      col_t = 0xfffffffeu;                      // every valid column (empty slots are 0xffffffff)
-      col_known = true;
-    }
-  }
-  key_t = kmin + u_t;
-  if (!col_known) {
-    // the need_ties lowest columns among the keys equal to key_t: largest ~column
-    uint32_t key2[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) key2[e] = (e < nv && key[e] == key_t) ? ~col[e] : 0u;
-    uint32_t u2, n2;
-    refine_regs<NT>(s, key2, nv, 0u, 32, 0u, need_ties, parity, u2, n2);
-    col_t = ~u2;
-  }
-  // ordered output of every candidate at or above (key_t, col_t)
-  uint32_t cnt = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    cnt += (e < nv && (key[e] > key_t || (key[e] == key_t && col[e] <= col_t))) ? 1u : 0u;
-  uint32_t tot;
-  uint32_t pos = block_scan<NT>(cnt, s, parity, tot);
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (e < nv && (key[e] > key_t || (key[e] == key_t && col[e] <= col_t))) {
-      if (pos < (uint32_t)k) out[pos] = (int32_t)col[e];
-      ++pos;
-    }
+  select_pairs<NT, kFewMerge>(s, key, col, okmask, nv, k, out, parity);
 }
 
 template <int NT, int E, int BINS>
@@ -742,22 +846,25 @@ hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32
   const bool long_rows = ld > (int64_t)NT * E;
   // 64 KB: candidate pairs, or first the per-wave histograms (<= 8 x 8 KB)
   const size_t dyn = long_rows ? (size_t)kCandPairs * 2 * sizeof(uint32_t) : 0;
-  if (long_rows) {
-    // once per device (setting it twice from racing threads is harmless)
-    constexpr int kMaxDevices = 64;
-    static bool attr_set[kMaxDevices] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<NT, E, BINS>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-      if (e != hipSuccess) return e;
-      if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
-    }
+  if (!long_rows) {
+    hipLaunchKernelGGL((topk_kernel<NT, E, BINS, false>), dim3((unsigned)rows), dim3(NT), 0, stream,
+                       logits, ld, ks, ke, k, out_idx);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((topk_kernel<NT, E, BINS>), dim3((unsigned)rows), dim3(NT), dyn, stream, logits,
-                     ld, ks, ke, k, out_idx);
+  // once per device (setting it twice from racing threads is harmless)
+  constexpr int kMaxDevices = 64;
+  static bool attr_set[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<NT, E, BINS, true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL((topk_kernel<NT, E, BINS, true>), dim3((unsigned)rows), dim3(NT), dyn, stream,
+                     logits, ld, ks, ke, k, out_idx);
   return hipGetLastError();
 }
 

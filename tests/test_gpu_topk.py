@@ -126,3 +126,38 @@ def test_topk_ties_across_the_kth_value(n, k, width):
     ks[1] = 7
     ke[2] = n - 5
     _check(x, ks, ke, k)
+
+
+def _trend_rows(rng, rows, n):
+    """Rows whose first chunk misrepresents the row: increasing (the estimate from
+    the first chunk keeps nearly every key, overflowing the pair buffer),
+    decreasing (it keeps fewer than k), and random (the one-read path)."""
+    base = rng.standard_normal((rows, n)).astype(np.float32)
+    ramp = np.linspace(0.0, 50.0, n, dtype=np.float32)
+    x = base.copy()
+    x[0::3] += ramp
+    x[1::3] -= ramp
+    return x
+
+
+@pytest.mark.parametrize("rows,n,k", [(6, 40000, 2048), (3, 131072, 2048), (512, 20000, 2048),
+                                      (520, 9000, 300)])
+def test_topk_long_rows_first_chunk_estimate_and_fallback(rows, n, k):
+    rng = np.random.default_rng(rows * 7 + n)
+    x = _trend_rows(rng, rows, n)
+    ks = np.zeros(rows, np.int32)
+    ke = np.full(rows, n, np.int32)
+    ke[2::5] = n - n // 9
+    ks[4::7] = n // 11
+    _check(x, ks, ke, k)
+
+
+def test_topk_long_rows_fallback_reaches_the_memory_path():
+    # increasing values that share their top bits: the estimate fails (the pair
+    # buffer overflows) and the two-pass path finds > 8192 keys in the threshold
+    # bin of the top digit
+    n, k = 60000, 2048
+    bits = np.float32(1.5).view(np.uint32) + np.sort(
+        np.random.default_rng(8).integers(0, 1 << 20, size=n)).astype(np.uint32)
+    x = bits.view(np.float32).reshape(1, n).copy()
+    _check(x, np.zeros(1, np.int32), np.full(1, n, np.int32), k)
