@@ -5,7 +5,8 @@
 // holds the min(k, n) selected columns followed by -1, in a deterministic
 // order: column order, except where the first level's threshold bin is ranked
 // directly -- then the keys above that bin come first, in column order, and
-// the bin's selected keys follow in rank order.
+// the bin's selected keys follow in rank order -- and for long rows selected
+// in one read (the order of the kept pairs, per wave region).
 //
 // Radix select on order-preserving 32-bit keys with 11-bit digits and one
 // workgroup per row (1024 threads for small batches, 512 threads when there
@@ -27,10 +28,14 @@
 //     the first level's threshold bin holds at most 64 keys (the usual case:
 //     2048 bins over the row's own range), those keys are ranked directly and
 //     written at their rank, instead of histogramming the remaining digits;
-//   * longer rows, in chunks of threads*E: a first read histograms the top
-//     digit of the keys, a second read writes the keys above the threshold bin
-//     directly and compacts the bin's (key, column) pairs into LDS (up to
-//     8192, else the remaining levels re-read the row filtered by the bin).
+//   * longer rows, in chunks of threads*E: one read when the first chunk
+//     predicts the row -- it gives a key with about 1.5 k of the row expected
+//     at or above it, one pass keeps every such key in LDS, and the top-k of
+//     the kept pairs is the row's when at least k were kept and none
+//     overflowed; otherwise two reads: the first histograms the top digit of
+//     the keys, the second writes the keys above the threshold bin directly
+//     and compacts the bin's (key, column) pairs into LDS (up to 8192, else
+//     the remaining levels re-read the row filtered by the bin).
 #include "common.hpp"
 #include "launch.hpp"
 
