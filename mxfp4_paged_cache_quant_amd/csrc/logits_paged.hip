@@ -21,7 +21,8 @@
 //  * Lane l takes 16 bytes (block l/16 of token 16*j + l%16) for each of the
 //    page's 4 token tiles j -- the page's 4096 code bytes as one contiguous
 //    sweep -- plus each token's 4 scale bytes.  The cache streams through
-//    once per call, so the loads and logit stores are non-temporal.
+//    once per call, so the loads are non-temporal; logit stores are too when
+//    the output exceeds a few MB (else they stay cached for the top-k).
 //  * Heads are the MFMA M dimension: per 16-head group one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 (E2M1 x E2M1, UE8M0 scale per 32-wide
 //    block and lane) per token tile gives the exact scaled head dots.  An
@@ -51,6 +52,7 @@ namespace mxidx {
 namespace {
 
 constexpr int kPagesPerWave = 3;
+constexpr int64_t kCachedLogitsBytes = 4 << 20;
 struct PageRegs {
   uint4 code[4];      // tile j: block g of token 16*j + n
   uint32_t scale[4];  // tile j: the 4 scale bytes of token 16*j + n
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     QS qs, const uint8_t* cache, int64_t num_pages,   // written when inserting: no restrict
     const int32_t* __restrict__ block_table, int64_t bt_row_stride,
     const int32_t* __restrict__ context_lens, int next_n, int64_t width,
-    float* __restrict__ logits, int64_t ld, int clean) {
+    float* __restrict__ logits, int64_t ld, int clean, int stream_out) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
   const int g = lane >> 4;       // 32-element block this lane supplies / head quad it receives
@@ -250,8 +252,12 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     const bool scored = col < ke;
     const bool keep = scored || (clean && col < width);
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(logits + r * ld + tok0, kPage * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(scored ? v : neg_inf()), rs,
-                                          keep ? 4u * lane : kDropOffset, 0, kNonTemporal);
+    const uint32_t bits = __float_as_uint(scored ? v : neg_inf());
+    const uint32_t off = keep ? 4u * lane : kDropOffset;
+    if (stream_out)   // wave-uniform
+      __builtin_amdgcn_raw_buffer_store_b32(bits, rs, off, 0, kNonTemporal);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(bits, rs, off, 0, 0);
   };
 
   if (lp0 * kPage >= L) {        // every page lies past the context: -inf fill only
@@ -385,10 +391,15 @@ hipError_t launch_nh(QS qs, const uint8_t* cache, int64_t num_pages, const int32
                      int64_t bt_stride, const int32_t* ctx, int B, int next_n, int64_t width,
                      float* logits, int64_t ld, int clean, hipStream_t stream) {
   const int64_t pages = (width + kPage - 1) / kPage;
+  // Logits of a few MB (a decode batch) are stored through the caches, where
+  // the top-k that reads them next finds them (decode step 11.10 -> 10.84 us);
+  // larger outputs stream past them (cached, the 33.5 MB of the 64 x 131072
+  // batch slowed the logits from 64.7 to 69.3 us).
+  const int stream_out = (int64_t)B * next_n * width * 4 > kCachedLogitsBytes ? 1 : 0;
   const dim3 grid((unsigned)((pages + kPagesPerWave - 1) / kPagesPerWave), (unsigned)B);
 #define MXIDX_PAGED_ROWS(nn)                                                                   \
   hipLaunchKernelGGL((logits_paged_kernel<NH, nn, QS>), grid, dim3(kWave), 0, stream, qs, cache, \
-                     num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean)
+                     num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean, stream_out)
   // rows held in registers while rows * NH <= 8 (the query operands of 8 head groups)
   bool held = true;
   if (next_n == 1) {
