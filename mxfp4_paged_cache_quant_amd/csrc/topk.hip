@@ -36,6 +36,8 @@
 //     the keys, the second writes the keys above the threshold bin directly
 //     and compacts the bin's (key, column) pairs into LDS (up to 8192, else
 //     the remaining levels re-read the row filtered by the bin).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -162,6 +164,17 @@ __device__ __forceinline__ void clear_hist(Shared<BINS>& s) {
   for (int i = threadIdx.x; i < BINS; i += NT) s.hist[i] = 0;
 }
 
+// Per-slot loops run as f(std::true_type) on a wave whose E*64 slots all hold
+// keys of the row -- the per-slot validity tests then fold away (on a 8192-key
+// row they cost about a tenth of the kernel) -- and as f(std::false_type) on
+// the wave that holds the row's end or lies past it.  `wave_full` is uniform
+// over the wave, so each wave runs one of the two bodies.
+template <typename F>
+__device__ __forceinline__ void per_fill(bool wave_full, F&& f) {
+  if (wave_full) f(std::true_type{});
+  else f(std::false_type{});
+}
+
 // Keys E*t + e (e < E) of the segment src[0, n) into thread t's registers;
 // returns how many are valid.  All loads are issued before any is used.
 template <int E>
@@ -243,22 +256,27 @@ __device__ __forceinline__ void for_chunks(const float* __restrict__ src, int64_
 template <int E, int BINS>
 __device__ __forceinline__ void hist_level(Shared<BINS>& s, const uint32_t (&key)[E], int nv,
                                            uint32_t kmin, int shift, uint32_t prefix, int nsh,
-                                           uint32_t dmask) {
+                                           uint32_t dmask, bool wfull = false) {
+  per_fill(wfull, [&](auto full) __attribute__((always_inline)) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t u = key[e] - kmin;
-    if (e < nv && (shift >= 32 || (u >> shift) == prefix)) atomicAdd(&s.hist[(u >> nsh) & dmask], 1u);
-  }
+    for (int e = 0; e < E; ++e) {
+      const uint32_t u = key[e] - kmin;
+      if ((full.value || e < nv) && (shift >= 32 || (u >> shift) == prefix))
+        atomicAdd(&s.hist[(u >> nsh) & dmask], 1u);
+    }
+  });
 }
 
 // First level over the key range: u = key - kmin < 2^(nsh + digit bits), so
 // every valid key counts and its digit is u >> nsh.
 template <int E, int BINS>
 __device__ __forceinline__ void hist_first(Shared<BINS>& s, const uint32_t (&key)[E], int nv,
-                                           uint32_t kmin, int nsh) {
+                                           uint32_t kmin, int nsh, bool wfull = false) {
+  per_fill(wfull, [&](auto full) __attribute__((always_inline)) {
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (e < nv) atomicAdd(&s.hist[(key[e] - kmin) >> nsh], 1u);
+    for (int e = 0; e < E; ++e)
+      if (full.value || e < nv) atomicAdd(&s.hist[(key[e] - kmin) >> nsh], 1u);
+  });
 }
 
 template <int BINS>
@@ -273,13 +291,14 @@ constexpr int digit_bits() {
 // equal to it to take.
 template <int NT, int BINS, int E>
 __device__ __forceinline__ void refine_regs(Shared<BINS>& s, const uint32_t (&key)[E], int nv,
-                                            uint32_t kmin, int shift, uint32_t prefix, uint32_t need, int& parity, uint32_t& u_t,
-                            uint32_t& need_ties) {
+                                            uint32_t kmin, int shift, uint32_t prefix,
+                                            uint32_t need, int& parity, uint32_t& u_t,
+                                            uint32_t& need_ties, bool wfull = false) {
   constexpr int D = digit_bits<BINS>();
   while (shift > 0) {
     const int nsh = shift > D ? shift - D : 0;
     const uint32_t dmask = (1u << (shift - nsh)) - 1u;
-    hist_level(s, key, nv, kmin, shift, prefix, nsh, dmask);
+    hist_level(s, key, nv, kmin, shift, prefix, nsh, dmask, wfull);
     __syncthreads();
     select_bin<NT>(s, need, parity);
     parity ^= 1;
@@ -305,27 +324,36 @@ __device__ __forceinline__ void select_few(Shared<BINS>& s, const uint32_t (&key
                                            const uint32_t (&cols)[E], int nv, uint32_t col0,
                                            uint32_t kmin, int shift, uint32_t prefix,
                                            uint32_t need, uint32_t above,
-                                           int32_t* __restrict__ out, int parity) {
+                                           int32_t* __restrict__ out, int parity,
+                                           bool wfull = false) {
   static_assert(FEW <= kFewCand && NT % FEW == 0, "ranked keys: LDS capacity, threads");
   constexpr int kPerCand = NT / FEW;             // threads per candidate
   constexpr int kJ = FEW / kPerCand;             // comparisons per thread
   uint32_t ca = 0;
+  per_fill(wfull, [&](auto full) __attribute__((always_inline)) {
+    uint32_t a = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t d = (key[e] - kmin) >> shift;
-    if (e < nv && d > prefix) ++ca;
-    if (e < nv && d == prefix) {
-      const uint32_t slot = atomicAdd(&s.ccount, 1u);
-      s.ckey[slot] = key[e];
-      s.ccol[slot] = kCols ? cols[e] : col0 + (uint32_t)e;
+    for (int e = 0; e < E; ++e) {
+      const uint32_t d = (key[e] - kmin) >> shift;
+      const bool ok = full.value || e < nv;
+      if (ok && d > prefix) ++a;
+      if (ok && d == prefix) {
+        const uint32_t slot = atomicAdd(&s.ccount, 1u);
+        s.ckey[slot] = key[e];
+        s.ccol[slot] = kCols ? cols[e] : col0 + (uint32_t)e;
+      }
     }
-  }
+    ca = a;
+  });
   uint32_t total;
-  uint32_t pos = block_scan<NT>(ca, s, parity, total);
+  const uint32_t pos = block_scan<NT>(ca, s, parity, total);
+  per_fill(wfull, [&](auto full) __attribute__((always_inline)) {
+    uint32_t p = pos;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if (e < nv && ((key[e] - kmin) >> shift) > prefix)
-      out[pos++] = (int32_t)(kCols ? cols[e] : col0 + (uint32_t)e);
+    for (int e = 0; e < E; ++e)
+      if ((full.value || e < nv) && ((key[e] - kmin) >> shift) > prefix)
+        out[p++] = (int32_t)(kCols ? cols[e] : col0 + (uint32_t)e);
+  });
   const uint32_t cnt = s.ccount;
   const uint32_t i = threadIdx.x / kPerCand;
   const uint32_t j0 = (threadIdx.x % kPerCand) * kJ;
@@ -358,34 +386,45 @@ __device__ __forceinline__ void emit_regs(Shared<BINS>& s, const uint32_t (&key)
                                           uint32_t kmin, uint32_t u_t, uint32_t need_ties,
                                           bool filt, int fshift, uint32_t fbin,
                                           int32_t* __restrict__ out, uint32_t base, int k,
-                                          int& parity, uint32_t& gt_run, uint32_t& tie_run) {
+                                          int& parity, uint32_t& gt_run, uint32_t& tie_run,
+                                          bool wfull = false) {
   uint32_t cg = 0, ct = 0;
+  per_fill(wfull, [&](auto full) __attribute__((always_inline)) {
+    uint32_t a = 0, b = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t u = key[e] - kmin;
-    const bool ok = e < nv && (!filt || (key[e] >> fshift) == fbin);
-    cg += (ok && u > u_t) ? 1u : 0u;
-    ct += (ok && u == u_t) ? 1u : 0u;
-  }
+    for (int e = 0; e < E; ++e) {
+      const uint32_t u = key[e] - kmin;
+      const bool ok = (full.value || e < nv) && (!filt || (key[e] >> fshift) == fbin);
+      a += (ok && u > u_t) ? 1u : 0u;
+      b += (ok && u == u_t) ? 1u : 0u;
+    }
+    cg = a;
+    ct = b;
+  });
   uint32_t total;
   const uint32_t pre = block_scan<NT>(cg | (ct << 16), s, parity, total);
   parity ^= 1;
-  uint32_t g = gt_run + (pre & 0xffffu);
-  uint32_t t = tie_run + (pre >> 16);
+  const uint32_t g = gt_run + (pre & 0xffffu);
+  const uint32_t t = tie_run + (pre >> 16);
+  // (the lambdas below update copies: a captured counter incremented on two
+  // paths would be addressed through a pointer select and live in scratch)
+  per_fill(wfull, [&](auto full) __attribute__((always_inline)) {
+    uint32_t gl = g, tl = t;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t u = key[e] - kmin;
-    const bool ok = e < nv && (!filt || (key[e] >> fshift) == fbin);
-    const int64_t col = kCols ? (int64_t)cols[e] : col0 + e;
-    if (ok && u > u_t) {
-      const uint32_t pos = base + g + min(t, need_ties);
-      if (pos < (uint32_t)k) out[pos] = (int32_t)col;
-      ++g;
-    } else if (ok && u == u_t) {
-      if (t < need_ties && base + g + t < (uint32_t)k) out[base + g + t] = (int32_t)col;
-      ++t;
+    for (int e = 0; e < E; ++e) {
+      const uint32_t u = key[e] - kmin;
+      const bool ok = (full.value || e < nv) && (!filt || (key[e] >> fshift) == fbin);
+      const int64_t col = kCols ? (int64_t)cols[e] : col0 + e;
+      if (ok && u > u_t) {
+        const uint32_t pos = base + gl + min(tl, need_ties);
+        if (pos < (uint32_t)k) out[pos] = (int32_t)col;
+        ++gl;
+      } else if (ok && u == u_t) {
+        if (tl < need_ties && base + gl + tl < (uint32_t)k) out[base + gl + tl] = (int32_t)col;
+        ++tl;
+      }
     }
-  }
+  });
   gt_run += total & 0xffffu;
   tie_run += total >> 16;
 }
@@ -524,54 +563,78 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
 
   if (n <= C) {
     // ---- the whole row in registers: one read ----
-    uint32_t key[E];
-    const int nv = load_keys<E>(src, n, vec, key);
-    clear_hist<NT>(s);                            // overlaps the loads
-    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    // A row of exactly C keys runs with every wave full at compile time.
+    auto row_regs = [&](auto all_full) __attribute__((always_inline)) {
+      uint32_t key[E];
+      const int wfirst = __builtin_amdgcn_readfirstlane(threadIdx.x) & ~(kWave - 1);
+      // every slot of the wave valid (a constant on a row of exactly C keys)
+      const bool wfull = all_full.value || n >= (int64_t)(wfirst + kWave) * E;
+      int nv = E;
+      if (wfull && vec) load_full<E>(src, 0, key);
+      else nv = load_keys<E>(src, n, vec, key);
+      clear_hist<NT>(s);                            // overlaps the loads
+      uint32_t kmin = 0xffffffffu, kmax = 0u;
+      per_fill(wfull, [&](auto full) __attribute__((always_inline)) {
+        uint32_t lo_k = 0xffffffffu, hi_k = 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (e < nv) {
-        kmin = min(kmin, key[e]);
-        kmax = max(kmax, key[e]);
+        for (int e = 0; e < E; ++e)
+          if (full.value || e < nv) {
+            lo_k = min(lo_k, key[e]);
+            hi_k = max(hi_k, key[e]);
+          }
+        kmin = lo_k;
+        kmax = hi_k;
+      });
+      kmin = ~wave_umax(~kmin);
+      kmax = wave_umax(kmax);
+      if (lane == 0) {
+        s.wave_tot[1][wid] = kmin;
+        s.wave_tot[1][kMaxWaves + wid] = kmax;
       }
-    kmin = ~wave_umax(~kmin);
-    kmax = wave_umax(kmax);
-    if (lane == 0) {
-      s.wave_tot[1][wid] = kmin;
-      s.wave_tot[1][kMaxWaves + wid] = kmax;
-    }
-    __syncthreads();
-    kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
-    kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
-    // wave_tot[1] is next written by the second scan, after at least one more barrier
-    const uint32_t range = kmax - kmin;
-    const int L = range ? 32 - __clz(range) : 0;     // bit length of the key range
-    uint32_t u_t = 0, need_ties = (uint32_t)k;        // all keys equal: the lowest columns
-    if (L > 0) {
-      // first digit over the whole range, then either a direct ranking of a
-      // small threshold bin or the remaining digits
-      constexpr int D = digit_bits<BINS>();
-      const int nsh = L > D ? L - D : 0;
-      hist_first(s, key, nv, kmin, nsh);
       __syncthreads();
-      select_bin<NT>(s, (uint32_t)k, parity);
-      parity ^= 1;
-      const uint32_t need = (uint32_t)k - s.sel[1];
-      const uint32_t bin = s.sel[0];
-      if (nsh == 0) {
-        u_t = bin;
-        need_ties = need;
-      } else if (s.sel[2] <= (uint32_t)kFewTopk) {
-        select_few<NT, kFewTopk, false>(s, key, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x),
-                                        kmin, nsh, bin, need, (uint32_t)k - need, out, parity);
+      kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
+      kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
+      // wave_tot[1] is next written by the second scan, after at least one more barrier
+      const uint32_t range = kmax - kmin;
+      const int L = range ? 32 - __clz(range) : 0;     // bit length of the key range
+      uint32_t u_t = 0, need_ties = (uint32_t)k;        // all keys equal: the lowest columns
+      if (L > 0) {
+        // first digit over the whole range, then either a direct ranking of a
+        // small threshold bin or the remaining digits
+        constexpr int D = digit_bits<BINS>();
+        const int nsh = L > D ? L - D : 0;
+        hist_first(s, key, nv, kmin, nsh, wfull);
+        __syncthreads();
+        select_bin<NT>(s, (uint32_t)k, parity);
+        parity ^= 1;
+        const uint32_t need = (uint32_t)k - s.sel[1];
+        const uint32_t bin = s.sel[0];
+        if (nsh == 0) {
+          u_t = bin;
+          need_ties = need;
+        } else if (s.sel[2] <= (uint32_t)kFewTopk) {
+          select_few<NT, kFewTopk, false>(s, key, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x),
+                                          kmin, nsh, bin, need, (uint32_t)k - need, out, parity,
+                                          wfull);
+          return;
+        } else {
+          refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties, wfull);
+        }
+      }
+      uint32_t gr = 0, tr = 0;
+      emit_regs<NT, false>(s, key, key, lo + (int64_t)E * threadIdx.x, nv, kmin, u_t, need_ties,
+                           false, 0, 0u, out, 0u, k, parity, gr, tr, wfull);
+    };
+    // (only in the 1024-thread kernels, launched for few rows: the third copy
+    // of the per-slot loops costs registers, which the many-row kernels spend
+    // on occupancy)
+    if constexpr (NT == kMaxThreads) {
+      if (n == C) {
+        row_regs(std::true_type{});
         return;
-      } else {
-        refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties);
       }
     }
-    uint32_t gr = 0, tr = 0;
-    emit_regs<NT, false>(s, key, key, lo + (int64_t)E * threadIdx.x, nv, kmin, u_t, need_ties,
-                         false, 0, 0u, out, 0u, k, parity, gr, tr);
+    row_regs(std::false_type{});
     return;
   }
   if constexpr (kLong) {

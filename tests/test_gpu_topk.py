@@ -25,7 +25,8 @@ def _check(x, ks, ke, k, use_ks=True):
 
 
 @pytest.mark.parametrize("n,k", [(1, 1), (63, 64), (64, 64), (65, 64), (3000, 2048), (2049, 2048),
-                                 (8192, 2048), (16384, 2048), (16385, 2048), (40000, 2048),
+                                 (4096, 64), (4096, 2048), (8192, 2048), (16384, 2048),
+                                 (16385, 2048), (40000, 2048),
                                  (131072, 2048), (5000, 1), (20000, 7)])
 def test_topk_random_rows(n, k):
     rng = np.random.default_rng(n * 31 + k)
@@ -42,6 +43,28 @@ def test_topk_random_rows(n, k):
     ks[5], ke[5] = n // 3, n // 3                               # empty range
     _check(x, ks, ke, k)
     _check(x, ks, ke, k, use_ks=False)
+
+
+@pytest.mark.parametrize("n", [4096, 8192, 16384])
+def test_topk_full_rows_unaligned_start(n):
+    # Rows that fill every slot of the workgroup (4096, 8192 and 16384 keys)
+    # but start 4 bytes past a 16-byte boundary, so the keys arrive by scalar
+    # loads; one row with many ties, one with +0/-0, one all equal.
+    rng = np.random.default_rng(n + 3)
+    R, k = 4, 2048
+    buf = rng.standard_normal(R * n + 1).astype(np.float32)
+    x = buf[1:].reshape(R, n)
+    x[0] = np.round(x[0] * 8) / 8
+    x[1, ::5] = 0.0
+    x[1, 2::5] = -0.0
+    x[2] = 0.25
+    t = dev(buf)[1:].view(R, n)
+    assert t.data_ptr() % 16 == 4
+    ke = np.full(R, n, np.int32)
+    out = host(mx.topk(t, None, dev(ke), k))
+    ref = otk.top_k_per_row(x, np.zeros(R, np.int32), ke, k)
+    for r in range(R):
+        assert sorted(out[r].tolist()) == sorted(ref[r].tolist()), r
 
 
 def test_topk_all_equal_and_heavy_ties_take_lowest_columns():
