@@ -433,8 +433,8 @@ __device__ __forceinline__ void emit_regs(Shared<BINS>& s, const uint32_t (&key)
 // which those with okmask bit e set are valid (the others take part as
 // (kmin, 0xffffffff), below every valid pair).  Ranking: key descending, then
 // column ascending.  Writes the min(k, valid) selected columns to out[0, k),
-// then -1; the order is deterministic.  Starts with the histogram cleared and
-// ccount zero.
+// then -1; the order is deterministic.  Starts with the histogram cleared,
+// ccount zero, and a barrier after the caller's last scan.
 template <int NT, int FEW, int BINS, int E>
 __device__ __forceinline__ void select_pairs(Shared<BINS>& s, uint32_t (&key)[E],
                                              const uint32_t (&col)[E], uint32_t okmask, int nv,
@@ -452,16 +452,19 @@ __device__ __forceinline__ void select_pairs(Shared<BINS>& s, uint32_t (&key)[E]
     }
   kmin = ~wave_umax(~kmin);
   kmax = wave_umax(kmax);
+  // the wave ranges go to the buffer the scan below does not write (the
+  // caller's last scan, if any, used it and has passed a barrier since)
+  uint32_t* wr = s.wave_tot[parity ^ 1];
   if (lane == 0) {
-    s.wave_tot[1][wid] = kmin;
-    s.wave_tot[1][kMaxWaves + wid] = kmax;
+    wr[wid] = kmin;
+    wr[kMaxWaves + wid] = kmax;
   }
   uint32_t total_valid;
   (void)block_scan<NT>((uint32_t)__popc(okmask), s, parity, total_valid);   // one barrier
   parity ^= 1;
-  kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
-  kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
-  __syncthreads();                              // the next scan rewrites wave_tot[1]
+  kmin = ~wave_umax(lane < kWaves ? ~wr[lane & 15] : 0u);
+  kmax = wave_umax(lane < kWaves ? wr[kMaxWaves + (lane & 15)] : 0u);
+  __syncthreads();                              // the next scan rewrites that buffer
 
   if (total_valid <= (uint32_t)k) {             // every valid candidate, then -1
     uint32_t tot;
