@@ -654,10 +654,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       constexpr int E2 = kRegion / kWave;           // kept pairs per thread afterwards
       uint32_t* ck = dyn;
       uint32_t* cc = dyn + kCandPairs;
-      uint32_t t_est;
-      {
-        uint32_t key[E];
-        (void)load_keys<E>(src, n, vec, key);       // n > C: a full chunk
+      // t_est from a full first chunk: about 1.5 k of the row's keys are
+      // expected at or above it
+      auto estimate = [&](const uint32_t (&key)[E]) __attribute__((always_inline)) -> uint32_t {
         clear_hist<NT>(s);
         uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -683,12 +682,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
         const int64_t want = ((int64_t)3 * k * C) / (2 * n) + 32;   // of the chunk's C keys
         select_bin<NT>(s, (uint32_t)min(want, C), parity);
         parity ^= 1;
-        t_est = kmin + (s.sel[0] << nsh);           // lower edge of that key's bin
-      }
+        return kmin + (s.sel[0] << nsh);            // lower edge of that key's bin
+      };
+      uint32_t t_est;
       uint32_t kept = 0;                            // this wave's pairs (wave-uniform)
       uint32_t* wk = ck + wid * kRegion;
       uint32_t* wc = cc + wid * kRegion;
-      for_chunks<NT, E>(src, n, vec, [&](int64_t c0, const uint32_t (&key)[E], int nv) {
+      // one pass keeps every key >= t_est, each wave appending to its region
+      auto keep = [&](int64_t c0, const uint32_t (&key)[E], int nv) __attribute__((always_inline)) {
         const uint32_t col0 = (uint32_t)(lo + c0 + (int64_t)E * threadIdx.x);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -705,7 +706,40 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
             kept += (uint32_t)__popcll(m);
           }
         }
-      });
+      };
+      if (vec) {
+        // Aligned row: the estimate's chunk 0 stays in registers for the pass
+        // (it is not read twice) and chunk 1 loads during the estimate; then
+        // two buffers, each refilled right after use (refills past the last
+        // full chunk re-read it, so waits stay exact).  A third buffer was
+        // measured: it slowed the estimate's own chunk more than it sped the
+        // pass, whose ballot bookkeeping, not memory, sets its pace.
+        const int64_t nfull = n / C;                // >= 1
+        uint32_t ka[E], kb[E];
+        load_full<E>(src, 0, ka);
+        load_full<E>(src, min((int64_t)1, nfull - 1) * C, kb);
+        t_est = estimate(ka);
+        int64_t i = 0;
+        for (; i + 1 < nfull; i += 2) {
+          keep(i * C, ka, E);
+          load_full<E>(src, min(i + 2, nfull - 1) * C, ka);
+          keep((i + 1) * C, kb, E);
+          load_full<E>(src, min(i + 3, nfull - 1) * C, kb);
+        }
+        if (i < nfull) keep(i * C, ka, E);
+        for (int64_t c0 = nfull * C; c0 < n; c0 += C) {
+          uint32_t key[E];
+          const int nv = load_keys<E>(src + c0, n - c0, vec, key);
+          keep(c0, key, nv);
+        }
+      } else {
+        {
+          uint32_t key[E];
+          (void)load_keys<E>(src, n, vec, key);     // n > C: a full chunk
+          t_est = estimate(key);
+        }
+        for_chunks<NT, E>(src, n, vec, keep);
+      }
       if (lane == 0) s.wave_tot[0][wid] = kept;
       __syncthreads();
       uint32_t total = 0, fullest = 0;
@@ -715,17 +749,22 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
         fullest = max(fullest, s.wave_tot[0][w]);
       }
       if (total >= (uint32_t)k && fullest <= (uint32_t)kRegion) {
+        // a wave's kept pairs are a prefix of its region, so each lane's valid
+        // slots are a prefix of its E2: passing their count (not E2) keeps the
+        // empty slots out of every histogram (as the range minimum they would
+        // all hit one bin, and those LDS atomics serialize)
         uint32_t key[E2], col[E2];
         uint32_t okmask = 0;
+        const int nv2 = (int)min((uint32_t)E2, kept - min(kept, (uint32_t)(lane * E2)));
 #pragma unroll
         for (int e = 0; e < E2; ++e) {
           const uint32_t i = (uint32_t)(lane * E2 + e);
-          key[e] = wk[i];
-          col[e] = wc[i];
-          okmask |= (i < kept ? 1u : 0u) << e;
+          key[e] = e < nv2 ? wk[i] : 0u;
+          col[e] = e < nv2 ? wc[i] : 0xffffffffu;
+          okmask |= (e < nv2 ? 1u : 0u) << e;
         }
         __syncthreads();                            // every count read before the next scans
-        select_pairs<NT, kFewMerge>(s, key, col, okmask, E2, k, out, parity);
+        select_pairs<NT, kFewMerge>(s, key, col, okmask, nv2, k, out, parity);
         return;
       }
       __syncthreads();                              // counts read before the buffers are reused
