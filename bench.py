@@ -151,19 +151,29 @@ def capture(fn_list):
     return g
 
 
-def time_graph(g, reps):
-    """Average ms per replay, HIP events on the current stream."""
+def time_graph(g, reps, batches=5, warm_ms=25.0):
+    """ms per replay: the median over `batches` batches of `reps` replays, timed with
+    HIP events on the current stream, after untimed replays for at least warm_ms
+    (the clocks settle after a light section; a single warm-up replay left the
+    first batches of a heavy kernel up to 20% slow)."""
+    import statistics
     import torch
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    g.replay()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(reps):
+    t0, n = time.perf_counter(), 0
+    while n < 2 or (time.perf_counter() - t0) * 1e3 < warm_ms:
         g.replay()
-    stop.record()
-    stop.synchronize()
-    return start.elapsed_time(stop) / reps
+        torch.cuda.synchronize()
+        n += 1
+    times = []
+    for _ in range(batches):
+        start.record()
+        for _ in range(reps):
+            g.replay()
+        stop.record()
+        stop.synchronize()
+        times.append(start.elapsed_time(stop) / reps)
+    return statistics.median(times)
 
 
 def bench_decode(args, case, sets, order):
