@@ -291,7 +291,11 @@ def bench_long_decode():
     # -inf fill of the columns past it (clean=True) is timed beside it
     lg = lambda: mx.logits_paged(qv, qs, w, cache, bt, ctx, 1, W, logits=logits, clean=False)  # noqa: E731
     lg_clean = lambda: mx.logits_paged(qv, qs, w, cache, bt, ctx, 1, W, logits=logits, clean=True)  # noqa: E731
-    tk = lambda: mx.topk(logits, None, ke, case["topk"], out=idx)  # noqa: E731
+    # the step's top-k splits each long row over workgroups (workspace from
+    # topk_workspace, allocated once); the one-workgroup-per-row call is timed beside it
+    ws = mx.topk_workspace(B, W)
+    tk = lambda: mx.topk_ws(logits, None, ke, case["topk"], ws, out=idx)  # noqa: E731
+    tk_row = lambda: mx.topk(logits, None, ke, case["topk"], out=idx)  # noqa: E731
     # profiler (--eager) runs launch only the calls of the step, so that
     # per-kernel counters are not averaged over the two clean variants
     extra = () if EAGER else (lg_clean,)
@@ -302,6 +306,7 @@ def bench_long_decode():
     t_lgc = None if EAGER else time_fn(lg_clean, 10, 4)
     t_lg = time_fn(lg, 10, 4)
     t_tk = time_fn(tk, 10, 4)
+    t_tk_row = None if EAGER else time_fn(tk_row, 10, 4)
     # multi-token decode (next_n = 2): the same cache, two query rows per sequence
     # (seeded N(0,1) bf16 q drawn on the device); rows see L-1 and L tokens
     gen = torch.Generator(device="cuda")
@@ -338,6 +343,9 @@ def bench_long_decode():
         "mtp2_scored_pairs_per_s": None if t_lg2 is None else round((2 * N - B) / (t_lg2 * 1e-6), 1),
         "dcp4_merge_us": None if t_mg is None else round(t_mg, 1),
         "topk_us": round(t_tk, 1), "topk_gbs": round(b_tk / t_tk / 1e3, 1),
+        "topk_one_workgroup_per_row_us": None if t_tk_row is None else round(t_tk_row, 1),
+        "decode_step_frac_hbm": round((N * 76 + B * H * 72 + B * case["topk"] * 4)
+                                      / ((t_lg + t_tk) * 1e3) / HBM_PEAK_GBS, 4),
         "decode_step_us": round(t_lg + t_tk, 1),
         "scored_tokens_per_s": round(N / ((t_lg + t_tk) * 1e-6), 1),
     }
@@ -453,6 +461,7 @@ KERNEL_SOURCES = {          # kernel-name prefix -> the source it is compiled fr
     "logits_paged_kernel": "logits_paged.hip",
     "logits_prefill_kernel": "logits_prefill.hip",
     "topk_kernel": "topk.hip",
+    "topk_part": "topk.hip",
     "mxfp4_rows_kernel": "insert.hip",
     "insert_quantize_kernel": "insert.hip",
     "gather_kernel": "gather.hip",

@@ -10,6 +10,8 @@
  *   idx_logits_prefill  logit[t,s] = sum_h w[t,h] * max(0, q[t,h] . k[s]), dense K
  *   idx_logits_paged    the same score, K read through a block table (decode)
  *   idx_topk            per-row top-k column indices over [ks, ke)
+ *   idx_topk_ws         the same with a workspace: few long rows split over
+ *                       workgroups
  *
  * Sources: P1 = "[Kernel] MXFP4 indexer cache for GLM-5.2 / DSA (glm_moe_dsa)"
  * (vLLM pull request 48558); P2 = "Enable SM86 MXFP4 sparse-indexer cache"
@@ -238,6 +240,32 @@ int idx_logits_paged_insert(const void* q, const void* k_new, int dtype, const f
 int idx_topk(const float* logits, int64_t rows, int64_t logits_row_stride,
              const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
              hipStream_t stream);
+
+/* idx_topk_workspace_bytes -- size of the device workspace idx_topk_ws needs
+ * for `rows` rows of a logits matrix with row stride `logits_row_stride`.
+ * Non-zero only when idx_topk_ws splits rows over several workgroups: fewer
+ * than 512 rows that may hold more than 8,192 columns, with a row stride of at
+ * most 64 x 8,192 columns.  For the 64 x 131,072 long-context batch it is
+ * about 33.6 MB (64 rows x 16 parts x 4,096 (key, column) pairs, plus a
+ * header per part).  0 for invalid sizes. */
+size_t idx_topk_workspace_bytes(int64_t rows, int64_t logits_row_stride);
+
+/* idx_topk_ws -- idx_topk with a device workspace: the same exact sets (same
+ * arguments, ranking and -1 padding).  When few rows are long it splits each
+ * into parts of 8,192 columns, one workgroup per part, each keeping the keys
+ * at or above an estimate of the row's top-k threshold in the workspace; a
+ * second launch on the same stream selects each row's top-k from its kept
+ * keys, or over the whole row when the kept keys cannot be shown to hold it.
+ * The order of the returned columns is deterministic but differs from
+ * idx_topk's.
+ *   workspace: device memory of at least idx_topk_workspace_bytes(rows,
+ *   logits_row_stride) bytes, 256-byte aligned, owned by the caller; its
+ *   contents need no initialization and are scratch after the call.  Calls
+ *   that share a workspace must not run concurrently.  May be NULL when that
+ *   size is 0.  IDX_ERR_ARG if it is missing, misaligned or too small. */
+int idx_topk_ws(const float* logits, int64_t rows, int64_t logits_row_stride,
+                const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* idx_topk_merge -- merge per-rank top-k lists into a sequence's top-k: the
  * exchange step of decode with the context split over `world` ranks (P3

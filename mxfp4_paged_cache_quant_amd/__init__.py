@@ -15,7 +15,8 @@ import os
 __all__ = [
     "MxidxError", "lib", "lib_path", "version", "init",
     "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged",
-    "logits_paged_insert", "topk", "topk_merge",
+    "logits_paged_insert", "topk", "topk_workspace_bytes", "topk_workspace", "topk_ws",
+    "topk_merge",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
 ]
 
@@ -56,6 +57,9 @@ EXPORTS = {
                                        _c_void_p, _i64, _c_void_p, _int, _int, _int, _i64,
                                        _c_void_p, _i64, _int, _c_void_p]),
     "idx_topk": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p]),
+    "idx_topk_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
+    "idx_topk_ws": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p,
+                           ctypes.c_size_t, _c_void_p]),
     "idx_topk_merge": (_int, [_c_void_p, _c_void_p, _int, _i64, _int, _int, _int, _c_void_p,
                               _c_void_p]),
 }
@@ -393,6 +397,47 @@ def topk(logits, ks, ke, k, out=None, stream=None):
         raise MxidxError("out must be a contiguous int32 [rows, k]")
     _check(lib().idx_topk(_ptr(logits), rows, logits.stride(0), _ptr(ks), _ptr(ke), k, _ptr(out),
                           _stream(stream)), "idx_topk")
+    return out
+
+
+def topk_workspace_bytes(rows, row_stride):
+    """Bytes of device workspace topk_ws needs for `rows` rows of stride `row_stride`
+    (0 when it does not split rows)."""
+    return int(lib().idx_topk_workspace_bytes(rows, row_stride))
+
+
+def topk_workspace(rows, row_stride, device=None):
+    """A uint8 workspace for topk_ws (uninitialized; reusable across calls in stream order)."""
+    torch = _torch()
+    n = topk_workspace_bytes(rows, row_stride)
+    return torch.empty(max(n, 1), dtype=torch.uint8,
+                       device=device if device is not None else torch.cuda.current_device())
+
+
+def topk_ws(logits, ks, ke, k, workspace, out=None, stream=None):
+    """topk with a device workspace (from topk_workspace): the same sets; few long rows
+    are split over workgroups."""
+    torch = _torch()
+    _dev(logits, "logits", torch.float32)
+    _dev(ke, "ke", torch.int32)
+    _dev(workspace, "workspace", torch.uint8)
+    if ks is not None:
+        _dev(ks, "ks", torch.int32)
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise MxidxError("logits must be 2-D with contiguous rows")
+    rows = logits.shape[0]
+    if ke.numel() != rows or not ke.is_contiguous() or \
+            (ks is not None and (ks.numel() != rows or not ks.is_contiguous())):
+        raise MxidxError("ks / ke must hold one entry per row")
+    if not workspace.is_contiguous():
+        raise MxidxError("workspace must be contiguous")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    _dev(out, "out", torch.int32)
+    if not out.is_contiguous() or tuple(out.shape) != (rows, k):
+        raise MxidxError("out must be a contiguous int32 [rows, k]")
+    _check(lib().idx_topk_ws(_ptr(logits), rows, logits.stride(0), _ptr(ks), _ptr(ke), k, _ptr(out),
+                             _ptr(workspace), workspace.numel(), _stream(stream)), "idx_topk_ws")
     return out
 
 

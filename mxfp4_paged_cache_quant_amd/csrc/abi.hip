@@ -57,7 +57,7 @@ int check_rows_input(const void* x, int dtype, int64_t rows, int64_t row_stride)
 
 extern "C" {
 
-int idx_version(void) { return 103; }
+int idx_version(void) { return 104; }
 
 const char* idx_strerror(int status) {
   switch (status) {
@@ -240,6 +240,28 @@ int idx_topk(const float* logits, int64_t rows, int64_t logits_row_stride, const
   int st = gate_current();
   if (st != IDX_OK) return st;
   return launched(mxidx::launch_topk(logits, rows, logits_row_stride, ks, ke, k, out_idx, stream));
+}
+
+size_t idx_topk_workspace_bytes(int64_t rows, int64_t logits_row_stride) {
+  if (rows < 0 || logits_row_stride < 0 || rows > 0x7fffffffLL) return 0;
+  return (size_t)mxidx::topk_workspace_bytes(rows, logits_row_stride);
+}
+
+int idx_topk_ws(const float* logits, int64_t rows, int64_t logits_row_stride, const int32_t* ks,
+                const int32_t* ke, int k, int32_t* out_idx, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  if (rows < 0 || k < 1 || k > IDX_TOPK_MAX || logits_row_stride < 0 ||
+      rows > 0x7fffffffLL)
+    return IDX_ERR_ARG;
+  if (rows == 0) return IDX_OK;
+  if (!logits || !aligned(logits, 4) || !ke || !out_idx) return IDX_ERR_ARG;
+  const size_t need = idx_topk_workspace_bytes(rows, logits_row_stride);
+  if (need > 0 && (!workspace || !aligned(workspace, 256) || workspace_bytes < need))
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_topk_ws(logits, rows, logits_row_stride, ks, ke, k, out_idx,
+                                        workspace, stream));
 }
 
 }  // extern "C"

@@ -55,5 +55,10 @@ hipError_t launch_topk_merge(const float* values, const int32_t* indices, int wo
 
 hipError_t launch_topk(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                        const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream);
+// Workspace bytes of launch_topk_ws (0: it runs launch_topk, no workspace).
+int64_t topk_workspace_bytes(int64_t rows, int64_t ld);
+hipError_t launch_topk_ws(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
+                          const int32_t* ke, int k, int32_t* out_idx, void* workspace,
+                          hipStream_t stream);
 
 }  // namespace mxidx

@@ -535,18 +535,17 @@ __device__ __forceinline__ void select_pairs(Shared<BINS>& s, uint32_t (&key)[E]
     }
 }
 
-// kLong = false: launched only when every row fits in registers (the long-row
-// code, and its registers, are left out).
+// Top-k of row r by one workgroup.  kLong = false: only rows that fit in
+// registers (the long-row code, and its registers, are left out); kLong =
+// true needs `dyn` = 64 KB of LDS.
 template <int NT, int E, int BINS, bool kLong>
-__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logits, int64_t ld,
-                                                  const int32_t* __restrict__ ks,
-                                                  const int32_t* __restrict__ ke, int k,
-                                                  int32_t* __restrict__ out_idx) {
+__device__ __forceinline__ void topk_row(Shared<BINS>& s, uint32_t* __restrict__ dyn,
+                                         const float* __restrict__ logits, int64_t ld, int64_t r,
+                                         const int32_t* __restrict__ ks,
+                                         const int32_t* __restrict__ ke, int k,
+                                         int32_t* __restrict__ out_idx) {
   constexpr int kWaves = NT / kWave;
   constexpr int64_t C = (int64_t)NT * E;          // keys held per pass
-  __shared__ Shared<BINS> s;
-  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];   // long rows only
-  const int64_t r = blockIdx.x;
   const float* row = logits + r * ld;
   int32_t* out = out_idx + r * (int64_t)k;
   const int64_t lo = ks ? max((int64_t)ks[r], (int64_t)0) : 0;
@@ -887,6 +886,225 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
   }
 }
 
+template <int NT, int E, int BINS, bool kLong>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logits, int64_t ld,
+                                                  const int32_t* __restrict__ ks,
+                                                  const int32_t* __restrict__ ke, int k,
+                                                  int32_t* __restrict__ out_idx) {
+  __shared__ Shared<BINS> s;
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];   // long rows only
+  topk_row<NT, E, BINS, kLong>(s, dyn, logits, ld, blockIdx.x, ks, ke, k, out_idx);
+}
+
+// ---------------------------------------------------------------------------
+// Long rows split over workgroups, in two launches.  With few long rows, one
+// workgroup per row leaves most CUs idle and the longest row sets the time.
+//
+// Parts: part p of row r -- columns [lo + p*P, lo + (p+1)*P), P = kPartKeys,
+// held in registers by one 512-thread workgroup -- picks a threshold t_p with
+// about 1.5 k * (part length / row length) + 32 of its keys at or above it
+// (one histogram level over the part's own key range) and writes those (key,
+// column) pairs in column order to its region of the workspace, with its
+// count and t_p (0 when it kept every key).  A row of at most P keys is
+// selected whole by its part 0.
+//
+// Merge, one 1024-thread workgroup per split row: every key of the row at or
+// above T = max_p t_p was kept by its part, so when at least k kept keys are
+// >= T the row's top-k lies among the kept pairs and is their top-k.
+// Otherwise -- a region overflowed, more pairs than the merge holds, or parts
+// so unlike that fewer than k kept keys reach T -- it selects over the whole
+// row as the one-workgroup kernel does.  The launch boundary makes the parts'
+// pairs visible to the merge (no fences or counters inside either kernel:
+// with one launch and a device counter, the per-workgroup L2 write-backs
+// serialized within each XCD).
+//
+// Workspace: headers [rows][parts] (count, t_p), then pair regions
+// [rows][parts][kPartPairs] (key, column); nothing needs initializing.
+constexpr int kPartThreads = 512;
+constexpr int kPartE = 16;
+constexpr int64_t kPartKeys = (int64_t)kPartThreads * kPartE;
+constexpr int kSplitMaxParts = 64;
+constexpr int kSplitMaxRows = 512;
+constexpr int kPartPairs = 4096;
+constexpr int kMergeThreads = 1024;
+constexpr int kMergePairs = 8192;       // 8 per thread of the merging workgroup
+
+__host__ __device__ constexpr int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+struct SplitWs {
+  uint2* hdr;
+  uint2* pairs;
+  __host__ __device__ SplitWs(void* base, int64_t rows, int parts) {
+    uint8_t* b = static_cast<uint8_t*>(base);
+    hdr = reinterpret_cast<uint2*>(b);
+    pairs = reinterpret_cast<uint2*>(b + align256(rows * parts * 8));
+  }
+  static int64_t bytes(int64_t rows, int parts) {
+    return align256(rows * parts * 8) + rows * parts * (int64_t)kPartPairs * 8;
+  }
+};
+
+__device__ __forceinline__ int64_t visible_len(const int32_t* __restrict__ ks,
+                                               const int32_t* __restrict__ ke, int64_t r,
+                                               int64_t ld, int64_t& lo) {
+  lo = ks ? max((int64_t)ks[r], (int64_t)0) : 0;
+  const int64_t hi = min((int64_t)ke[r], ld);
+  return hi > lo ? hi - lo : 0;
+}
+
+template <int NT, int E, int BINS>
+__global__ __launch_bounds__(NT) void topk_part_kernel(const float* __restrict__ logits,
+                                                       int64_t ld, const int32_t* __restrict__ ks,
+                                                       const int32_t* __restrict__ ke, int k,
+                                                       int32_t* __restrict__ out_idx,
+                                                       void* __restrict__ workspace, int64_t rows,
+                                                       int parts) {
+  constexpr int kWaves = NT / kWave;
+  constexpr int64_t C = (int64_t)NT * E;
+  static_assert(C == kPartKeys, "part size");
+  __shared__ Shared<BINS> s;
+  const int64_t r = blockIdx.y;
+  const int p = blockIdx.x;
+  int64_t lo;
+  const int64_t n = visible_len(ks, ke, r, ld, lo);
+  const int nparts = (int)((n + C - 1) / C);
+  if (nparts <= 1) {
+    if (p == 0) topk_row<NT, E, BINS, false>(s, nullptr, logits, ld, r, ks, ke, k, out_idx);
+    return;
+  }
+  if (p >= nparts) return;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const SplitWs ws(workspace, rows, parts);
+  int parity = 0;
+  const int64_t c0 = (int64_t)p * C;
+  const int64_t np = min(C, n - c0);
+  const float* src = logits + r * ld + lo + c0;
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  uint32_t key[E];
+  const int nv = load_keys<E>(src, np, vec, key);
+  clear_hist<NT>(s);
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e < nv) {
+      kmin = min(kmin, key[e]);
+      kmax = max(kmax, key[e]);
+    }
+  kmin = ~wave_umax(~kmin);
+  kmax = wave_umax(kmax);
+  if (lane == 0) {
+    s.wave_tot[1][wid] = kmin;
+    s.wave_tot[1][kMaxWaves + wid] = kmax;
+  }
+  __syncthreads();
+  kmin = ~wave_umax(lane < kWaves ? ~s.wave_tot[1][lane & 15] : 0u);
+  kmax = wave_umax(lane < kWaves ? s.wave_tot[1][kMaxWaves + (lane & 15)] : 0u);
+  const int64_t want = min(np, ((int64_t)3 * k * np) / (2 * n) + 32);
+  uint32_t t_p = kmin;                            // keep all (one distinct key, or want = np)
+  const uint32_t range = kmax - kmin;
+  if (range != 0 && want < np) {
+    const int L = 32 - __clz(range);
+    constexpr int D = digit_bits<BINS>();
+    const int nsh = L > D ? L - D : 0;
+    hist_first(s, key, nv, kmin, nsh);
+    __syncthreads();
+    select_bin<NT>(s, (uint32_t)want, parity);     // its scan writes wave_tot[0]
+    parity ^= 1;
+    t_p = kmin + (s.sel[0] << nsh);               // lower edge of the want-th key's bin
+  }
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) cnt += (e < nv && key[e] >= t_p) ? 1u : 0u;
+  uint32_t kept;
+  uint32_t pos = block_scan<NT>(cnt, s, parity, kept);
+  if (kept <= (uint32_t)kPartPairs) {
+    uint2* region = ws.pairs + (r * parts + p) * (int64_t)kPartPairs;
+    const uint32_t col0 = (uint32_t)(lo + c0 + (int64_t)E * threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (e < nv && key[e] >= t_p) region[pos++] = make_uint2(key[e], col0 + (uint32_t)e);
+  }
+  if (threadIdx.x == 0) ws.hdr[r * parts + p] = make_uint2(kept, t_p == kmin ? 0u : t_p);
+}
+
+template <int NT, int E, int BINS>
+__global__ __launch_bounds__(NT) void topk_part_merge_kernel(const float* __restrict__ logits,
+                                                             int64_t ld,
+                                                             const int32_t* __restrict__ ks,
+                                                             const int32_t* __restrict__ ke, int k,
+                                                             int32_t* __restrict__ out_idx,
+                                                             const void* __restrict__ workspace,
+                                                             int64_t rows, int parts) {
+  constexpr int E2 = kMergePairs / NT;
+  __shared__ Shared<BINS> s;
+  __shared__ uint32_t pbase[kSplitMaxParts + 1];
+  __shared__ uint32_t mstat[3];           // T, total, overflow
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  const int64_t r = blockIdx.x;
+  int64_t lo;
+  const int64_t n = visible_len(ks, ke, r, ld, lo);
+  const int nparts = (int)((n + kPartKeys - 1) / kPartKeys);
+  if (nparts <= 1) return;                      // selected by the part kernel
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const SplitWs ws(const_cast<void*>(workspace), rows, parts);
+  int parity = 0;
+  if (threadIdx.x == 0) s.ccount = 0;
+  clear_hist<NT>(s);
+  if (wid == 0) {
+    const uint2 h = lane < nparts ? ws.hdr[r * parts + lane] : make_uint2(0u, 0u);
+    const uint32_t inc = wave_incl_scan(h.x);
+    const uint32_t tstar = wave_umax(h.y);
+    const bool over = __ballot(h.x > (uint32_t)kPartPairs) != 0;
+    if (lane < nparts) pbase[lane + 1] = inc;
+    if (lane == 0) {
+      pbase[0] = 0;
+      mstat[0] = tstar;
+      mstat[1] = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+      mstat[2] = over ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint32_t tstar = mstat[0], total = mstat[1];
+  if (!mstat[2] && total <= (uint32_t)kMergePairs) {
+    // thread t takes the kept pairs E2*t .. E2*t + E2-1 (of all parts in order):
+    // its valid slots are a prefix, and only those are candidates
+    uint32_t mkey[E2], mcol[E2];
+    const uint32_t first = (uint32_t)(E2 * threadIdx.x);
+    const int nv2 = (int)min((uint32_t)E2, total - min(total, first));
+    int q = 0;                                   // part holding pair `first`
+    for (int step = kSplitMaxParts / 2; step > 0; step >>= 1)
+      if (q + step < nparts && pbase[q + step] <= first) q += step;
+    uint32_t reach = 0;
+#pragma unroll
+    for (int e = 0; e < E2; ++e) {
+      const uint32_t i = first + (uint32_t)e;
+      mkey[e] = 0u;
+      mcol[e] = 0xffffffffu;
+      if (e < nv2) {
+        while (pbase[q + 1] <= i) ++q;
+        const uint2 pr = ws.pairs[(r * parts + q) * (int64_t)kPartPairs + (i - pbase[q])];
+        mkey[e] = pr.x;
+        mcol[e] = pr.y;
+        reach += pr.x >= tstar ? 1u : 0u;
+      }
+    }
+    uint32_t reach_all;
+    (void)block_scan<NT>(reach, s, parity, reach_all);
+    parity ^= 1;
+    if (reach_all >= (uint32_t)k) {
+      // at least k kept keys reach T, so the row's top-k is the top-k of the kept pairs
+      __syncthreads();                            // wave_tot reads done before select_pairs
+      const uint32_t okmask = (1u << nv2) - 1u;
+      select_pairs<NT, kFewMerge>(s, mkey, mcol, okmask, nv2, k, out_idx + r * (int64_t)k, parity);
+      return;
+    }
+  }
+  __syncthreads();                                // shared state is reused below
+  topk_row<NT, E, BINS, true>(s, dyn, logits, ld, r, ks, ke, k, out_idx);
+}
+
 // ---------------------------------------------------------------------------
 // Merge of per-rank top-k lists (the exchange step of context-parallel
 // decode, P3 "SparseAttnIndexerKpool": dcp_rank / dcp_world_size /
@@ -978,7 +1196,50 @@ hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32
   return hipGetLastError();
 }
 
+// Rows split over workgroups: few rows (fewer than the 512 that fill the chip
+// with one workgroup each), rows longer than one part, and at most
+// kSplitMaxParts parts per row.
+int split_parts(int64_t rows, int64_t ld) {
+  if (rows < 1 || rows >= kSplitMaxRows || ld <= kPartKeys) return 0;
+  const int64_t parts = (ld + kPartKeys - 1) / kPartKeys;
+  return parts <= kSplitMaxParts ? (int)parts : 0;
+}
+
 }  // namespace
+
+int64_t topk_workspace_bytes(int64_t rows, int64_t ld) {
+  const int parts = split_parts(rows, ld);
+  return parts ? SplitWs::bytes(rows, parts) : 0;
+}
+
+hipError_t launch_topk_ws(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
+                          const int32_t* ke, int k, int32_t* out_idx, void* workspace,
+                          hipStream_t stream) {
+  const int parts = split_parts(rows, ld);
+  if (!parts) return launch_topk(logits, rows, ld, ks, ke, k, out_idx, stream);
+  // the merge's whole-row fallback uses the long-row path's 64 KB of LDS
+  constexpr size_t dyn = (size_t)kCandPairs * 2 * sizeof(uint32_t);
+  constexpr int kMaxDevices = 64;
+  static bool attr_set[kMaxDevices] = {};       // per device; racing first calls set it twice, harmlessly
+  const auto merge = topk_part_merge_kernel<kMergeThreads, 16, 2048>;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(merge),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL((topk_part_kernel<kPartThreads, kPartE, 2048>),
+                     dim3((unsigned)parts, (unsigned)rows), dim3(kPartThreads), 0, stream, logits,
+                     ld, ks, ke, k, out_idx, workspace, rows, parts);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge, dim3((unsigned)rows), dim3(kMergeThreads), dyn, stream, logits, ld, ks,
+                     ke, k, out_idx, static_cast<const void*>(workspace), rows, parts);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk_merge(const float* values, const int32_t* indices, int world, int k_in,
                              int64_t rows, int interleave, int k, int32_t* out_idx,

@@ -45,7 +45,7 @@ def test_header_declarations_are_exported(L):
 
 
 def test_version_and_strerror(L):
-    assert L.idx_version() == 103
+    assert L.idx_version() == 104
     for st in range(5):
         assert L.idx_strerror(st)
     assert L.idx_strerror(99) == b"unknown status"
@@ -154,11 +154,36 @@ def test_topk_argument_validation(L):
     assert L.idx_topk(P, 0, 64, None, P, 8, P, None) == OK
 
 
+def test_topk_workspace_sizes(L):
+    f = L.idx_topk_workspace_bytes
+    # 64 rows x 16 parts of 8192 columns: part headers, then 4096 pairs per part
+    assert f(64, 131072) == 8192 + 64 * 16 * 4096 * 8
+    assert f(3, 8193) == 256 + 3 * 2 * 4096 * 8
+    assert f(64, 8192) == 0             # one workgroup holds a row
+    assert f(512, 131072) == 0          # many rows fill the GPU unsplit
+    assert f(8, 64 * 8192) > 0 and f(8, 64 * 8192 + 1) == 0     # at most 64 parts
+    assert f(0, 131072) == 0 and f(-1, 131072) == 0 and f(4, -5) == 0
+
+
+def test_topk_ws_argument_validation(L):
+    f = L.idx_topk_ws
+    need = L.idx_topk_workspace_bytes(4, 40000)
+    assert need > 0
+    assert f(P, 4, 40000, None, P, 0, P, P2, need, None) == ERR_ARG        # k < 1
+    assert f(P, 4, 40000, None, None, 8, P, P2, need, None) == ERR_ARG     # null ke
+    assert f(P, 4, 40000, None, P, 8, P, None, need, None) == ERR_ARG      # no workspace
+    assert f(P, 4, 40000, None, P, 8, P, P2, need - 1, None) == ERR_ARG    # too small
+    assert f(P, 4, 40000, None, P, 8, P, ctypes.c_void_p(0x20080), need, None) == ERR_ARG  # misaligned
+    assert f(P, 0, 40000, None, P, 8, P, None, 0, None) == OK              # empty: no-op
+
+
 @pytest.mark.skipif(_has_gpu(), reason="checks the no-device path")
 def test_fails_closed_without_device(L):
     assert L.idx_init(0) == ERR_NO_DEVICE
     assert L.idx_quantize(P, 0, 4, 128, P, P2, None) == ERR_NO_DEVICE
     assert L.idx_topk(P, 4, 64, None, P, 8, P, None) == ERR_NO_DEVICE
+    assert L.idx_topk_ws(P, 4, 64, None, P, 8, P, None, 0, None) == ERR_NO_DEVICE   # no split: no workspace
+    assert L.idx_topk_ws(P, 4, 40000, None, P, 8, P, P2, 1 << 24, None) == ERR_NO_DEVICE
     assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 64, 1, None) == ERR_NO_DEVICE
     assert L.idx_logits_paged_insert(P, P, 0, P, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 64, 1,
                                      None) == ERR_NO_DEVICE
