@@ -40,12 +40,14 @@
 namespace mxidx {
 namespace {
 
-// Keys per workgroup: 1024, or 512 when S <= 16384 -- short causal inputs
+// Keys per workgroup: 4096, or 512 when S <= 16384 -- short causal inputs
 // (the 8192 chunk) have too little work per workgroup to hide its start-up,
-// and twice the workgroups balance better (measured: 8192 x 8192 145 -> 140 us;
-// 122880 keys 9.8 -> 10.1 ms with 512).
+// and more workgroups balance better (measured at 8192 x 8192: 512 keys 119.5 us,
+// 1024 129, 2048 156, 8192 136); long inputs amortize each workgroup's q and
+// weight loads over more keys (16384 x 122880: 1024 keys 9.86-9.90 ms, 4096
+// 9.64-9.68, 8192 9.63).
 constexpr int kKeyChunkSmallS = 512;
-constexpr int kKeyChunk = 1024;
+constexpr int kKeyChunk = 4096;
 constexpr int64_t kSmallS = 16384;
 
 // B operands of 64 consecutive keys c0..c0+63: lane (g, n) takes the 16 code
