@@ -37,7 +37,7 @@ def _end_to_end(ref_rows, bound_rows, ks, ke, k, idx_rows):
     return exact_rows
 
 
-def _decode_case_check(case, sample_seqs, check_bytes_tokens=None):
+def _decode_case_check(case, sample_seqs, check_bytes_tokens=None, split_topk=False):
     cache = new_cache(case["num_pages"], fill=0)
     mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
     qv, qs = mx.quantize(dev(case["q"]))
@@ -48,6 +48,9 @@ def _decode_case_check(case, sample_seqs, check_bytes_tokens=None):
                     dev(case["context_lens"]), case["next_n"], W, logits=logits, clean=True)
     ke = olog.decode_visible_end(case["context_lens"], case["next_n"]).astype(np.int32)
     idx = mx.topk(logits, None, dev(ke), case["topk"])
+    # the workspace top-k the long-context bench times (long rows split over workgroups)
+    idx_ws = mx.topk_ws(logits, None, dev(ke), case["topk"], mx.topk_workspace(R, W)) \
+        if split_topk else None
     torch.cuda.synchronize()
     cache_np = host(cache)
     if check_bytes_tokens is not None:
@@ -67,6 +70,11 @@ def _decode_case_check(case, sample_seqs, check_bytes_tokens=None):
     check_logits(g[rows], ref[rows], bound[rows], case["name"])
     out_idx = host(idx)
     _exact_sets(g, np.zeros(R, np.int32), ke, case["topk"], out_idx)
+    if idx_ws is not None:
+        ws_idx = host(idx_ws)
+        _exact_sets(g, np.zeros(R, np.int32), ke, case["topk"], ws_idx)
+        _end_to_end(ref[rows], bound[rows], np.zeros(len(rows), np.int32), ke[rows],
+                    case["topk"], ws_idx[rows])
     return _end_to_end(ref[rows], bound[rows], np.zeros(len(rows), np.int32), ke[rows],
                        case["topk"], out_idx[rows])
 
@@ -81,7 +89,7 @@ def test_long_context_decode_64_seqs():
     rng = np.random.default_rng(123)
     toks = rng.choice(len(case["slot_mapping"]), 4096, replace=False)
     _decode_case_check(case, sample_seqs=[int(np.argmax(case["context_lens"])), 5],
-                       check_bytes_tokens=toks)
+                       check_bytes_tokens=toks, split_topk=True)
 
 
 def _prefill_case_check(case, sample_rows):
