@@ -963,18 +963,54 @@ __global__ __launch_bounds__(NT) void topk_part_kernel(const float* __restrict__
   constexpr int64_t C = (int64_t)NT * E;
   static_assert(C == kPartKeys, "part size");
   __shared__ Shared<BINS> s;
-  const int64_t r = blockIdx.y;
-  const int p = blockIdx.x;
+  __shared__ int item_rp[2];
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  // Work items are listed row by row, row r holding max(1, its part count)
+  // of them, and workgroup i takes item i: the grid (rows x parts, an upper
+  // bound) ends with the workgroups that have no item, so those do not delay
+  // the dispatch of live ones.  Wave 0 finds (row, part) from a prefix over
+  // the rows' visible lengths.
+  if (wid == 0) {
+    const int64_t item = blockIdx.x;
+    int64_t base = 0;
+    int found_r = -1, found_p = 0;
+    for (int64_t r0 = 0; r0 < rows; r0 += kWave) {
+      const int64_t rr = r0 + lane;
+      uint32_t cnt = 0;
+      if (rr < rows) {
+        int64_t lo_r;
+        const int64_t n_r = visible_len(ks, ke, rr, ld, lo_r);
+        cnt = (uint32_t)max((int64_t)1, (n_r + C - 1) / C);
+      }
+      const uint32_t incl = wave_incl_scan(cnt);
+      const int64_t first = base + incl - cnt;
+      const bool mine = rr < rows && item >= first && item < first + cnt;
+      const uint64_t m = __ballot(mine);
+      if (m) {                                    // wave-uniform
+        const int src = (int)__builtin_ctzll(m);
+        found_r = __builtin_amdgcn_readlane((int)rr, src);
+        found_p = __builtin_amdgcn_readlane((int)(item - first), src);
+        break;
+      }
+      base += __builtin_amdgcn_readlane((int)incl, 63);
+    }
+    if (lane == 0) {
+      item_rp[0] = found_r;
+      item_rp[1] = found_p;
+    }
+  }
+  __syncthreads();
+  if (item_rp[0] < 0) return;                     // past the last item
+  const int64_t r = item_rp[0];
+  const int p = item_rp[1];
   int64_t lo;
   const int64_t n = visible_len(ks, ke, r, ld, lo);
   const int nparts = (int)((n + C - 1) / C);
   if (nparts <= 1) {
-    if (p == 0) topk_row<NT, E, BINS, false>(s, nullptr, logits, ld, r, ks, ke, k, out_idx);
+    topk_row<NT, E, BINS, false>(s, nullptr, logits, ld, r, ks, ke, k, out_idx);
     return;
   }
-  if (p >= nparts) return;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
   const SplitWs ws(workspace, rows, parts);
   int parity = 0;
   const int64_t c0 = (int64_t)p * C;
@@ -1232,8 +1268,8 @@ hipError_t launch_topk_ws(const float* logits, int64_t rows, int64_t ld, const i
     if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
   }
   hipLaunchKernelGGL((topk_part_kernel<kPartThreads, kPartE, 2048>),
-                     dim3((unsigned)parts, (unsigned)rows), dim3(kPartThreads), 0, stream, logits,
-                     ld, ks, ke, k, out_idx, workspace, rows, parts);
+                     dim3((unsigned)(parts * rows)), dim3(kPartThreads), 0, stream, logits, ld, ks,
+                     ke, k, out_idx, workspace, rows, parts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge, dim3((unsigned)rows), dim3(kMergeThreads), dyn, stream, logits, ld, ks,
