@@ -1088,42 +1088,76 @@ __global__ __launch_bounds__(NT) void topk_part_merge_kernel(const float* __rest
   int parity = 0;
   if (threadIdx.x == 0) s.ccount = 0;
   clear_hist<NT>(s);
+  // Pairs are loaded before the headers arrive: part q gets NT / P2 threads
+  // (P2 = the part count rounded up to a power of two, >= 2), thread j of
+  // them slots j*E2 .. j*E2 + E2-1 of the part's region -- at most 4096
+  // slots, so always inside the region; the headers then tell which slots
+  // hold pairs.  A part that kept more than its share of slots sends the
+  // merge to a dense reload.
+  int p2 = 2;
+  while (p2 < nparts) p2 <<= 1;
+  const int tpp = NT / p2;
+  const int sq = (int)threadIdx.x / tpp;
+  const uint32_t sbase = (uint32_t)(((int)threadIdx.x % tpp) * E2);
+  uint32_t mkey[E2], mcol[E2];
+  if (sq < nparts) {
+    const uint2* reg = ws.pairs + (r * parts + sq) * (int64_t)kPartPairs + sbase;
+#pragma unroll
+    for (int e = 0; e < E2; ++e) {
+      const uint2 pr = reg[e];
+      mkey[e] = pr.x;
+      mcol[e] = pr.y;
+    }
+  }
   if (wid == 0) {
     const uint2 h = lane < nparts ? ws.hdr[r * parts + lane] : make_uint2(0u, 0u);
     const uint32_t inc = wave_incl_scan(h.x);
     const uint32_t tstar = wave_umax(h.y);
     const bool over = __ballot(h.x > (uint32_t)kPartPairs) != 0;
+    const bool spill = __ballot(h.x > (uint32_t)(tpp * E2)) != 0;
     if (lane < nparts) pbase[lane + 1] = inc;
     if (lane == 0) {
       pbase[0] = 0;
       mstat[0] = tstar;
       mstat[1] = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-      mstat[2] = over ? 1u : 0u;
+      mstat[2] = (over ? 1u : 0u) | (spill ? 2u : 0u);
     }
   }
   __syncthreads();
   const uint32_t tstar = mstat[0], total = mstat[1];
-  if (!mstat[2] && total <= (uint32_t)kMergePairs) {
-    // thread t takes the kept pairs E2*t .. E2*t + E2-1 (of all parts in order):
-    // its valid slots are a prefix, and only those are candidates
-    uint32_t mkey[E2], mcol[E2];
-    const uint32_t first = (uint32_t)(E2 * threadIdx.x);
-    const int nv2 = (int)min((uint32_t)E2, total - min(total, first));
-    int q = 0;                                   // part holding pair `first`
-    for (int step = kSplitMaxParts / 2; step > 0; step >>= 1)
-      if (q + step < nparts && pbase[q + step] <= first) q += step;
+  const bool spill = (mstat[2] & 2u) != 0;
+  if (!(mstat[2] & 1u) && (!spill || total <= (uint32_t)kMergePairs)) {
+    // each thread's valid slots are a prefix of its E2, and only those are candidates
+    int nv2;
+    if (!spill) {
+      const uint32_t kq = sq < nparts ? pbase[sq + 1] - pbase[sq] : 0u;
+      nv2 = (int)min((uint32_t)E2, kq - min(kq, sbase));
+    } else {
+      // dense: thread t takes the kept pairs E2*t .. E2*t + E2-1 of all parts in order
+      const uint32_t first = (uint32_t)(E2 * threadIdx.x);
+      nv2 = (int)min((uint32_t)E2, total - min(total, first));
+      int q = 0;                                 // part holding pair `first`
+      for (int step = kSplitMaxParts / 2; step > 0; step >>= 1)
+        if (q + step < nparts && pbase[q + step] <= first) q += step;
+#pragma unroll
+      for (int e = 0; e < E2; ++e) {
+        const uint32_t i = first + (uint32_t)e;
+        if (e < nv2) {
+          while (pbase[q + 1] <= i) ++q;
+          const uint2 pr = ws.pairs[(r * parts + q) * (int64_t)kPartPairs + (i - pbase[q])];
+          mkey[e] = pr.x;
+          mcol[e] = pr.y;
+        }
+      }
+    }
     uint32_t reach = 0;
 #pragma unroll
     for (int e = 0; e < E2; ++e) {
-      const uint32_t i = first + (uint32_t)e;
-      mkey[e] = 0u;
-      mcol[e] = 0xffffffffu;
       if (e < nv2) {
-        while (pbase[q + 1] <= i) ++q;
-        const uint2 pr = ws.pairs[(r * parts + q) * (int64_t)kPartPairs + (i - pbase[q])];
-        mkey[e] = pr.x;
-        mcol[e] = pr.y;
-        reach += pr.x >= tstar ? 1u : 0u;
+        reach += mkey[e] >= tstar ? 1u : 0u;
+      } else {
+        mkey[e] = 0u;
+        mcol[e] = 0xffffffffu;
       }
     }
     uint32_t reach_all;
