@@ -361,11 +361,22 @@ __device__ __forceinline__ void select_few(Shared<BINS>& s, const uint32_t (&key
   if (i < cnt) {
     ki = s.ckey[i];
     ci = s.ccol[i];
+    if constexpr (kJ <= 8) {
+      // a few comparisons per thread: unrolled, their LDS reads in flight together
 #pragma unroll
-    for (int jj = 0; jj < kJ; ++jj) {
-      const uint32_t j = j0 + jj;
-      if (j < cnt) {
-        const uint32_t kj = s.ckey[j], cj = s.ccol[j];
+      for (int jj = 0; jj < kJ; ++jj) {
+        const uint32_t j = j0 + jj;
+        if (j < cnt) {
+          const uint32_t kj = s.ckey[j], cj = s.ccol[j];
+          before += (kj > ki || (kj == ki && cj < ci)) ? 1u : 0u;
+        }
+      }
+    } else {
+      // a long share (the 256-key ranking): bounded by the bin's size, which is
+      // usually a few keys, instead of testing every slot of the share
+      const uint32_t jn = cnt > j0 ? min((uint32_t)kJ, cnt - j0) : 0u;
+      for (uint32_t jj = 0; jj < jn; ++jj) {
+        const uint32_t kj = s.ckey[j0 + jj], cj = s.ccol[j0 + jj];
         before += (kj > ki || (kj == ki && cj < ci)) ? 1u : 0u;
       }
     }
