@@ -1054,9 +1054,16 @@ __global__ __launch_bounds__(NT) void topk_part_kernel(const float* __restrict__
     const int L = 32 - __clz(range);
     constexpr int D = digit_bits<BINS>();
     const int nsh = L > D ? L - D : 0;
-    hist_first(s, key, nv, kmin, nsh);
+    // the estimate histograms every other key (half the LDS atomics; the
+    // merge's checks keep the result exact whatever the estimate)
+    constexpr int EH = E / 2;
+    uint32_t half[EH];
+#pragma unroll
+    for (int e = 0; e < EH; ++e) half[e] = key[2 * e];
+    const int nvh = (nv + 1) / 2;
+    hist_first(s, half, nvh, kmin, nsh);
     __syncthreads();
-    select_bin<NT>(s, (uint32_t)want, parity);     // its scan writes wave_tot[0]
+    select_bin<NT>(s, (uint32_t)max((int64_t)1, want / 2), parity);   // its scan writes wave_tot[0]
     parity ^= 1;
     t_p = kmin + (s.sel[0] << nsh);               // lower edge of the want-th key's bin
   }
