@@ -447,6 +447,13 @@ __device__ __forceinline__ void emit_regs(Shared<BINS>& s, const uint32_t (&key)
 // then -1; the order is deterministic.  Starts with the histogram cleared,
 // ccount zero, and a barrier after the caller's last scan.
 template <int NT, int FEW, int BINS, int E>
+__device__ __forceinline__ void select_pairs_ranged(Shared<BINS>& s, uint32_t (&key)[E],
+                                                    const uint32_t (&col)[E], uint32_t okmask,
+                                                    int nv, int k, int32_t* __restrict__ out,
+                                                    int parity, uint32_t kmin, uint32_t kmax,
+                                                    uint32_t total_valid);
+
+template <int NT, int FEW, int BINS, int E>
 __device__ __forceinline__ void select_pairs(Shared<BINS>& s, uint32_t (&key)[E],
                                              const uint32_t (&col)[E], uint32_t okmask, int nv,
                                              int k, int32_t* __restrict__ out, int parity) {
@@ -476,7 +483,18 @@ __device__ __forceinline__ void select_pairs(Shared<BINS>& s, uint32_t (&key)[E]
   kmin = ~wave_umax(lane < kWaves ? ~wr[lane & 15] : 0u);
   kmax = wave_umax(lane < kWaves ? wr[kMaxWaves + (lane & 15)] : 0u);
   __syncthreads();                              // the next scan rewrites that buffer
+  select_pairs_ranged<NT, FEW>(s, key, col, okmask, nv, k, out, parity, kmin, kmax, total_valid);
+}
 
+// select_pairs once the valid count and bounds of the valid keys are known:
+// kmin <= every valid key <= kmax (bounds, not necessarily attained).  Starts
+// like select_pairs, after a barrier that follows the caller's last scan.
+template <int NT, int FEW, int BINS, int E>
+__device__ __forceinline__ void select_pairs_ranged(Shared<BINS>& s, uint32_t (&key)[E],
+                                                    const uint32_t (&col)[E], uint32_t okmask,
+                                                    int nv, int k, int32_t* __restrict__ out,
+                                                    int parity, uint32_t kmin, uint32_t kmax,
+                                                    uint32_t total_valid) {
   if (total_valid <= (uint32_t)k) {             // every valid candidate, then -1
     uint32_t tot;
     uint32_t pos = block_scan<NT>((uint32_t)__popc(okmask), s, parity, tot);
@@ -929,8 +947,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
 // with one launch and a device counter, the per-workgroup L2 write-backs
 // serialized within each XCD).
 //
-// Workspace: headers [rows][parts] (count, t_p), then pair regions
-// [rows][parts][kPartPairs] (key, column); nothing needs initializing.
+// Workspace: headers [rows][parts] (count, t_p or 0, a lower bound of the kept
+// keys, the part's largest key), then pair regions [rows][parts][kPartPairs]
+// (key, column); nothing needs initializing.
 constexpr int kPartThreads = 512;
 constexpr int kPartE = 16;
 constexpr int64_t kPartKeys = (int64_t)kPartThreads * kPartE;
@@ -943,15 +962,15 @@ constexpr int kMergePairs = 8192;       // 8 per thread of the merging workgroup
 __host__ __device__ constexpr int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 struct SplitWs {
-  uint2* hdr;
+  uint4* hdr;
   uint2* pairs;
   __host__ __device__ SplitWs(void* base, int64_t rows, int parts) {
     uint8_t* b = static_cast<uint8_t*>(base);
-    hdr = reinterpret_cast<uint2*>(b);
-    pairs = reinterpret_cast<uint2*>(b + align256(rows * parts * 8));
+    hdr = reinterpret_cast<uint4*>(b);
+    pairs = reinterpret_cast<uint2*>(b + align256(rows * parts * 16));
   }
   static int64_t bytes(int64_t rows, int parts) {
-    return align256(rows * parts * 8) + rows * parts * (int64_t)kPartPairs * 8;
+    return align256(rows * parts * 16) + rows * parts * (int64_t)kPartPairs * 8;
   }
 };
 
@@ -1079,7 +1098,7 @@ __global__ __launch_bounds__(NT) void topk_part_kernel(const float* __restrict__
     for (int e = 0; e < E; ++e)
       if (e < nv && key[e] >= t_p) region[pos++] = make_uint2(key[e], col0 + (uint32_t)e);
   }
-  if (threadIdx.x == 0) ws.hdr[r * parts + p] = make_uint2(kept, t_p == kmin ? 0u : t_p);
+  if (threadIdx.x == 0) ws.hdr[r * parts + p] = make_uint4(kept, t_p == kmin ? 0u : t_p, t_p, kmax);
 }
 
 template <int NT, int E, int BINS>
@@ -1093,7 +1112,7 @@ __global__ __launch_bounds__(NT) void topk_part_merge_kernel(const float* __rest
   constexpr int E2 = kMergePairs / NT;
   __shared__ Shared<BINS> s;
   __shared__ uint32_t pbase[kSplitMaxParts + 1];
-  __shared__ uint32_t mstat[3];           // T, total, overflow
+  __shared__ uint32_t mstat[5];           // T, total, overflow / spill, key bounds
   extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
   const int64_t r = blockIdx.x;
   int64_t lo;
@@ -1128,9 +1147,11 @@ __global__ __launch_bounds__(NT) void topk_part_merge_kernel(const float* __rest
     }
   }
   if (wid == 0) {
-    const uint2 h = lane < nparts ? ws.hdr[r * parts + lane] : make_uint2(0u, 0u);
+    const uint4 h = lane < nparts ? ws.hdr[r * parts + lane] : make_uint4(0u, 0u, 0xffffffffu, 0u);
     const uint32_t inc = wave_incl_scan(h.x);
     const uint32_t tstar = wave_umax(h.y);
+    const uint32_t klo = ~wave_umax(~h.z);      // every kept key lies in [klo, khi]
+    const uint32_t khi = wave_umax(h.w);
     const bool over = __ballot(h.x > (uint32_t)kPartPairs) != 0;
     const bool spill = __ballot(h.x > (uint32_t)(tpp * E2)) != 0;
     if (lane < nparts) pbase[lane + 1] = inc;
@@ -1139,6 +1160,8 @@ __global__ __launch_bounds__(NT) void topk_part_merge_kernel(const float* __rest
       mstat[0] = tstar;
       mstat[1] = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
       mstat[2] = (over ? 1u : 0u) | (spill ? 2u : 0u);
+      mstat[3] = klo;
+      mstat[4] = khi;
     }
   }
   __syncthreads();
@@ -1184,8 +1207,11 @@ __global__ __launch_bounds__(NT) void topk_part_merge_kernel(const float* __rest
     if (reach_all >= (uint32_t)k) {
       // at least k kept keys reach T, so the row's top-k is the top-k of the kept pairs
       __syncthreads();                            // wave_tot reads done before select_pairs
+      // the kept pairs are all valid: their count and key bounds come from the
+      // headers, so the selection skips its own range and count pass
       const uint32_t okmask = (1u << nv2) - 1u;
-      select_pairs<NT, kFewMerge>(s, mkey, mcol, okmask, nv2, k, out_idx + r * (int64_t)k, parity);
+      select_pairs_ranged<NT, kFewMerge>(s, mkey, mcol, okmask, nv2, k, out_idx + r * (int64_t)k,
+                                         parity, mstat[3], mstat[4], total);
       return;
     }
   }

@@ -156,8 +156,8 @@ def test_topk_argument_validation(L):
 
 def test_topk_workspace_sizes(L):
     f = L.idx_topk_workspace_bytes
-    # 64 rows x 16 parts of 8192 columns: part headers, then 4096 pairs per part
-    assert f(64, 131072) == 8192 + 64 * 16 * 4096 * 8
+    # 64 rows x 16 parts of 8192 columns: 16-byte part headers, then 4096 pairs per part
+    assert f(64, 131072) == 64 * 16 * 16 + 64 * 16 * 4096 * 8
     assert f(3, 8193) == 256 + 3 * 2 * 4096 * 8
     assert f(64, 8192) == 0             # one workgroup holds a row
     assert f(512, 131072) == 0          # many rows fill the GPU unsplit
