@@ -30,12 +30,35 @@ Arithmetic: integer bit operations for the codec, float64 for the logits.
 Every reading taken where the pages are silent is stated in the function
 that takes it.
 
-Parity status: every function here is pinned by ``tests/test_oracle_*.py``
-against closed forms, exhaustive brute force, hand-worked bytes
-(``tests/golden/``) or exact rational arithmetic.  No function is left
-"parity unpinned", but the byte-layout choices that the pages leave open
-(page split, nibble order, sign of zero, scale byte order) are pinned only by
-the hand-worked bytes derived from the adopted reading.
+Parity status: every function here is pinned on the CPU against values fixed
+independently of its code.  Function -> pin (test file):
+
+* mxfp4.e2m1_value -- the OCP E2M1 table, all 16 nibbles (test_oracle_codec)
+* mxfp4.ue8m0_exponent -- its defining property (smallest E with
+  amax <= 6 * 2**E), exhaustively over positive finite bf16 and at fp32
+  boundaries (test_oracle_codec)
+* mxfp4.e2m1_encode -- brute-force nearest grid point, ties to the even code,
+  over every finite bf16 pattern (test_oracle_codec)
+* mxfp4.quantize_rows / dequantize_rows -- hand-worked blocks A-G
+  (tests/golden/mxfp4_blocks.txt) and the exact round trip (test_oracle_codec)
+* paged_cache.insert / write_rows / gather / read_token -- hand-worked byte
+  offsets, canaries, slot -1 and the insert/gather round trip (test_oracle_codec)
+* logits.mqa_logits / paged_mqa_logits -- exact rational arithmetic, closed
+  forms (one head, one-hot weights), 2**m scaling, page-order invariance, paged
+  == dense (test_oracle_logits)
+* logits.abs_bound and the with_bound outputs -- the exact rational A, and
+  equality of the three ways of computing it (test_oracle_tolerance)
+* topk.top_k_per_row, merge_shard_topk, shard_to_global / global_to_shard --
+  brute-force sorts, hand-worked rows and layouts (test_oracle_topk)
+* topk.kth_value -- a plain Python sort (test_oracle_tolerance)
+* tolerance.logits_close, tolerance.topk_end_to_end_ok -- exact boundary
+  cases and hand-worked rows (test_oracle_tolerance)
+
+The pins of the comparison rules and of A are also run against copies of the
+functions with one planted mistake each, and must reject every copy.  The
+byte-layout choices that the pages leave open (page split, nibble order, sign
+of zero, scale byte order) are pinned by the hand-worked bytes derived from the
+adopted reading.
 """
 
 from . import mxfp4, paged_cache, logits, topk, tolerance  # noqa: F401
