@@ -53,7 +53,9 @@
  *     (fail-closed gate, as P2 "Summary" asks of its kernels); on other
  *     devices every call returns IDX_ERR_UNSUPPORTED_ARCH.
  *   - No exception crosses this boundary; launch failures return IDX_ERR_LAUNCH.
- *   - Calls are thread-safe; calls on one stream execute in order.
+ *   - Calls are thread-safe: the library's only global state is the gate's
+ *     per-device result and per-device "attribute set" flags, all atomics.
+ *     Calls on one stream execute in order.
  */
 #ifndef MXIDX_H
 #define MXIDX_H
@@ -93,6 +95,15 @@ int idx_version(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* idx_strerror(int status);
+
+/* The architecture rule of the gate, on a device's gcnArchName string (host
+ * only; no device is touched): IDX_OK for "gfx950", alone or followed by
+ * ':'-separated target features, IDX_ERR_UNSUPPORTED_ARCH for any other
+ * string or NULL.  Every call runs this rule on the current device's name
+ * before its first launch there (P2 "Summary": fail-closed capability gates);
+ * the environment variable MXIDX_FORCE_ARCH, read at that first check,
+ * replaces the device's name (a test hook). */
+int idx_arch_supported(const char* gcn_arch_name);
 
 /* Run the architecture gate for `device` now (it otherwise runs on the first
  * call that enqueues work on that device).  Returns IDX_OK on gfx950,
@@ -170,8 +181,9 @@ int idx_gather(const uint8_t* cache, int64_t num_pages, int page_size,
  *   logits   [T, logits_row_stride] fp32 out, logits_row_stride >= S.
  *   clean != 0: columns outside [ks, ke) of [0, S) are set to -inf;
  *   clean == 0: they are left untouched.
- * H must be a multiple of 16 in [16, 128].  Accumulation is fp32 (exact
- * products, fp32 sums over the 4 blocks and the heads). */
+ * H must be a multiple of 16 in [16, 128]; 0 <= S <= 2^31 - 1025 (columns are
+ * int32 in the kernel).  Accumulation is fp32 (exact products, fp32 sums over
+ * the 4 blocks and the heads). */
 int idx_logits_prefill(const uint8_t* q_values, const uint8_t* q_scales,
                        const uint8_t* k_values, const uint8_t* k_scales,
                        const float* weights, const int32_t* ks, const int32_t* ke,

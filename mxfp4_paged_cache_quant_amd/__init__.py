@@ -42,6 +42,7 @@ EXPORTS = {
     "idx_version": (_int, []),
     "idx_strerror": (ctypes.c_char_p, [_int]),
     "idx_init": (_int, [_int]),
+    "idx_arch_supported": (_int, [ctypes.c_char_p]),
     "idx_quantize": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
     "idx_insert": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int, _c_void_p]),
     "idx_insert_quantize": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int,

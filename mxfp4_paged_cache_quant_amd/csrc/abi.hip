@@ -8,6 +8,8 @@
 #include "mxidx.h"
 #include "launch.hpp"
 
+extern "C" int idx_arch_supported(const char* gcn_arch_name);
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -26,7 +28,7 @@ int gate_device(int dev) {
   const char* arch = prop.gcnArchName;
   // Test hook: pretend the device reports another architecture.
   if (const char* forced = std::getenv("MXIDX_FORCE_ARCH")) arch = forced;
-  const bool ok = std::strncmp(arch, "gfx950", 6) == 0 && (arch[6] == '\0' || arch[6] == ':');
+  const bool ok = idx_arch_supported(arch) == IDX_OK;
   g_gate[dev].store(ok ? 1 : 2, std::memory_order_release);
   return ok ? IDX_OK : IDX_ERR_UNSUPPORTED_ARCH;
 }
@@ -57,7 +59,15 @@ int check_rows_input(const void* x, int dtype, int64_t rows, int64_t row_stride)
 
 extern "C" {
 
-int idx_version(void) { return 104; }
+int idx_version(void) { return 105; }
+
+int idx_arch_supported(const char* gcn_arch_name) {
+  // "gfx950" alone or followed by target features ("gfx950:sramecc+:xnack-")
+  if (!gcn_arch_name) return IDX_ERR_UNSUPPORTED_ARCH;
+  const bool ok = std::strncmp(gcn_arch_name, "gfx950", 6) == 0 &&
+                  (gcn_arch_name[6] == '\0' || gcn_arch_name[6] == ':');
+  return ok ? IDX_OK : IDX_ERR_UNSUPPORTED_ARCH;
+}
 
 const char* idx_strerror(int status) {
   switch (status) {

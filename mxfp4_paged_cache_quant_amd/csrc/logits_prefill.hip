@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(
   }
   const int64_t t0 = qb * (4 * RW) + wave * RW;
   const int c_begin = (int)kc * key_chunk;
-  const int c_end = min(c_begin + key_chunk, S);
+  const int c_end = (int)min((int64_t)c_begin + key_chunk, (int64_t)S);   // no int32 overflow near S = 2^31
 
   // visible range of each row (empty for rows past T), and the key window
   // [need_lo, need_hi) inside this chunk that any of the rows needs

@@ -36,6 +36,7 @@
 //     the keys, the second writes the keys above the threshold bin directly
 //     and compacts the bin's (key, column) pairs into LDS (up to 8192, else
 //     the remaining levels re-read the row filtered by the bin).
+#include <atomic>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1282,6 +1283,31 @@ __global__ __launch_bounds__(NT) void topk_merge_kernel(const float* __restrict_
   select_pairs<NT, kFewMerge>(s, key, col, okmask, nv, k, out, parity);
 }
 
+// Kernels that take more than the default dynamic LDS need the attribute set
+// once per device.  The per-device flags are atomics (release after the set,
+// acquire before skipping it), so concurrent first calls from several host
+// threads are well defined: at worst two of them both set the attribute.
+constexpr int kAttrDevices = 64;
+
+hipError_t allow_dyn_lds(const void* kernel, int bytes, std::atomic<bool>* flags) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool tracked = dev >= 0 && dev < kAttrDevices;
+  if (tracked && flags[dev].load(std::memory_order_acquire)) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  if (tracked) flags[dev].store(true, std::memory_order_release);
+  return hipSuccess;
+}
+
+// One set of flags per kernel instantiation.
+template <int NT, int E, int BINS>
+std::atomic<bool>* attr_flags() {
+  static std::atomic<bool> flags[kAttrDevices];
+  return flags;
+}
+
 template <int NT, int E, int BINS>
 hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                       const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {
@@ -1293,18 +1319,9 @@ hipError_t launch_cfg(const float* logits, int64_t rows, int64_t ld, const int32
                        logits, ld, ks, ke, k, out_idx);
     return hipGetLastError();
   }
-  // once per device (setting it twice from racing threads is harmless)
-  constexpr int kMaxDevices = 64;
-  static bool attr_set[kMaxDevices] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(topk_kernel<NT, E, BINS, true>),
+                               (int)dyn, attr_flags<NT, E, BINS>());
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(topk_kernel<NT, E, BINS, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
-  }
   hipLaunchKernelGGL((topk_kernel<NT, E, BINS, true>), dim3((unsigned)rows), dim3(NT), dyn, stream,
                      logits, ld, ks, ke, k, out_idx);
   return hipGetLastError();
@@ -1333,18 +1350,10 @@ hipError_t launch_topk_ws(const float* logits, int64_t rows, int64_t ld, const i
   if (!parts) return launch_topk(logits, rows, ld, ks, ke, k, out_idx, stream);
   // the merge's whole-row fallback uses the long-row path's 64 KB of LDS
   constexpr size_t dyn = (size_t)kCandPairs * 2 * sizeof(uint32_t);
-  constexpr int kMaxDevices = 64;
-  static bool attr_set[kMaxDevices] = {};       // per device; racing first calls set it twice, harmlessly
+  static std::atomic<bool> merge_attr[kAttrDevices];
   const auto merge = topk_part_merge_kernel<kMergeThreads, 16, 2048>;
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  hipError_t e = allow_dyn_lds(reinterpret_cast<const void*>(merge), (int)dyn, merge_attr);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(merge),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-    if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices) attr_set[dev] = true;
-  }
   hipLaunchKernelGGL((topk_part_kernel<kPartThreads, kPartE, 2048>),
                      dim3((unsigned)(parts * rows)), dim3(kPartThreads), 0, stream, logits, ld, ks,
                      ke, k, out_idx, workspace, rows, parts);

@@ -60,3 +60,31 @@ def check_logits(gpu, ref, bound, what=""):
         bad = np.argwhere(vis)[~ok][:5]
         raise AssertionError(f"{what}: {int((~ok).sum())} logits out of tolerance, e.g. at "
                              f"{bad.tolist()}: gpu {gpu[tuple(bad[0])]} ref {ref[tuple(bad[0])]}")
+
+
+def check_topk_sets(g_logits, ks, ke, k, out_idx, what=""):
+    """Exact top-k sets vs the oracle's top-k of the same (GPU) fp32 logits."""
+    from oracle import topk as otk
+    ref_sets = otk.top_k_per_row(g_logits, ks, ke, k)
+    for r in range(g_logits.shape[0]):
+        assert sorted(out_idx[r].tolist()) == sorted(ref_sets[r].tolist()), f"{what} top-k row {r}"
+
+
+def check_topk_end_to_end(ref_rows, bound_rows, ks, ke, k, idx_rows, what=""):
+    """End-to-end margin rule of GPU top-k rows against the oracle's float64
+    logits of the same rows; returns how many rows needed the exact set."""
+    from oracle import tolerance, topk as otk
+    exact_rows = 0
+    for j in range(len(ref_rows)):
+        vis = np.isfinite(ref_rows[j])
+        vk = otk.kth_value(ref_rows[j], int(ks[j]), int(ke[j]), k)
+        if vk is None:
+            assert np.all(np.asarray(idx_rows[j]) == -1), f"{what}: empty row {j} returned columns"
+            exact_rows += 1
+            continue
+        tol = tolerance.REL * abs(vk) + tolerance.ABS_FACTOR * float(bound_rows[j][vis].max())
+        ok, exact_req = tolerance.topk_end_to_end_ok(idx_rows[j], ref_rows[j], int(ks[j]),
+                                                     int(ke[j]), k, tol)
+        assert ok, f"{what}: end-to-end top-k, row {j}"
+        exact_rows += exact_req
+    return exact_rows

@@ -45,7 +45,7 @@ def test_header_declarations_are_exported(L):
 
 
 def test_version_and_strerror(L):
-    assert L.idx_version() == 104
+    assert L.idx_version() == 105
     for st in range(5):
         assert L.idx_strerror(st)
     assert L.idx_strerror(99) == b"unknown status"
@@ -192,3 +192,23 @@ def test_fails_closed_without_device(L):
 def test_python_wrapper_raises_on_error(L):
     with pytest.raises(mx.MxidxError):
         mx._check(ERR_ARG, "probe")
+
+
+def test_arch_rule_fails_closed(L):
+    """The gate's architecture rule (P2 "Summary": fail-closed capability gates):
+    only gfx950, bare or with target features, is accepted."""
+    for name in (b"gfx950", b"gfx950:sramecc+:xnack-", b"gfx950:xnack+"):
+        assert L.idx_arch_supported(name) == OK, name
+    for name in (b"gfx942", b"gfx942:sramecc+:xnack-", b"gfx9500", b"gfx95", b"gfx90a", b"gfx1100",
+                 b"", b"sm_100", b" gfx950", b"GFX950"):
+        assert L.idx_arch_supported(name) == ERR_ARCH, name
+    assert L.idx_arch_supported(None) == ERR_ARCH
+
+
+def test_prefill_key_count_limit(L):
+    """S up to 2^31 - 1025 is accepted (here with no query rows: a no-op), one
+    more is rejected before any device work."""
+    lim = 0x7fffffff - 1024
+    assert L.idx_logits_prefill(P, P, P, P, P, P, P, 0, 32, lim, P, lim, 1, None) == OK
+    assert L.idx_logits_prefill(P, P, P, P, P, P, P, 0, 32, lim + 1, P, lim + 1, 1, None) == ERR_ARG
+    assert L.idx_logits_prefill(P, P, P, P, P, P, P, 4, 32, lim + 1, P, lim + 1, 1, None) == ERR_ARG

@@ -10,31 +10,19 @@ import torch
 
 import mxfp4_paged_cache_quant_amd as mx
 import workloads
-from oracle import logits as olog, mxfp4 as omx, paged_cache as opc, tolerance, topk as otk
-from tests.gpu_helpers import check_logits, dev, exact, host, new_cache, oracle_q  # noqa: F401
+from oracle import logits as olog, mxfp4 as omx, paged_cache as opc
+from tests.gpu_helpers import (check_logits, check_topk_end_to_end, check_topk_sets, dev, exact,  # noqa: F401
+                               host, new_cache, oracle_q)
 
 pytestmark = pytest.mark.gpu
 
 
 def _exact_sets(g_logits, ks, ke, k, out_idx):
-    """Exact top-k sets vs the oracle's top-k of the same GPU logits."""
-    ref_sets = otk.top_k_per_row(g_logits, ks, ke, k)
-    for r in range(g_logits.shape[0]):
-        assert sorted(out_idx[r].tolist()) == sorted(ref_sets[r].tolist()), f"row {r}"
+    check_topk_sets(g_logits, ks, ke, k, out_idx)
 
 
 def _end_to_end(ref_rows, bound_rows, ks, ke, k, idx_rows):
-    """End-to-end margin rule of the GPU top-k against the oracle's logits."""
-    exact_rows = 0
-    for j in range(len(ref_rows)):
-        vis = np.isfinite(ref_rows[j])
-        vk = otk.kth_value(ref_rows[j], int(ks[j]), int(ke[j]), k)
-        tol = tolerance.REL * abs(vk) + tolerance.ABS_FACTOR * float(bound_rows[j][vis].max())
-        ok, exact_req = tolerance.topk_end_to_end_ok(idx_rows[j], ref_rows[j], int(ks[j]),
-                                                     int(ke[j]), k, tol)
-        assert ok, f"end-to-end top-k, sampled row {j}"
-        exact_rows += exact_req
-    return exact_rows
+    return check_topk_end_to_end(ref_rows, bound_rows, ks, ke, k, idx_rows)
 
 
 def _decode_case_check(case, sample_seqs, check_bytes_tokens=None, split_topk=False):

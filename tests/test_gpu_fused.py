@@ -1,8 +1,11 @@
 """GPU parity of the one-launch decode step (idx_logits_paged_insert): the cache
 bytes and logits must equal, bit for bit, those of the separate calls --
 idx_insert of the new tokens into their block-table slots, idx_quantize of q,
-idx_logits_paged -- which the other GPU tests hold to the oracle; one small case
-is also checked against the oracle directly."""
+idx_logits_paged -- and they are also held to the oracle directly: the whole
+cache against the oracle's insert of every token, the logits of sampled
+sequences at the logits tolerance, and the top-k sets of those rows (the
+16 x 8192 bf16 step the bench times, a bf16 next_n = 2 step, and a small fp32
+step)."""
 
 import numpy as np
 import pytest
@@ -10,8 +13,9 @@ import torch
 
 import mxfp4_paged_cache_quant_amd as mx
 import workloads
-from oracle import logits as olog
-from tests.gpu_helpers import check_logits, dev, host, new_cache, oracle_q
+from oracle import logits as olog, paged_cache as opc
+from tests.gpu_helpers import (CANARY, check_logits, check_topk_end_to_end, check_topk_sets, dev,
+                               exact, host, new_cache, oracle_q)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +121,58 @@ def test_fused_invalid_table_entries_skip_the_page():
 def test_fused_paged_decode_16x8192():
     case = workloads.paged_decode()
     _assert_same(case, clean=False, what="16x8192")
+
+
+def _against_oracle(case, sample_seqs, clean, what):
+    """The one-launch step vs the oracle: the whole cache (every token, the new
+    ones written by the step itself), the logits of ``sample_seqs`` at the
+    logits tolerance, and exact / end-to-end top-k sets of those rows (the GPU
+    top-k of the step's logits, as the bench runs it)."""
+    cache, logits = _assert_same(case, clean=clean, what=what)
+    ke = olog.decode_visible_end(case["context_lens"], case["next_n"]).astype(np.int32)
+    R = len(ke)
+    idx = mx.topk(logits, None, dev(ke), case["topk"])
+    torch.cuda.synchronize()
+    ref_cache = opc.insert(np.full((case["num_pages"], 64 * 68), CANARY, np.uint8),
+                           exact(case, "k"), case["slot_mapping"])
+    got_cache = host(cache)
+    assert np.array_equal(got_cache, ref_cache), \
+        f"{what}: cache bytes differ from the oracle at {np.argwhere(got_cache != ref_cache)[:4].tolist()}"
+    qc, qs = oracle_q(case)
+    ref, bound = olog.paged_mqa_logits(qc, qs, case["w"], ref_cache, case["block_table"],
+                                       case["context_lens"], case["next_n"], case["width"],
+                                       seqs=sample_seqs, with_bound=True)
+    nn = case["next_n"]
+    rows = np.concatenate([np.arange(b * nn, (b + 1) * nn) for b in sample_seqs])
+    g = host(logits)
+    if clean:
+        check_logits(g[rows], ref[rows], bound[rows], what)
+    else:
+        # clean = 0 leaves masked columns untouched: compare the visible ones
+        for r in rows:
+            vis = np.isfinite(ref[r])
+            check_logits(g[r][vis][None], ref[r][vis][None], bound[r][vis][None], f"{what} row {r}")
+    out = host(idx)
+    zeros = np.zeros(R, np.int32)
+    gv = np.where(np.arange(g.shape[1])[None, :] < ke[:, None], g, -np.inf).astype(np.float32)
+    check_topk_sets(gv[rows], zeros[rows], ke[rows], case["topk"], out[rows], what)
+    return check_topk_end_to_end(ref[rows], bound[rows], zeros[rows], ke[rows], case["topk"],
+                                 out[rows], what)
+
+
+def test_fused_paged_decode_16x8192_against_oracle():
+    """The bench's timed step (bf16, 16 x 8192, H 32, clean = 0, top-2048)."""
+    case = workloads.paged_decode()
+    _against_oracle(case, sample_seqs=[0, 5, 11, 15], clean=False, what="16x8192 vs oracle")
+
+
+def test_fused_bf16_next_n2_against_oracle():
+    case = workloads.decode_case(31, seq_lens=[4096, 3001, 8192, 129, 2], H=32, next_n=2,
+                                 dtype="bf16", spare_pages=2, width=8192 + 64, topk=2048)
+    _against_oracle(case, sample_seqs=[0, 1, 2, 3, 4], clean=True, what="bf16 next_n=2 vs oracle")
+
+
+def test_fused_f32_next_n4_against_oracle():
+    case = workloads.decode_case(32, seq_lens=[700, 64, 65, 3], H=64, next_n=4, dtype="f32",
+                                 spare_pages=1, width=768, topk=64)
+    _against_oracle(case, sample_seqs=[0, 1, 2, 3], clean=True, what="f32 next_n=4 vs oracle")
