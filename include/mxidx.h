@@ -279,6 +279,29 @@ int idx_topk_ws(const float* logits, int64_t rows, int64_t logits_row_stride,
                 const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* idx_topk_noalloc -- idx_topk_ws for callers that cannot allocate device
+ * memory: code under HIP graph capture that may not call hipMalloc, tight
+ * serving loops, harnesses that forbid allocation.  The same arguments,
+ * kernels and exact sets as idx_topk_ws, the workspace being the library's
+ * own static device array of IDX_TOPK_NOALLOC_MAX_WORKSPACE bytes (36 MiB, which
+ * holds the workspace of 64 rows of up to 131,072 columns) instead of a
+ * caller's buffer.  Each device holds its own copy of that array from the
+ * library's load until the process ends; its address is looked up once per
+ * device, on the first call there.  Nothing is allocated or freed per call.
+ *   Returns IDX_ERR_ARG (before any device work) when the call needs more
+ *   workspace than the array holds, i.e. when
+ *   idx_topk_workspace_bytes(rows, logits_row_stride) >
+ *   IDX_TOPK_NOALLOC_MAX_WORKSPACE.
+ *   Every call on a device shares that device's array, which keeps the last
+ *   call's contents (no call depends on them: each split call rewrites every
+ *   byte it reads).  Calls that may overlap on one device -- on different
+ *   streams, or from several host threads without ordering -- race on the
+ *   array and must not be issued. */
+#define IDX_TOPK_NOALLOC_MAX_WORKSPACE (36ll << 20)
+int idx_topk_noalloc(const float* logits, int64_t rows, int64_t logits_row_stride,
+                     const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
+                     hipStream_t stream);
+
 /* idx_topk_merge -- merge per-rank top-k lists into a sequence's top-k: the
  * exchange step of decode with the context split over `world` ranks (P3
  * "SparseAttnIndexerKpool": dcp_rank, dcp_world_size,

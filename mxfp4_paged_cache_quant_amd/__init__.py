@@ -16,7 +16,7 @@ __all__ = [
     "MxidxError", "lib", "lib_path", "version", "init",
     "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged",
     "logits_paged_insert", "topk", "topk_workspace_bytes", "topk_workspace", "topk_ws",
-    "topk_merge",
+    "topk_noalloc", "topk_merge", "TOPK_NOALLOC_MAX_WORKSPACE",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
 ]
 
@@ -27,6 +27,7 @@ ROW_BYTES = 68
 PAGE_SIZE = 64
 TOPK_MAX = 2048
 MAX_HEADS = 128
+TOPK_NOALLOC_MAX_WORKSPACE = 36 << 20
 
 IDX_BF16, IDX_F32 = 0, 1
 
@@ -61,6 +62,8 @@ EXPORTS = {
     "idx_topk_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "idx_topk_ws": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p,
                            ctypes.c_size_t, _c_void_p]),
+    "idx_topk_noalloc": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p,
+                                _c_void_p]),
     "idx_topk_merge": (_int, [_c_void_p, _c_void_p, _int, _i64, _int, _int, _int, _c_void_p,
                               _c_void_p]),
 }
@@ -439,6 +442,32 @@ def topk_ws(logits, ks, ke, k, workspace, out=None, stream=None):
         raise MxidxError("out must be a contiguous int32 [rows, k]")
     _check(lib().idx_topk_ws(_ptr(logits), rows, logits.stride(0), _ptr(ks), _ptr(ke), k, _ptr(out),
                              _ptr(workspace), workspace.numel(), _stream(stream)), "idx_topk_ws")
+    return out
+
+
+def topk_noalloc(logits, ks, ke, k, out=None, stream=None):
+    """topk_ws with the library's static device scratch instead of a caller's
+    workspace (no device allocation by the library; `out` is allocated here only
+    when it is not given).  Raises when the call needs more than
+    TOPK_NOALLOC_MAX_WORKSPACE bytes of workspace."""
+    torch = _torch()
+    _dev(logits, "logits", torch.float32)
+    _dev(ke, "ke", torch.int32)
+    if ks is not None:
+        _dev(ks, "ks", torch.int32)
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise MxidxError("logits must be 2-D with contiguous rows")
+    rows = logits.shape[0]
+    if ke.numel() != rows or not ke.is_contiguous() or \
+            (ks is not None and (ks.numel() != rows or not ks.is_contiguous())):
+        raise MxidxError("ks / ke must hold one entry per row")
+    if out is None:
+        out = torch.empty((rows, k), dtype=torch.int32, device=logits.device)
+    _dev(out, "out", torch.int32)
+    if not out.is_contiguous() or tuple(out.shape) != (rows, k):
+        raise MxidxError("out must be a contiguous int32 [rows, k]")
+    _check(lib().idx_topk_noalloc(_ptr(logits), rows, logits.stride(0), _ptr(ks), _ptr(ke), k,
+                                  _ptr(out), _stream(stream)), "idx_topk_noalloc")
     return out
 
 

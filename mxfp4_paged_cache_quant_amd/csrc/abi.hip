@@ -8,6 +8,9 @@
 #include "mxidx.h"
 #include "launch.hpp"
 
+static_assert(IDX_TOPK_NOALLOC_MAX_WORKSPACE == mxidx::kNoAllocScratchBytes,
+              "the header's scratch limit is the size of the library's scratch array");
+
 extern "C" int idx_arch_supported(const char* gcn_arch_name);
 
 namespace {
@@ -272,6 +275,22 @@ int idx_topk_ws(const float* logits, int64_t rows, int64_t logits_row_stride, co
   if (st != IDX_OK) return st;
   return launched(mxidx::launch_topk_ws(logits, rows, logits_row_stride, ks, ke, k, out_idx,
                                         workspace, stream));
+}
+
+int idx_topk_noalloc(const float* logits, int64_t rows, int64_t logits_row_stride,
+                     const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
+                     hipStream_t stream) {
+  if (rows < 0 || k < 1 || k > IDX_TOPK_MAX || logits_row_stride < 0 || rows > 0x7fffffffLL)
+    return IDX_ERR_ARG;
+  if (rows == 0) return IDX_OK;
+  if (!logits || !aligned(logits, 4) || !ke || !out_idx) return IDX_ERR_ARG;
+  // the library's scratch holds at most IDX_TOPK_NOALLOC_MAX_WORKSPACE bytes
+  if (idx_topk_workspace_bytes(rows, logits_row_stride) > (size_t)IDX_TOPK_NOALLOC_MAX_WORKSPACE)
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_topk_noalloc(logits, rows, logits_row_stride, ks, ke, k, out_idx,
+                                             stream));
 }
 
 }  // extern "C"

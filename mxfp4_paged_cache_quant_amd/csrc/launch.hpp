@@ -60,5 +60,10 @@ int64_t topk_workspace_bytes(int64_t rows, int64_t ld);
 hipError_t launch_topk_ws(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
                           const int32_t* ke, int k, int32_t* out_idx, void* workspace,
                           hipStream_t stream);
+// launch_topk_ws with the workspace in the library's static device array
+// (kNoAllocScratchBytes per device); hipErrorInvalidValue when the call needs more.
+constexpr int64_t kNoAllocScratchBytes = 36ll << 20;
+hipError_t launch_topk_noalloc(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
+                               const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream);
 
 }  // namespace mxidx

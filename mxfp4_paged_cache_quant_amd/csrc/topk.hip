@@ -37,6 +37,7 @@
 //     and compacts the bin's (key, column) pairs into LDS (up to 8192, else
 //     the remaining levels re-read the row filtered by the bin).
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -1338,6 +1339,41 @@ int split_parts(int64_t rows, int64_t ld) {
 
 }  // namespace
 
+// Scratch of the allocation-free entry point (launch_topk_noalloc): the split
+// top-k's workspace as a file-scope device array of kNoAllocScratchBytes.  Each
+// device that loads the library holds its own copy until the process ends.  In
+// host code `scratch` names a host-side stand-in, never the device memory: the
+// device address is taken once per device, with that device current, from
+// hipGetSymbolAddress and kept in g_scratch_ptr; only that address is passed to
+// kernels.
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+std::atomic<void*> g_scratch_ptr[kAttrDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (set up on the first call per device).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kAttrDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
 int64_t topk_workspace_bytes(int64_t rows, int64_t ld) {
   const int parts = split_parts(rows, ld);
   return parts ? SplitWs::bytes(rows, parts) : 0;
@@ -1394,6 +1430,19 @@ hipError_t launch_topk(const float* logits, int64_t rows, int64_t ld, const int3
   }
   if (ld <= 8 * 512) return launch_cfg<512, 8, 2048>(logits, rows, ld, ks, ke, k, out_idx, stream);
   return launch_cfg<512, 16, 2048>(logits, rows, ld, ks, ke, k, out_idx, stream);
+}
+
+hipError_t launch_topk_noalloc(const float* logits, int64_t rows, int64_t ld, const int32_t* ks,
+                               const int32_t* ke, int k, int32_t* out_idx, hipStream_t stream) {
+  if (topk_workspace_bytes(rows, ld) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  if (split_parts(rows, ld)) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+  }
+  // the split workspace needs no initialization: every header and pair the
+  // merge reads is written by the part launch of the same call
+  return launch_topk_ws(logits, rows, ld, ks, ke, k, out_idx, ws, stream);
 }
 
 }  // namespace mxidx

@@ -212,3 +212,19 @@ def test_prefill_key_count_limit(L):
     assert L.idx_logits_prefill(P, P, P, P, P, P, P, 0, 32, lim, P, lim, 1, None) == OK
     assert L.idx_logits_prefill(P, P, P, P, P, P, P, 0, 32, lim + 1, P, lim + 1, 1, None) == ERR_ARG
     assert L.idx_logits_prefill(P, P, P, P, P, P, P, 4, 32, lim + 1, P, lim + 1, 1, None) == ERR_ARG
+
+
+def test_topk_noalloc_argument_validation(L):
+    f = L.idx_topk_noalloc
+    assert f(P, 4, 64, None, P, 0, P2, None) == ERR_ARG                 # k = 0
+    assert f(P, 4, 64, None, P, 2049, P2, None) == ERR_ARG              # k > 2048
+    assert f(MIS, 4, 64, None, P, 8, P2, None) == ERR_ARG               # misaligned logits
+    assert f(P, 4, 64, None, None, 8, P2, None) == ERR_ARG              # null ke
+    assert f(None, 0, 64, None, None, 8, None, None) == OK              # no rows: no-op
+    # more workspace than the library's scratch holds: rejected on the host
+    assert L.idx_topk_workspace_bytes(64, 8192 * 64) > mx.TOPK_NOALLOC_MAX_WORKSPACE
+    assert f(P, 64, 8192 * 64, None, P, 2048, P2, None) == ERR_ARG
+    # the long-context decode shape fits (it stops at the device gate here)
+    assert 0 < L.idx_topk_workspace_bytes(64, 131072) <= mx.TOPK_NOALLOC_MAX_WORKSPACE
+    if not _has_gpu():
+        assert f(P, 64, 131072, None, P, 2048, P2, None) == ERR_NO_DEVICE
