@@ -151,11 +151,13 @@ def capture(fn_list):
     return g
 
 
-def time_graph(g, reps, batches=5, warm_ms=25.0):
+def time_graph(g, reps, batches=9, warm_ms=25.0, spread=None):
     """ms per replay: the median over `batches` batches of `reps` replays, timed with
     HIP events on the current stream, after untimed replays for at least warm_ms
     (the clocks settle after a light section; a single warm-up replay left the
-    first batches of a heavy kernel up to 20% slow)."""
+    first batches of a heavy kernel up to 20% slow).  With a dict `spread`, the
+    10th and 90th percentiles of the batch times are stored there."""
+    import numpy as np
     import statistics
     import torch
     start = torch.cuda.Event(enable_timing=True)
@@ -173,6 +175,8 @@ def time_graph(g, reps, batches=5, warm_ms=25.0):
         stop.record()
         stop.synchronize()
         times.append(start.elapsed_time(stop) / reps)
+    if spread is not None:
+        spread["p10"], spread["p90"] = (float(v) for v in np.percentile(times, [10, 90]))
     return statistics.median(times)
 
 
@@ -180,21 +184,28 @@ def bench_decode(args, case, sets, order):
     import torch
     ops = decode_ops(case)
 
-    def step_fns(lo, hi):
-        return [(lambda s=s, name=name: ops[name](s)) for s in sets[lo:hi] for name in order]
+    G = len(sets)
+    wfull, wrem = divmod(args.warmup, G)
+    # the timed steps start at the set after the warm-up's last one, so that no
+    # timed set has been touched since the others evicted it from the MALL
+    # (with fewer steps than sets, every timed set is one the warm-up skipped)
+    timed = sets[wrem:] + sets[:wrem]
+
+    def step_fns(pool, lo, hi):
+        return [(lambda s=s, name=name: ops[name](s)) for s in pool[lo:hi] for name in order]
 
     # eager warm-up of every call (also runs the architecture gate outside capture)
-    for fn in step_fns(0, 1):
+    # on the set the warm-up replays end with
+    for fn in step_fns(sets, max(wrem - 1, 0), max(wrem, 1)):
         fn()
     torch.cuda.synchronize()
-    G = len(sets)
-    g_full = capture(step_fns(0, G))
+    g_full = capture(step_fns(timed, 0, G))
     rem = args.steps % G
-    g_rem = capture(step_fns(0, rem)) if rem else None
-    wfull, wrem = divmod(args.warmup, G)
-    g_wrem = capture(step_fns(0, wrem)) if wrem else None
+    g_rem = capture(step_fns(timed, 0, rem)) if rem else None
+    g_wrem = capture(step_fns(sets, 0, wrem)) if wrem else None
+    g_wfull = capture(step_fns(sets, 0, G)) if wfull else None
     for _ in range(wfull):
-        g_full.replay()
+        g_wfull.replay()
     if g_wrem is not None:
         g_wrem.replay()
     torch.cuda.synchronize()
@@ -208,12 +219,17 @@ def bench_decode(args, case, sets, order):
     elapsed = time.perf_counter() - t0
 
     # per-kernel average durations: a graph of G back-to-back launches of one kernel
-    per_kernel = {}
+    per_kernel, spread = {}, {}
     for name in order:
         g = capture([(lambda s=s: ops[name](s)) for s in sets])
-        per_kernel[name] = time_graph(g, args.kernel_reps) / G * 1e3     # us per launch
+        sp = {}
+        per_kernel[name] = time_graph(g, args.kernel_reps, spread=sp) / G * 1e3     # us per launch
+        spread[name] = {k: round(v / G * 1e3, 3) for k, v in sp.items()}
         del g
-    return elapsed, per_kernel
+    return elapsed, per_kernel, spread
+
+
+CASES = {}            # workloads built by the GPU sections, reused by the oracle's legs
 
 
 def bench_prefill(args):
@@ -222,6 +238,7 @@ def bench_prefill(args):
     import mxfp4_paged_cache_quant_amd as mx
     import workloads
     case = workloads.prefill_chunk()
+    CASES["prefill_chunk"] = case
     T, S, H = case["T"], case["S"], case["H"]
     cache = torch.zeros((case["num_pages"], 64 * 68), dtype=torch.uint8, device="cuda")
     k, slots, q, w = dev(case["k"]), dev(case["slot_mapping"]), dev(case["q"]), dev(case["w"])
@@ -244,10 +261,9 @@ def bench_prefill(args):
     for fn in ops.values():
         fn()
     torch.cuda.synchronize()
-    per = {}
+    per, spread = {}, {}
     for name, fn in ops.items():
-        g = capture([fn] * 4)
-        per[name] = time_graph(g, 10) / 4 * 1e3
+        per[name] = time_fn(fn, 10, 4, spread, name)
     step_us = sum(per.values())
     pairs = int(np.sum(case["ke"].astype(np.int64) - case["ks"]))
     flops = 2.0 * H * 128 * pairs
@@ -259,13 +275,18 @@ def bench_prefill(args):
         "logits_frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
         "step_us": round(step_us, 2),
         "kernels_us": {k2: round(v, 2) for k2, v in per.items()},
+        "kernels_p10_p90_us": spread,
     }
 
 
-def time_fn(fn, reps, per_graph=4):
-    """Average us per call of fn, from a graph of per_graph back-to-back calls."""
+def time_fn(fn, reps, per_graph=4, spread=None, key=None):
+    """Average us per call of fn, from a graph of per_graph back-to-back calls;
+    with a dict `spread`, its p10/p90 (us) go there under `key`."""
     g = capture([fn] * per_graph)
-    t = time_graph(g, reps) / per_graph * 1e3
+    sp = {}
+    t = time_graph(g, reps, spread=sp) / per_graph * 1e3
+    if spread is not None:
+        spread[key] = [round(sp["p10"] / per_graph * 1e3, 2), round(sp["p90"] / per_graph * 1e3, 2)]
     del g
     return t
 
@@ -302,10 +323,11 @@ def bench_long_decode():
     for fn in (ins, *extra, lg, tk):
         fn()
     torch.cuda.synchronize()
-    t_ins = time_fn(ins, 5, 2)
+    spread = {}
+    t_ins = time_fn(ins, 5, 2, spread, "insert")
     t_lgc = None if EAGER else time_fn(lg_clean, 10, 4)
-    t_lg = time_fn(lg, 10, 4)
-    t_tk = time_fn(tk, 10, 4)
+    t_lg = time_fn(lg, 10, 4, spread, "logits_paged")
+    t_tk = time_fn(tk, 10, 4, spread, "topk")
     t_tk_row = None if EAGER else time_fn(tk_row, 10, 4)
     # multi-token decode (next_n = 2): the same cache, two query rows per sequence
     # (seeded N(0,1) bf16 q drawn on the device); rows see L-1 and L tokens
@@ -348,6 +370,7 @@ def bench_long_decode():
                                       / ((t_lg + t_tk) * 1e3) / HBM_PEAK_GBS, 4),
         "decode_step_us": round(t_lg + t_tk, 1),
         "scored_tokens_per_s": round(N / ((t_lg + t_tk) * 1e-6), 1),
+        "p10_p90_us": spread,
     }
 
 
@@ -358,6 +381,7 @@ def bench_long_prefill():
     import mxfp4_paged_cache_quant_amd as mx
     import workloads
     case = workloads.long_prefill()
+    CASES["long_prefill"] = case
     T, S, H = case["T"], case["S"], case["H"]
     cache = torch.zeros((case["num_pages"], 64 * 68), dtype=torch.uint8, device="cuda")
     mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
@@ -372,8 +396,9 @@ def bench_long_prefill():
     lg()
     tk()
     torch.cuda.synchronize()
-    t_lg = time_fn(lg, 3, 2)
-    t_tk = time_fn(tk, 3, 2)
+    spread = {}
+    t_lg = time_fn(lg, 3, 2, spread, "logits_prefill")
+    t_tk = time_fn(tk, 3, 2, spread, "topk")
     pairs = int(np.sum(case["ke"].astype(np.int64) - case["ks"]))
     flops = 2.0 * H * 128 * pairs
     tflops = flops / (t_lg * 1e-6) / 1e12
@@ -382,6 +407,7 @@ def bench_long_prefill():
         "logits_us": round(t_lg, 1), "logits_tflops": round(tflops, 1),
         "logits_frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
         "topk_us": round(t_tk, 1), "topk_gbs": round((pairs * 4 + T * case["topk"] * 4) / t_tk / 1e3, 1),
+        "p10_p90_us": spread,
     }
 
 
@@ -415,15 +441,47 @@ def bench_copy(nbytes=1 << 30, reps=5):
             "read_only_sum_us": round(us_r, 1), "read_only_gbs": round(nbytes / us_r / 1e3, 1)}
 
 
-def cpu_baseline(case, seconds):
-    """The oracle (never tuned for this) on a bounded sample of the decode step."""
-    import numpy as np
-    from oracle import logits as olog, mxfp4 as omx, paged_cache as opc, topk as otk
+def host_info():
+    """The host CPU the oracle runs on: model, logical CPUs this process may use,
+    physical cores, and the BLAS threads the oracle's matrix products use."""
+    model, phys = None, set()
+    try:
+        cur = {}
+        for line in open("/proc/cpuinfo"):
+            if ":" not in line:
+                if cur:
+                    phys.add((cur.get("physical id"), cur.get("core id")))
+                cur = {}
+                continue
+            key, val = (x.strip() for x in line.split(":", 1))
+            cur[key] = val
+            if key == "model name" and model is None:
+                model = val
+        if cur:
+            phys.add((cur.get("physical id"), cur.get("core id")))
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        logical = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        logical = os.cpu_count()
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        threads = logical
+    return {"cpu_model": model, "logical_cpus_available": logical,
+            "physical_cores_on_host": len(phys) or None, "blas_threads": int(threads)}
+
+
+def cpu_baseline(case, seconds, prefill_case=None, long_prefill_case=None):
+    """The oracle (never tuned for this) on bounded samples: decode steps of the
+    16 x 8192 workload (the headline metric), sampled query rows of the 8192
+    prefill chunk and the 256 sampled rows of the long prefill (throughput and
+    extrapolated totals, labelled as such)."""
+    import numpy as np
+    from oracle import logits as olog, mxfp4 as omx, paged_cache as opc, topk as otk
+    host = host_info()
     B = len(case["context_lens"])
     H = case["H"]
     cache = np.zeros((case["num_pages"], 64 * 68), np.uint8)
@@ -445,11 +503,49 @@ def cpu_baseline(case, seconds):
         scored += L
         seqs_done += 1
         b = (b + 1) % B
-    return {"value": scored / t_total, "unit": "scored cache tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{seqs_done} single-sequence decode steps (new-token insert, q quantize, "
-                      f"paged logits over 8192 tokens, top-2048) of the 16x8192 workload, "
-                      f"{t_total:.1f} s of CPU time"}
+    out = {"value": scored / t_total, "unit": "scored cache tokens/s", "cores": host["blas_threads"],
+           "kind": "oracle",
+           "sample": f"{seqs_done} single-sequence decode steps (new-token insert, q quantize, "
+                     f"paged logits over 8192 tokens, top-2048) of the 16x8192 workload, "
+                     f"{t_total:.1f} s of CPU time; the oracle's insert returns a new copy of the "
+                     f"8.9 MB cache at every step (its plain form), which is included",
+           "host": host}
+
+    def prefill_leg(pc, rows, label):
+        # K side in full (insert + gather of every token), query side on `rows`
+        t0 = time.perf_counter()
+        c = opc.insert(np.zeros((pc["num_pages"], 64 * 68), np.uint8),
+                       omx.bf16_bits_to_f64(pc["k"]), pc["slot_mapping"])
+        kc, kscale = opc.gather(c, pc["block_table"], pc["seq_lens"], pc["cu_seq_offsets"], pc["S"])
+        t_k = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        Hp = pc["H"]
+        qc, qsc = omx.quantize_rows(omx.bf16_bits_to_f64(pc["q"][rows]))
+        ref = olog.mqa_logits(qc.reshape(-1, Hp, 64), qsc.reshape(-1, Hp, 4), kc, kscale,
+                              pc["w"][rows], pc["ks"][rows], pc["ke"][rows], chunk=16)
+        otk.top_k_per_row(ref.astype(np.float32), pc["ks"][rows], pc["ke"][rows], pc["topk"])
+        t_q = time.perf_counter() - t0
+        pairs_s = int(np.sum(pc["ke"][rows].astype(np.int64) - pc["ks"][rows]))
+        pairs = int(np.sum(pc["ke"].astype(np.int64) - pc["ks"]))
+        est = t_k + t_q * pairs / pairs_s
+        return {"sample": label, "k_side_s": round(t_k, 2), "sampled_rows_s": round(t_q, 2),
+                "sampled_pairs": pairs_s, "pairs_per_s": round(pairs_s / t_q, 1),
+                "logits_tflops": round(2.0 * Hp * 128 * pairs_s / t_q / 1e12, 4),
+                "extrapolated_full_s": round(est, 1), "extrapolated": True}
+
+    if prefill_case is not None:
+        rows = np.arange(0, prefill_case["T"], 16)
+        out["prefill_chunk"] = prefill_leg(
+            prefill_case, rows, f"insert + gather of all 8192 tokens, then q quantize, logits and "
+                                f"top-2048 of {len(rows)} query rows (every 16th) of the 8192 causal "
+                                f"chunk; the full chunk's time extrapolated by causal pairs")
+    if long_prefill_case is not None:
+        rows = np.asarray(long_prefill_case["sample_rows"])
+        out["long_prefill"] = prefill_leg(
+            long_prefill_case, rows, f"insert + gather of all 122880 tokens, then q quantize, logits "
+                                     f"and top-2048 of the {len(rows)} sampled query rows; the full "
+                                     f"16384-row time extrapolated by causal pairs")
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -574,8 +670,9 @@ def main():
     case = workloads.paged_decode()
     log(f"[bench] decode workload {case['name']}: building {args.sets} rotating sets")
     sets = build_decode_sets(case, args.sets)
-    elapsed, per_kernel = bench_decode(args, case, sets, ["logits_paged_insert", "topk"])
-    sep_elapsed, sep_kernel = bench_decode(args, case, sets, ["insert_quantize", "logits_paged", "topk"])
+    elapsed, per_kernel, per_spread = bench_decode(args, case, sets, ["logits_paged_insert", "topk"])
+    sep_elapsed, sep_kernel, _ = bench_decode(args, case, sets,
+                                              ["insert_quantize", "logits_paged", "topk"])
     del sets
     ms_per_step = elapsed / args.steps * 1e3
     scored = int(np.sum(case["context_lens"]))
@@ -600,7 +697,8 @@ def main():
                 "traffic": measured_traffic("decode", dom_kernel),
                 "alg_bytes_per_launch": alg_bytes[dominant],
                 "avg_launch_us": round(per_kernel[dominant], 3)}
-    kernels = {k: {"avg_us": round(v, 3), "alg_bytes": alg_bytes[k],
+    kernels = {k: {"avg_us": round(v, 3), "p10_us": per_spread[k]["p10"], "p90_us": per_spread[k]["p90"],
+                   "alg_bytes": alg_bytes[k],
                    "gbs": round(alg_bytes[k] / (v * 1e-6) / 1e9, 1)} for k, v in per_kernel.items()}
     separate = {"step": "insert_quantize+logits_paged+topk",
                 "us_per_step": round(sep_elapsed / args.steps * 1e6, 3),
@@ -635,7 +733,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        cpu = cpu_baseline(case, args.cpu_seconds)
+        cpu = cpu_baseline(case, args.cpu_seconds, CASES.get("prefill_chunk"),
+                           CASES.get("long_prefill"))
 
     out = {
         "metric": "scored cache tokens/sec (paged decode) + prefill logits TFLOP/s, % of roofline",
