@@ -53,6 +53,13 @@ independently of its code.  Function -> pin (test file):
 * topk.kth_value -- a plain Python sort (test_oracle_tolerance)
 * tolerance.logits_close, tolerance.topk_end_to_end_ok -- exact boundary
   cases and hand-worked rows (test_oracle_tolerance)
+* fp8.e4m3_value / e4m3_encode / scale_exponent / row_scales / quantize_rows /
+  fold_weights -- the OCP E4M3 table and hand-worked rows
+  (tests/golden/fp8_e4m3.txt), brute-force nearest values over every bf16
+  pattern and every midpoint, exact rational fp32 rounding (test_oracle_fp8)
+* fp8.write_rows / insert / gather -- hand-worked 132-byte offsets, canaries,
+  slot -1, round trip; fp8.mqa_logits / paged_mqa_logits -- exact rational
+  arithmetic, a closed form, 2**m scaling, paged == dense (test_oracle_fp8)
 
 The pins of the comparison rules and of A are also run against copies of the
 functions with one planted mistake each, and must reject every copy.  The
@@ -61,4 +68,4 @@ of zero, scale byte order) are pinned by the hand-worked bytes derived from the
 adopted reading.
 """
 
-from . import mxfp4, paged_cache, logits, topk, tolerance  # noqa: F401
+from . import mxfp4, paged_cache, logits, topk, tolerance, fp8  # noqa: F401
