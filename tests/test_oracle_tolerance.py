@@ -143,13 +143,14 @@ def test_logits_close_pins():
 
 
 def test_logits_close_fp8_factor():
-    # the FP8 rule's factor 2**-16: A = 2**16 gives a tolerance of exactly 1
-    assert tolerance.ABS_FACTOR_FP8 == 2.0 ** -16
+    # the FP8 rule's factor 2**-15: A = 2**15 gives a tolerance of exactly 1
+    assert tolerance.ABS_FACTOR_FP8 == 2.0 ** -15
     f = tolerance.logits_close
-    assert f([1.0], [0.0], [2.0 ** 16], abs_factor=tolerance.ABS_FACTOR_FP8)[0]
-    assert not f([_next_up(1.0)], [0.0], [2.0 ** 16], abs_factor=tolerance.ABS_FACTOR_FP8)[0]
-    # (257 roundings of 2**-24 each stay below the factor)
-    assert 257 * 2.0 ** -24 < tolerance.ABS_FACTOR_FP8
+    assert f([1.0], [0.0], [2.0 ** 15], abs_factor=tolerance.ABS_FACTOR_FP8)[0]
+    assert not f([_next_up(1.0)], [0.0], [2.0 ** 15], abs_factor=tolerance.ABS_FACTOR_FP8)[0]
+    # the first-order rounding count of the derivation (127 + 131 + 1 roundings of
+    # 2**-24) stays below the factor
+    assert (127 + 131 + 1) * 2.0 ** -24 < tolerance.ABS_FACTOR_FP8
 
 
 @pytest.mark.parametrize("mutant", [_lc_strict, _lc_rel_on_gpu, _lc_no_bound, _lc_wide_factor,
