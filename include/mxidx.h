@@ -12,6 +12,8 @@
  *   idx_topk            per-row top-k column indices over [ks, ke)
  *   idx_topk_ws         the same with a workspace: few long rows split over
  *                       workgroups
+ *   idx_*_fp8           the FP8 (E4M3) indexer cache the MXFP4 one replaces:
+ *                       quantize, insert, gather, dense and paged logits
  *
  * Sources: P1 = "[Kernel] MXFP4 indexer cache for GLM-5.2 / DSA (glm_moe_dsa)"
  * (vLLM pull request 48558); P2 = "Enable SM86 MXFP4 sparse-indexer cache"
@@ -239,6 +241,74 @@ int idx_logits_paged_insert(const void* q, const void* k_new, int dtype, const f
                             const int32_t* context_lens, int B, int next_n, int H,
                             int64_t max_context_len, float* logits, int64_t logits_row_stride,
                             int clean, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * FP8 indexer cache: the format the MXFP4 cache replaces (P1 "Benefit": 132
+ * bytes per token per head against 68), with the same calls.
+ *
+ * FP8 row (132 bytes): 128 OCP E4M3 values (bias 7, largest finite 448, no
+ * infinities) and one little-endian fp32 scale.  Encode rule: s = amax / 448
+ * rounded to fp32, floored at 2^-126 (IDX_FP8_SCALE_F32), or s = 2^E with E the
+ * smallest integer such that amax <= 448 * 2^E, clamped to [-126, 127]
+ * (IDX_FP8_SCALE_POW2, the power-of-two "round_scale" of P3
+ * "_kpool_compress_insert"); each element is x / s rounded to fp32, then to the
+ * nearest E4M3 value, ties to the even code; the sign bit is kept.
+ * Page (block-split, as the MXFP4 page copies it; P1 live-validation comment):
+ * the page_size value rows (128 B each) in token order, then the page_size
+ * scale words (4 B each).  Slot s = page * page_size + offset.
+ * FP8 q is a single tensor whose per-row scale is folded into the head weights
+ * (P3 "forward_cuda"): the logits take w' = w * s_q.  Logits:
+ *   logits[t, s] = s_k[s] * sum_h w'[t,h] * max(0, q8[t,h] . k8[s])
+ * with q8, k8 the E4M3 values, fp32 accumulation.
+ * ------------------------------------------------------------------------- */
+typedef enum { IDX_FP8_SCALE_F32 = 0, IDX_FP8_SCALE_POW2 = 1 } idx_fp8_scale;
+#define IDX_FP8_ROW_BYTES 132
+
+/* idx_quantize_fp8 -- FP8-encode `rows` rows of 128 values (the FP8 query).
+ *   x, dtype, rows, row_stride: as for idx_quantize.
+ *   scale_fmt: IDX_FP8_SCALE_F32 or IDX_FP8_SCALE_POW2.
+ *   values: [rows, 128] uint8 out (16-byte aligned);  scales: [rows] fp32 out.
+ *   w_in, w_out: both NULL, or both [rows] fp32: w_out[r] = w_in[r] * scales[r]
+ *   (one fp32 product), the folded weights for a query whose rows are
+ *   [T, H, 128] and weights [T, H] (w_out may alias w_in). */
+int idx_quantize_fp8(const void* x, int dtype, int64_t rows, int64_t row_stride, int scale_fmt,
+                     uint8_t* values, float* scales, const float* w_in, float* w_out,
+                     hipStream_t stream);
+
+/* idx_insert_fp8 -- quantize K rows to FP8 and scatter them into the FP8 paged
+ * cache [num_pages, page_size * 132] (the indexer K quant-and-cache of the FP8
+ * format); slots as for idx_insert (negative or out-of-range slots write
+ * nothing).  page_size must be 64; the cache 16-byte aligned. */
+int idx_insert_fp8(const void* k, int dtype, int64_t num_tokens, int64_t k_row_stride,
+                   int scale_fmt, const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
+                   int page_size, hipStream_t stream);
+
+/* idx_gather_fp8 -- FP8 paged cache -> contiguous k_values [total_tokens, 128]
+ * uint8 and k_scales [total_tokens] fp32; addressing and skipping as for
+ * idx_gather. */
+int idx_gather_fp8(const uint8_t* cache, int64_t num_pages, int page_size,
+                   const int32_t* block_table, int64_t bt_row_stride, const int32_t* seq_lens,
+                   const int64_t* cu_seq_offsets, int batch, int64_t max_seq_len,
+                   int64_t total_tokens, uint8_t* k_values, float* k_scales, hipStream_t stream);
+
+/* idx_logits_prefill_fp8 -- dense FP8 logits (mqa_logits on the FP8 format):
+ *   q_values [T, H, 128] (idx_quantize_fp8 output), weights [T, H] fp32 holding
+ *   w' (the query scales folded in), k_values [S, 128], k_scales [S] fp32;
+ *   ks, ke, T, H, S, logits, logits_row_stride, clean: as for idx_logits_prefill. */
+int idx_logits_prefill_fp8(const uint8_t* q_values, const float* weights, const uint8_t* k_values,
+                           const float* k_scales, const int32_t* ks, const int32_t* ke, int64_t T,
+                           int H, int64_t S, float* logits, int64_t logits_row_stride, int clean,
+                           hipStream_t stream);
+
+/* idx_logits_paged_fp8 -- paged FP8 decode logits (paged_mqa_logits on the FP8
+ * format): q_values [B*next_n, H, 128], weights [B*next_n, H] fp32 (w'), the FP8
+ * cache; every other argument, the visibility rule and the error behaviour
+ * are those of idx_logits_paged. */
+int idx_logits_paged_fp8(const uint8_t* q_values, const float* weights, const uint8_t* cache,
+                         int64_t num_pages, int page_size, const int32_t* block_table,
+                         int64_t bt_row_stride, const int32_t* context_lens, int B, int next_n,
+                         int H, int64_t max_context_len, float* logits, int64_t logits_row_stride,
+                         int clean, hipStream_t stream);
 
 /* idx_topk -- per-row top-k column indices (top_k_per_row, P3
  * "SparseAttnIndexerKpool"; exact sets as tested in P2 "Validation").

@@ -17,6 +17,8 @@ __all__ = [
     "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged",
     "logits_paged_insert", "topk", "topk_workspace_bytes", "topk_workspace", "topk_ws",
     "topk_noalloc", "topk_merge", "TOPK_NOALLOC_MAX_WORKSPACE",
+    "quantize_fp8", "insert_fp8", "gather_fp8", "logits_prefill_fp8", "logits_paged_fp8",
+    "FP8_ROW_BYTES", "FP8_SCALE_F32", "FP8_SCALE_POW2",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
 ]
 
@@ -28,6 +30,8 @@ PAGE_SIZE = 64
 TOPK_MAX = 2048
 MAX_HEADS = 128
 TOPK_NOALLOC_MAX_WORKSPACE = 36 << 20
+FP8_ROW_BYTES = 132
+FP8_SCALE_F32, FP8_SCALE_POW2 = 0, 1
 
 IDX_BF16, IDX_F32 = 0, 1
 
@@ -58,6 +62,18 @@ EXPORTS = {
     "idx_logits_paged_insert": (_int, [_c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _i64, _int,
                                        _c_void_p, _i64, _c_void_p, _int, _int, _int, _i64,
                                        _c_void_p, _i64, _int, _c_void_p]),
+    "idx_quantize_fp8": (_int, [_c_void_p, _int, _i64, _i64, _int, _c_void_p, _c_void_p, _c_void_p,
+                                _c_void_p, _c_void_p]),
+    "idx_insert_fp8": (_int, [_c_void_p, _int, _i64, _i64, _int, _c_void_p, _c_void_p, _i64, _int,
+                              _c_void_p]),
+    "idx_gather_fp8": (_int, [_c_void_p, _i64, _int, _c_void_p, _i64, _c_void_p, _c_void_p, _int,
+                              _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "idx_logits_prefill_fp8": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                      _c_void_p, _i64, _int, _i64, _c_void_p, _i64, _int,
+                                      _c_void_p]),
+    "idx_logits_paged_fp8": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _int, _c_void_p, _i64,
+                                    _c_void_p, _int, _int, _int, _i64, _c_void_p, _i64, _int,
+                                    _c_void_p]),
     "idx_topk": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p]),
     "idx_topk_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "idx_topk_ws": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p,
@@ -443,6 +459,167 @@ def topk_ws(logits, ks, ke, k, workspace, out=None, stream=None):
     _check(lib().idx_topk_ws(_ptr(logits), rows, logits.stride(0), _ptr(ks), _ptr(ke), k, _ptr(out),
                              _ptr(workspace), workspace.numel(), _stream(stream)), "idx_topk_ws")
     return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) indexer cache: 128 E4M3 values + an fp32 scale per row
+# ---------------------------------------------------------------------------
+
+def _fp8_cache_pages(cache):
+    torch = _torch()
+    _dev(cache, "cache", torch.uint8)
+    if not cache.is_contiguous() or cache.numel() % (PAGE_SIZE * FP8_ROW_BYTES) != 0:
+        raise MxidxError("cache must be a contiguous uint8 [num_pages, 64*132]")
+    return cache.numel() // (PAGE_SIZE * FP8_ROW_BYTES)
+
+
+def quantize_fp8(x, round_scale=False, weights=None, values=None, scales=None, weights_out=None,
+                 stream=None):
+    """FP8-encode rows of 128 values: returns (values u8 [..., 128], scales f32 [...]) and,
+    with ``weights`` (one fp32 per row, e.g. [T, H] for q [T, H, 128]), also the folded
+    weights w' = weights * scales as a third result."""
+    torch = _torch()
+    rows, stride, code = _rows_view(x, "x")
+    lead = tuple(x.shape[:-1])
+    if values is None:
+        values = torch.empty(lead + (HEAD_DIM,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead, dtype=torch.float32, device=x.device)
+    _dev(values, "values", torch.uint8)
+    _dev(scales, "scales", torch.float32)
+    if values.numel() != rows * HEAD_DIM or scales.numel() != rows or \
+            not values.is_contiguous() or not scales.is_contiguous():
+        raise MxidxError("values/scales must be contiguous [rows, 128] / [rows]")
+    if weights is not None:
+        _dev(weights, "weights", torch.float32)
+        if weights.numel() != rows or not weights.is_contiguous():
+            raise MxidxError("weights must be a contiguous fp32 tensor with one entry per row")
+        if weights_out is None:
+            weights_out = torch.empty_like(weights)
+        _dev(weights_out, "weights_out", torch.float32)
+        if weights_out.numel() != rows or not weights_out.is_contiguous():
+            raise MxidxError("weights_out must be a contiguous fp32 tensor with one entry per row")
+    fmt = FP8_SCALE_POW2 if round_scale else FP8_SCALE_F32
+    _check(lib().idx_quantize_fp8(_ptr(x), code, rows, stride, fmt, _ptr(values), _ptr(scales),
+                                  _ptr(weights), _ptr(weights_out), _stream(stream)),
+           "idx_quantize_fp8")
+    return (values, scales) if weights is None else (values, scales, weights_out)
+
+
+def insert_fp8(k, slot_mapping, cache, round_scale=False, stream=None):
+    """FP8-encode K rows [N, 128] into ``cache`` [num_pages, 64*132] (in place)."""
+    torch = _torch()
+    rows, stride, code = _rows_view(k, "k")
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    if slot_mapping.numel() != rows or not slot_mapping.is_contiguous():
+        raise MxidxError("slot_mapping must be a contiguous int64 [N]")
+    num_pages = _fp8_cache_pages(cache)
+    fmt = FP8_SCALE_POW2 if round_scale else FP8_SCALE_F32
+    _check(lib().idx_insert_fp8(_ptr(k), code, rows, stride, fmt, _ptr(slot_mapping), _ptr(cache),
+                                num_pages, PAGE_SIZE, _stream(stream)), "idx_insert_fp8")
+    return cache
+
+
+def gather_fp8(cache, block_table, seq_lens, cu_seq_offsets, max_seq_len, total_tokens,
+               k_values=None, k_scales=None, stream=None):
+    """FP8 paged cache -> contiguous (k_values u8 [total, 128], k_scales f32 [total])."""
+    torch = _torch()
+    num_pages = _fp8_cache_pages(cache)
+    _dev(block_table, "block_table", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32)
+    _dev(cu_seq_offsets, "cu_seq_offsets", torch.int64)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise MxidxError("block_table must be [batch, pages] with unit inner stride")
+    batch = block_table.shape[0]
+    if seq_lens.numel() != batch or cu_seq_offsets.numel() != batch:
+        raise MxidxError("seq_lens / cu_seq_offsets must have one entry per sequence")
+    if block_table.shape[1] * PAGE_SIZE < max_seq_len:
+        raise MxidxError("block_table has fewer pages than max_seq_len needs")
+    if k_values is None:
+        k_values = torch.zeros((total_tokens, HEAD_DIM), dtype=torch.uint8, device=cache.device)
+    if k_scales is None:
+        k_scales = torch.zeros((total_tokens,), dtype=torch.float32, device=cache.device)
+    _dev(k_values, "k_values", torch.uint8)
+    _dev(k_scales, "k_scales", torch.float32)
+    if not k_values.is_contiguous() or k_values.numel() < total_tokens * HEAD_DIM or \
+            not k_scales.is_contiguous() or k_scales.numel() < total_tokens:
+        raise MxidxError("k_values / k_scales must be contiguous [total, 128] uint8 / [total] fp32")
+    _check(lib().idx_gather_fp8(_ptr(cache), num_pages, PAGE_SIZE, _ptr(block_table),
+                                block_table.stride(0), _ptr(seq_lens), _ptr(cu_seq_offsets), batch,
+                                int(max_seq_len), int(total_tokens), _ptr(k_values), _ptr(k_scales),
+                                _stream(stream)), "idx_gather_fp8")
+    return k_values, k_scales
+
+
+def logits_prefill_fp8(q_values, weights, k_values, k_scales, ks, ke, logits=None, clean=True,
+                       stream=None):
+    """Dense FP8 logits [T, S]: q_values u8 [T, H, 128], weights f32 [T, H] (the folded w'),
+    k_values u8 [S, 128], k_scales f32 [S]."""
+    torch = _torch()
+    T, H = q_values.shape[0], q_values.shape[1]
+    S = k_values.shape[0]
+    for name, t, dt in (("q_values", q_values, torch.uint8), ("weights", weights, torch.float32),
+                        ("k_values", k_values, torch.uint8), ("k_scales", k_scales, torch.float32),
+                        ("ke", ke, torch.int32)):
+        _dev(t, name, dt)
+        if not t.is_contiguous():
+            raise MxidxError(f"{name} must be contiguous")
+    if ks is not None:
+        _dev(ks, "ks", torch.int32)
+    if tuple(q_values.shape) != (T, H, HEAD_DIM) or tuple(weights.shape) != (T, H) or \
+            tuple(k_values.shape) != (S, HEAD_DIM) or tuple(k_scales.shape) != (S,):
+        raise MxidxError("shape mismatch among q/k/weights")
+    if ke.numel() != T or (ks is not None and (ks.numel() != T or not ks.is_contiguous())):
+        raise MxidxError("ks / ke must hold one entry per query row")
+    if logits is None:
+        fill = float("-inf") if clean else 0.0
+        logits = torch.full((T, S), fill, dtype=torch.float32, device=q_values.device)
+    _dev(logits, "logits", torch.float32)
+    if logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] < T or logits.shape[1] < S:
+        raise MxidxError("logits must be [>=T, >=S] with contiguous rows")
+    _check(lib().idx_logits_prefill_fp8(_ptr(q_values), _ptr(weights), _ptr(k_values),
+                                        _ptr(k_scales), _ptr(ks), _ptr(ke), T, H, S, _ptr(logits),
+                                        logits.stride(0), 1 if clean else 0, _stream(stream)),
+           "idx_logits_prefill_fp8")
+    return logits
+
+
+def logits_paged_fp8(q_values, weights, cache, block_table, context_lens, next_n,
+                     max_context_len, logits=None, clean=True, stream=None):
+    """Paged FP8 decode logits [B*next_n, max_context_len]: q_values u8 [B*next_n, H, 128],
+    weights f32 [B*next_n, H] (the folded w')."""
+    torch = _torch()
+    R, H = q_values.shape[0], q_values.shape[1]
+    B = context_lens.numel()
+    num_pages = _fp8_cache_pages(cache)
+    for name, t, dt in (("q_values", q_values, torch.uint8), ("weights", weights, torch.float32),
+                        ("block_table", block_table, torch.int32),
+                        ("context_lens", context_lens, torch.int32)):
+        _dev(t, name, dt)
+    if R != B * next_n:
+        raise MxidxError("q rows must be batch * next_n")
+    for name, t in (("q_values", q_values), ("weights", weights), ("context_lens", context_lens)):
+        if not t.is_contiguous():
+            raise MxidxError(f"{name} must be contiguous")
+    if tuple(q_values.shape) != (R, H, HEAD_DIM) or tuple(weights.shape) != (R, H):
+        raise MxidxError("shape mismatch among q/weights")
+    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.shape[0] != B:
+        raise MxidxError("block_table must be [batch, pages] with unit inner stride")
+    if block_table.shape[1] * PAGE_SIZE < max_context_len:
+        raise MxidxError("block_table has fewer pages than max_context_len needs")
+    if logits is None:
+        fill = float("-inf") if clean else 0.0
+        logits = torch.full((R, max_context_len), fill, dtype=torch.float32, device=q_values.device)
+    _dev(logits, "logits", torch.float32)
+    if logits.dim() != 2 or logits.stride(1) != 1 or logits.shape[0] < R or \
+            logits.shape[1] < max_context_len:
+        raise MxidxError("logits must be [>=rows, >=max_context_len] with contiguous rows")
+    _check(lib().idx_logits_paged_fp8(_ptr(q_values), _ptr(weights), _ptr(cache), num_pages,
+                                      PAGE_SIZE, _ptr(block_table), block_table.stride(0),
+                                      _ptr(context_lens), B, next_n, H, int(max_context_len),
+                                      _ptr(logits), logits.stride(0), 1 if clean else 0,
+                                      _stream(stream)), "idx_logits_paged_fp8")
+    return logits
 
 
 def topk_noalloc(logits, ks, ke, k, out=None, stream=None):

@@ -277,6 +277,101 @@ int idx_topk_ws(const float* logits, int64_t rows, int64_t logits_row_stride, co
                                         workspace, stream));
 }
 
+int idx_quantize_fp8(const void* x, int dtype, int64_t rows, int64_t row_stride, int scale_fmt,
+                     uint8_t* values, float* scales, const float* w_in, float* w_out,
+                     hipStream_t stream) {
+  int st = check_rows_input(x, dtype, rows, row_stride);
+  if (st != IDX_OK) return st;
+  if (scale_fmt != IDX_FP8_SCALE_F32 && scale_fmt != IDX_FP8_SCALE_POW2) return IDX_ERR_ARG;
+  if ((w_in == nullptr) != (w_out == nullptr)) return IDX_ERR_ARG;
+  if (rows == 0) return IDX_OK;
+  if (!values || !aligned(values, 16) || !scales || !aligned(scales, 4)) return IDX_ERR_ARG;
+  if (w_in && (!aligned(w_in, 4) || !aligned(w_out, 4))) return IDX_ERR_ARG;
+  if ((st = gate_current()) != IDX_OK) return st;
+  return launched(mxidx::launch_quantize_fp8(x, dtype == IDX_F32, rows, row_stride,
+                                             scale_fmt == IDX_FP8_SCALE_POW2, values, scales, w_in,
+                                             w_out, stream));
+}
+
+int idx_insert_fp8(const void* k, int dtype, int64_t num_tokens, int64_t k_row_stride,
+                   int scale_fmt, const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
+                   int page_size, hipStream_t stream) {
+  int st = check_rows_input(k, dtype, num_tokens, k_row_stride);
+  if (st != IDX_OK) return st;
+  if (scale_fmt != IDX_FP8_SCALE_F32 && scale_fmt != IDX_FP8_SCALE_POW2) return IDX_ERR_ARG;
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0) return IDX_ERR_ARG;
+  if (num_tokens == 0) return IDX_OK;
+  if (!slot_mapping || !aligned(slot_mapping, 8)) return IDX_ERR_ARG;
+  if (num_pages > 0 && (!cache || !aligned(cache, 16))) return IDX_ERR_ARG;
+  if ((st = gate_current()) != IDX_OK) return st;
+  return launched(mxidx::launch_insert_fp8(k, dtype == IDX_F32, num_tokens, k_row_stride,
+                                           scale_fmt == IDX_FP8_SCALE_POW2, slot_mapping, cache,
+                                           num_pages, stream));
+}
+
+int idx_gather_fp8(const uint8_t* cache, int64_t num_pages, int page_size,
+                   const int32_t* block_table, int64_t bt_row_stride, const int32_t* seq_lens,
+                   const int64_t* cu_seq_offsets, int batch, int64_t max_seq_len,
+                   int64_t total_tokens, uint8_t* k_values, float* k_scales, hipStream_t stream) {
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0 || batch < 0 || batch > 65535 ||
+      max_seq_len < 0 || total_tokens < 0)
+    return IDX_ERR_ARG;
+  if (batch == 0 || max_seq_len == 0 || total_tokens == 0 || num_pages == 0) return IDX_OK;
+  const int64_t pages_per_seq = (max_seq_len + IDX_PAGE_SIZE - 1) / IDX_PAGE_SIZE;
+  if (bt_row_stride < pages_per_seq) return IDX_ERR_ARG;
+  if (!cache || !aligned(cache, 16) || !block_table || !seq_lens || !cu_seq_offsets ||
+      !aligned(cu_seq_offsets, 8) || !k_values || !aligned(k_values, 16) || !k_scales ||
+      !aligned(k_scales, 4))
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_gather_fp8(cache, num_pages, block_table, bt_row_stride, seq_lens,
+                                           cu_seq_offsets, batch, max_seq_len, total_tokens,
+                                           k_values, k_scales, stream));
+}
+
+int idx_logits_prefill_fp8(const uint8_t* q_values, const float* weights, const uint8_t* k_values,
+                           const float* k_scales, const int32_t* ks, const int32_t* ke, int64_t T,
+                           int H, int64_t S, float* logits, int64_t logits_row_stride, int clean,
+                           hipStream_t stream) {
+  if (T < 0 || S < 0 || S > 0x7fffffffLL - 1024 || !heads_ok(H)) return IDX_ERR_ARG;
+  if (T == 0 || S == 0) return IDX_OK;
+  if (logits_row_stride < S) return IDX_ERR_ARG;
+  if (!q_values || !aligned(q_values, 16) || !weights || !aligned(weights, 16) || !k_values ||
+      !aligned(k_values, 16) || !k_scales || !aligned(k_scales, 4) || !ke || !logits ||
+      !aligned(logits, 4))
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_logits_prefill_fp8(q_values, weights, k_values, k_scales, ks, ke, T,
+                                                   H, S, logits, logits_row_stride, clean, stream));
+}
+
+int idx_logits_paged_fp8(const uint8_t* q_values, const float* weights, const uint8_t* cache,
+                         int64_t num_pages, int page_size, const int32_t* block_table,
+                         int64_t bt_row_stride, const int32_t* context_lens, int B, int next_n,
+                         int H, int64_t max_context_len, float* logits, int64_t logits_row_stride,
+                         int clean, hipStream_t stream) {
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0 || B < 0 || B > IDX_MAX_DECODE_SEQS ||
+      next_n < 1 || next_n > 16 || !heads_ok(H) || max_context_len < 0 ||
+      max_context_len > 0x7fffffffLL - IDX_PAGE_SIZE)
+    return IDX_ERR_ARG;
+  if (B == 0 || max_context_len == 0) return IDX_OK;
+  const int64_t pages_per_seq = (max_context_len + IDX_PAGE_SIZE - 1) / IDX_PAGE_SIZE;
+  if (bt_row_stride < pages_per_seq || logits_row_stride < max_context_len || num_pages < 1 ||
+      (int64_t)B * pages_per_seq > 0x7fffffffLL)
+    return IDX_ERR_ARG;
+  if (!q_values || !aligned(q_values, 16) || !weights || !aligned(weights, 16) || !cache ||
+      !aligned(cache, 16) || !block_table || !context_lens || !logits || !aligned(logits, 4))
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_logits_paged_fp8(q_values, weights, cache, num_pages, block_table,
+                                                 bt_row_stride, context_lens, B, next_n, H,
+                                                 max_context_len, logits, logits_row_stride, clean,
+                                                 stream));
+}
+
 int idx_topk_noalloc(const float* logits, int64_t rows, int64_t logits_row_stride,
                      const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
                      hipStream_t stream) {

@@ -1,0 +1,540 @@
+// FP8 (E4M3) indexer cache: the format the MXFP4 cache replaces (P1 "[Kernel]
+// MXFP4 indexer cache for GLM-5.2 / DSA", section "Benefit": 132 bytes per
+// token per head against 68), with the same roles -- quantize, insert through
+// a slot mapping, gather, dense and paged logits -- on gfx950's FP8 MFMA.
+//
+// Row format (132 bytes): 128 OCP E4M3 values and one fp32 scale.  Encode rule:
+// s = amax / 448 in fp32 (floored at 2^-126), or with power-of-two scales
+// (P3 "_kpool_compress_insert": round_scale) s = 2^E, E the smallest integer
+// with amax <= 448 * 2^E; each element is x / s rounded to fp32, then to the
+// nearest E4M3 value (ties to even) by the hardware conversion.  Pages keep
+// the block-split layout: 64 value rows (8192 bytes), then 64 scale words.
+//
+// Query (P3 "forward_cuda": FP8 q is a single tensor, its per-token scale
+// folded into the weights): the row encoder can also write w' = w * s_q, and
+// the logits kernels take q's E4M3 values with w' as given:
+//
+//   logits[t, s] = s_k[s] * sum_h w'[t,h] * max(0, q8[t,h] . k8[s]),
+//
+// the positive K scale applied after the head sum.  Heads are the M dimension
+// of v_mfma_scale_f32_16x16x128_f8f6f4 in its E4M3 x E4M3 form (unit scales):
+// lane (g, n) supplies the 32 bytes 32g..32g+31 of row n, i.e. the whole
+// 128-wide dot in one instruction; the ReLU-weighted head sum and the
+// cross-lane reduction are the MXFP4 kernels' (logits_reduce.hpp).
+//
+// At equal throughput the FP8 MFMA takes twice the FP4 instruction's cycles
+// for the same 65,536 flops, so here the 8 VALU instructions of the epilogue
+// per MFMA no longer bound the prefill kernel: it is MFMA-bound at the FP8
+// peak (half the FP4 one), which is where the FP4 kernel's VALU co-bound
+// already holds that one.
+#include "common.hpp"
+#include "launch.hpp"
+#include "logits_reduce.hpp"
+
+namespace mxidx {
+namespace {
+
+constexpr int kF8Row = 128;                        // value bytes per token
+constexpr int kF8PageValues = kPage * kF8Row;      // 8192: value rows first ...
+constexpr int kF8PageBytes = kPage * (kF8Row + 4); // 8448: ... then the scale words
+constexpr float kE4M3Max = 448.0f;
+constexpr int kF8RowsPerBlock = 16;                // 256 threads, 16 lanes per row
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Per-row scale from the amax bits (a non-negative finite fp32).
+__device__ __forceinline__ float fp8_row_scale(uint32_t a, bool pow2) {
+  if (pow2) {
+    // amax = 1.f * 2^e: 448 * 2^E = 1.75 * 2^(E+8) >= amax first at E = e - 8
+    // when 1.f <= 1.75 (mantissa field <= 0x600000), else at e - 7; amax below
+    // 2^-126 (subnormal or zero) clamps to -126
+    const uint32_t ex = a >> 23;
+    int E = -126;
+    if (ex != 0u) {
+      const int e = (int)ex - 127;
+      E = max(((a & 0x7fffffu) <= 0x600000u) ? e - 8 : e - 7, -126);
+    }
+    return __uint_as_float((uint32_t)(E + 127) << 23);
+  }
+  const float s = __uint_as_float(a) / kE4M3Max;   // correctly rounded fp32 division
+  return fmaxf(s, __uint_as_float(0x00800000u));   // floor: 2^-126
+}
+
+// Four E4M3 bytes of y0..y3 (byte i = y_i), hardware round to nearest even.
+__device__ __forceinline__ uint32_t pack_fp8x4(float y0, float y1, float y2, float y3) {
+  int out = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  out = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, out, true);
+  return (uint32_t)out;
+}
+
+// 8 consecutive elements of a row as fp32 values.
+struct Bf16x8 {
+  static __device__ __forceinline__ void load(const void* base, int64_t row, int64_t stride,
+                                              int sub, float (&v)[8]) {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) +
+                                                    row * stride + 8 * sub);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+};
+struct F32x8 {
+  static __device__ __forceinline__ void load(const void* base, int64_t row, int64_t stride,
+                                              int sub, float (&v)[8]) {
+    const float* p = static_cast<const float*>(base) + row * stride + 8 * sub;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+
+// kPaged = false: row r -> values[r*128], scales[r] (and w_out[r] = w_in[r] * s when given).
+// kPaged = true:  row r -> slot slot_mapping[r]: values at page*8448 + off*128, the
+//                 scale at page*8448 + 8192 + off*4; slots outside the cache write nothing.
+// 16 lanes per row, 8 elements per lane; the row amax is an integer max over
+// the magnitude bits reduced over the row's 16 lanes.
+template <typename In, bool kPaged>
+__global__ __launch_bounds__(256) void fp8_rows_kernel(const void* __restrict__ x, int64_t rows,
+                                                       int64_t stride,
+                                                       const int64_t* __restrict__ slot_mapping,
+                                                       int64_t num_slots,
+                                                       uint8_t* __restrict__ dst_values,
+                                                       float* __restrict__ dst_scales, int pow2,
+                                                       const float* __restrict__ w_in,
+                                                       float* __restrict__ w_out) {
+  const int sub = threadIdx.x & 15;
+  for (int64_t row = (int64_t)blockIdx.x * kF8RowsPerBlock + (threadIdx.x >> 4); row < rows;
+       row += (int64_t)gridDim.x * kF8RowsPerBlock) {
+    uint8_t* vdst;
+    float* sdst;
+    if constexpr (kPaged) {
+      const int64_t slot = slot_mapping[row];       // same for the row's 16 lanes
+      if (slot < 0 || slot >= num_slots) continue;
+      const int64_t page = slot / kPage, off = slot % kPage;
+      vdst = dst_values + page * kF8PageBytes + off * kF8Row;
+      sdst = reinterpret_cast<float*>(dst_values + page * kF8PageBytes + kF8PageValues + off * 4);
+    } else {
+      vdst = dst_values + row * kF8Row;
+      sdst = dst_scales + row;
+    }
+    float v[8];
+    In::load(x, row, stride, sub, v);
+    uint32_t a = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = max(a, __float_as_uint(v[i]) & 0x7fffffffu);
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) a = max(a, (uint32_t)__shfl_xor((int)a, m));
+    const float s = fp8_row_scale(a, pow2 != 0);
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = v[i] / s;      // correctly rounded fp32 division
+    const uint2 packed = make_uint2(pack_fp8x4(y[0], y[1], y[2], y[3]),
+                                    pack_fp8x4(y[4], y[5], y[6], y[7]));
+    *reinterpret_cast<uint2*>(vdst + 8 * sub) = packed;
+    if (sub == 0) {
+      *sdst = s;
+      if constexpr (!kPaged)
+        if (w_out) w_out[row] = w_in[row] * s;
+    }
+  }
+}
+
+int f8_grid(int64_t rows) {
+  const int64_t blocks = (rows + kF8RowsPerBlock - 1) / kF8RowsPerBlock;
+  const int64_t cap = 256 * 32;
+  return (int)(blocks < cap ? blocks : cap);
+}
+
+// Paged FP8 cache -> contiguous rows: one 512-thread workgroup per (sequence,
+// page), 8 lanes of 16 bytes per token, the first of them also moving the scale.
+__global__ __launch_bounds__(512) void gather_fp8_kernel(const uint8_t* __restrict__ cache,
+                                                         int64_t num_pages,
+                                                         const int32_t* __restrict__ block_table,
+                                                         int64_t bt_row_stride,
+                                                         const int32_t* __restrict__ seq_lens,
+                                                         const int64_t* __restrict__ cu_seq_offsets,
+                                                         int64_t total_tokens,
+                                                         uint8_t* __restrict__ k_values,
+                                                         float* __restrict__ k_scales) {
+  const int b = blockIdx.y;
+  const int64_t lp = blockIdx.x;
+  const int64_t j = lp * kPage + (threadIdx.x >> 3);
+  const int part = threadIdx.x & 7;
+  if (j >= (int64_t)seq_lens[b]) return;
+  const int64_t page = block_table[(int64_t)b * bt_row_stride + lp];
+  if (page < 0 || page >= num_pages) return;
+  const int64_t row = cu_seq_offsets[b] + j;
+  if (row < 0 || row >= total_tokens) return;
+  const int off = (int)(j % kPage);
+  const uint8_t* pbase = cache + page * kF8PageBytes;
+  *reinterpret_cast<uint4*>(k_values + row * kF8Row + part * 16) =
+      *reinterpret_cast<const uint4*>(pbase + off * kF8Row + part * 16);
+  if (part == 0) k_scales[row] = *reinterpret_cast<const float*>(pbase + kF8PageValues + off * 4);
+}
+
+// E4M3 x E4M3 MFMA (unit scales): 16 heads x 16 keys, the full 128-wide dot.
+__device__ __forceinline__ v4f mfma_fp8(const uint4 (&a)[2], const uint4 (&b)[2], v4f c) {
+  const v8i av = {(int)a[0].x, (int)a[0].y, (int)a[0].z, (int)a[0].w,
+                  (int)a[1].x, (int)a[1].y, (int)a[1].z, (int)a[1].w};
+  const v8i bv = {(int)b[0].x, (int)b[0].y, (int)b[0].z, (int)b[0].w,
+                  (int)b[1].x, (int)b[1].y, (int)b[1].z, (int)b[1].w};
+  // cbsz = blgp = 0: E4M3 operands; scale bytes 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 127, 0, 127);
+}
+
+template <int kAux>
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  const u32x4 c = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kAux);
+  return make_uint4(c.x, c.y, c.z, c.w);
+}
+
+template <int NH>
+struct F8Query {
+  uint4 a[NH][2];     // group grp: bytes 32g..32g+31 of head 16*grp + n
+  float4 w[NH];       // w' of heads 16*grp + 4g .. +3
+};
+
+template <int NH>
+__device__ __forceinline__ F8Query<NH> load_f8_query(const uint8_t* __restrict__ q_values,
+                                                     const float* __restrict__ weights, int64_t r,
+                                                     int g, int n) {
+  constexpr int H = 16 * NH;
+  F8Query<NH> q;
+#pragma unroll
+  for (int grp = 0; grp < NH; ++grp) {
+    const uint8_t* p = q_values + (r * H + 16 * grp + n) * kF8Row + 32 * g;
+    q.a[grp][0] = *reinterpret_cast<const uint4*>(p);
+    q.a[grp][1] = *reinterpret_cast<const uint4*>(p + 16);
+    q.w[grp] = *reinterpret_cast<const float4*>(weights + r * H + 16 * grp + 4 * g);
+  }
+  return q;
+}
+
+// 64 keys: tile j = keys 16j + n, lane (g, n) holding bytes 32g..32g+31; lane l
+// also holds the scale of key l.
+struct F8Tile {
+  uint4 v[4][2];
+  float scale;
+};
+
+template <int NH>
+__device__ __forceinline__ float f8_tile_score(const F8Tile& t, const F8Query<NH>& q) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int grp = 0; grp < NH; ++grp)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = relu_weighted(mfma_fp8(q.a[grp], t.v[j], zero), q.w[grp], acc[j]);
+  return reduce_tiles(acc) * t.scale;
+}
+
+// ---------------------------------------------------------------------------
+// Paged decode: one wave per workgroup over kF8Pages consecutive pages of one
+// sequence (17 KB of cache in flight per wave), pages read through buffer
+// descriptors with a wave-uniform base (a missing page reads zeros, no access),
+// query rows one at a time.
+constexpr int kF8Pages = 2;
+
+template <int NH>
+__global__ __launch_bounds__(kWave) void logits_paged_fp8_kernel(
+    const uint8_t* __restrict__ q_values, const float* __restrict__ weights,
+    const uint8_t* __restrict__ cache, int64_t num_pages, const int32_t* __restrict__ block_table,
+    int64_t bt_row_stride, const int32_t* __restrict__ context_lens, int next_n, int64_t width,
+    float* __restrict__ logits, int64_t ld, int clean, int stream_out) {
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, n = lane & 15;
+  const int64_t lp0 = (int64_t)blockIdx.x * kF8Pages;
+  const int64_t wpages = (width + kPage - 1) / kPage;
+  const int64_t row0 = (int64_t)b * next_n;
+  const int bt_count = (int)min((int64_t)kF8Pages, wpages - lp0);
+  const int bt_lane = (int)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_rsrc(block_table + (int64_t)b * bt_row_stride + lp0, 4 * bt_count), 4u * lane, 0, 0);
+  const int64_t ctx = (int32_t)__builtin_amdgcn_readfirstlane(
+      (int)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(context_lens + b, 4), 0, 0, 0));
+  const int64_t L = min(ctx, width);
+
+  auto store = [&](int64_t r, int64_t tok0, int64_t ke, float v) {
+    const int64_t col = tok0 + lane;
+    const bool scored = col < ke;
+    const bool keep = scored || (clean && col < width);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(logits + r * ld + tok0, kPage * 4);
+    const uint32_t bits = __float_as_uint(scored ? v : neg_inf());
+    const uint32_t off = keep ? 4u * lane : kDropOffset;
+    if (stream_out)
+      __builtin_amdgcn_raw_buffer_store_b32(bits, rs, off, 0, kNonTemporal);
+    else
+      __builtin_amdgcn_raw_buffer_store_b32(bits, rs, off, 0, 0);
+  };
+
+  if (lp0 * kPage >= L) {
+    if (clean)
+      for (int i = 0; i < next_n; ++i)
+#pragma unroll
+        for (int p = 0; p < kF8Pages; ++p) store(row0 + i, (lp0 + p) * kPage, 0, 0.f);
+    return;
+  }
+  const int np = (int)min((int64_t)kF8Pages, (L - lp0 * kPage + kPage - 1) / kPage);
+
+  F8Tile pg[kF8Pages];
+  bool page_ok[kF8Pages];
+  const uint32_t off_v = (uint32_t)(kF8Row * n + 32 * g);
+#pragma unroll
+  for (int p = 0; p < kF8Pages; ++p) {
+    const int pid = __builtin_amdgcn_readlane(bt_lane, p);
+    const bool valid = pid >= 0 && pid < num_pages;
+    page_ok[p] = p >= np || valid;
+    const int live = __builtin_amdgcn_readfirstlane((p < np && valid) ? 1 : 0);
+    const int64_t page = __builtin_amdgcn_readfirstlane(live ? pid : 0);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(cache + page * kF8PageBytes, live ? kF8PageBytes : 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pg[p].v[j][0] = ld16<kNonTemporal>(rs, off_v + 2048u * j);
+      pg[p].v[j][1] = ld16<kNonTemporal>(rs, off_v + 2048u * j + 16u);
+    }
+    pg[p].scale = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(kF8PageValues + 4 * lane), 0, kNonTemporal));
+  }
+  for (int i = 0; i < next_n; ++i) {
+    const int64_t r = row0 + i;
+    const int64_t ke = L - next_n + i + 1;
+    const F8Query<NH> q = load_f8_query<NH>(q_values, weights, r, g, n);
+#pragma unroll
+    for (int p = 0; p < kF8Pages; ++p)
+      if (page_ok[p]) store(r, (lp0 + p) * kPage, ke, f8_tile_score<NH>(pg[p], q));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dense prefill: 4 waves x RW query rows per workgroup over a chunk of keys,
+// 64 keys per step with the next step's tile in flight, as the MXFP4 kernel
+// (logits_prefill.hip) does; K rows are 128 bytes and each key's scale is
+// applied to its logit after the head sum.
+constexpr int kF8KeyChunkSmallS = 512;
+constexpr int kF8KeyChunk = 4096;
+constexpr int64_t kF8SmallS = 16384;
+
+__device__ __forceinline__ void load_f8_tile(F8Tile& t, const uint8_t* __restrict__ kv,
+                                             const float* __restrict__ ksc, int c0, int S, int g,
+                                             int n, int lane) {
+  c0 = __builtin_amdgcn_readfirstlane(c0);
+  const int keys = __builtin_amdgcn_readfirstlane(max(min(S - c0, 64), 0));
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(kv + (int64_t)c0 * kF8Row, keys * kF8Row);
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(ksc + (int64_t)c0, keys * 4);
+  const uint32_t off = (uint32_t)(kF8Row * n + 32 * g);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t.v[j][0] = ld16<0>(rv, off + 2048u * j);
+    t.v[j][1] = ld16<0>(rv, off + 2048u * j + 16u);
+  }
+  t.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4u * lane, 0, 0));
+}
+
+template <int NH, int RW>
+__global__ __launch_bounds__(256) void logits_prefill_fp8_kernel(
+    const uint8_t* __restrict__ q_values, const float* __restrict__ weights,
+    const uint8_t* __restrict__ k_values, const float* __restrict__ k_scales,
+    const int32_t* __restrict__ ks, const int32_t* __restrict__ ke, int64_t T, int S,
+    float* __restrict__ logits, int64_t ld, int clean, int64_t n_qb, int64_t n_kc, int key_chunk) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  // XCD-aware order (workgroup i runs on XCD i % 8): one XCD's resident
+  // workgroups share a query block, causal work spreads over the XCDs, and
+  // query blocks run last to first (the longest causal rows first)
+  int64_t qb, kc;
+  if (n_qb % 8 == 0) {
+    const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
+    qb = n_qb - 1 - ((j / n_kc) * 8 + x);
+    kc = j % n_kc;
+  } else {
+    qb = n_qb - 1 - blockIdx.x / n_kc;
+    kc = blockIdx.x % n_kc;
+  }
+  const int64_t t0 = qb * (4 * RW) + wave * RW;
+  const int c_begin = (int)kc * key_chunk;
+  const int c_end = (int)min((int64_t)c_begin + key_chunk, (int64_t)S);
+  int lo[RW], hi[RW];
+  int need_lo = c_end, need_hi = c_begin;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int64_t t = t0 + i;
+    lo[i] = 0;
+    hi[i] = 0;
+    if (t < T) {
+      lo[i] = ks ? max(ks[t], 0) : 0;
+      hi[i] = min(ke[t], S);
+      if (lo[i] < hi[i]) {
+        need_lo = min(need_lo, max(lo[i], c_begin));
+        need_hi = max(need_hi, min(hi[i], c_end));
+      }
+    }
+  }
+  float* lrow[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) lrow[i] = logits + min(t0 + i, T - 1) * ld;
+  auto store = [&](int i, int c0, float v) {
+    c0 = __builtin_amdgcn_readfirstlane(c0);
+    uint32_t off = 4u * lane;
+    if (t0 + i >= T) off = kDropOffset;
+    if (!(c0 >= lo[i] && c0 + 64 <= hi[i])) {          // a tile that straddles [ks, ke)
+      const int col = c0 + lane;
+      const bool scored = col >= lo[i] && col < hi[i];
+      if (!scored) v = neg_inf();
+      if (!scored && !(clean && col < c_end)) off = kDropOffset;
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), buffer_rsrc(lrow[i] + c0, 64 * 4), off,
+                                          0, kNonTemporal);
+  };
+  const int k_first = c_begin + ((need_lo - c_begin) & ~63);
+  if (clean) {
+    for (int c0 = c_begin; c0 < c_end; c0 += 64) {
+      if (need_lo < need_hi && c0 >= k_first && c0 < need_hi) continue;
+#pragma unroll
+      for (int i = 0; i < RW; ++i) store(i, c0, neg_inf());
+    }
+  }
+  if (need_lo >= need_hi) return;
+
+  F8Query<NH> q[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) q[i] = load_f8_query<NH>(q_values, weights, min(t0 + i, T - 1), g, n);
+
+  F8Tile kt0, kt1;
+  load_f8_tile(kt0, k_values, k_scales, k_first, S, g, n, lane);
+  for (int c0 = k_first; c0 < need_hi; c0 += 128) {
+    load_f8_tile(kt1, k_values, k_scales, c0 + 64, S, g, n, lane);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) store(i, c0, f8_tile_score<NH>(kt0, q[i]));
+    if (c0 + 64 >= need_hi) break;
+    load_f8_tile(kt0, k_values, k_scales, c0 + 128, S, g, n, lane);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) store(i, c0 + 64, f8_tile_score<NH>(kt1, q[i]));
+  }
+}
+
+template <int NH>
+hipError_t launch_paged_fp8_nh(const uint8_t* qv, const float* w, const uint8_t* cache,
+                               int64_t num_pages, const int32_t* bt, int64_t bt_stride,
+                               const int32_t* ctx, int B, int next_n, int64_t width, float* logits,
+                               int64_t ld, int clean, hipStream_t stream) {
+  const int64_t pages = (width + kPage - 1) / kPage;
+  const int stream_out = (int64_t)B * next_n * width * 4 > (4 << 20) ? 1 : 0;
+  const dim3 grid((unsigned)((pages + kF8Pages - 1) / kF8Pages), (unsigned)B);
+  hipLaunchKernelGGL((logits_paged_fp8_kernel<NH>), grid, dim3(kWave), 0, stream, qv, w, cache,
+                     num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean, stream_out);
+  return hipGetLastError();
+}
+
+template <int NH, int RW>
+hipError_t launch_prefill_fp8_cfg(const uint8_t* qv, const float* w, const uint8_t* kv,
+                                  const float* ksc, const int32_t* ks, const int32_t* ke, int64_t T,
+                                  int64_t S, float* logits, int64_t ld, int clean,
+                                  hipStream_t stream) {
+  const int64_t n_qb = (T + 4 * RW - 1) / (4 * RW);
+  const int key_chunk = S <= kF8SmallS ? kF8KeyChunkSmallS : kF8KeyChunk;
+  const int64_t n_kc = (S + key_chunk - 1) / key_chunk;
+  hipLaunchKernelGGL((logits_prefill_fp8_kernel<NH, RW>), dim3((unsigned)(n_qb * n_kc)), dim3(256), 0,
+                     stream, qv, w, kv, ksc, ks, ke, T, (int)S, logits, ld, clean, n_qb, n_kc,
+                     key_chunk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fp8(const void* x, bool f32, int64_t rows, int64_t row_stride, bool pow2,
+                               uint8_t* values, float* scales, const float* w_in, float* w_out,
+                               hipStream_t stream) {
+  const int grid = f8_grid(rows);
+  if (f32)
+    hipLaunchKernelGGL((fp8_rows_kernel<F32x8, false>), dim3(grid), dim3(256), 0, stream, x, rows,
+                       row_stride, nullptr, 0, values, scales, pow2 ? 1 : 0, w_in, w_out);
+  else
+    hipLaunchKernelGGL((fp8_rows_kernel<Bf16x8, false>), dim3(grid), dim3(256), 0, stream, x, rows,
+                       row_stride, nullptr, 0, values, scales, pow2 ? 1 : 0, w_in, w_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_insert_fp8(const void* k, bool f32, int64_t num_tokens, int64_t row_stride,
+                             bool pow2, const int64_t* slot_mapping, uint8_t* cache,
+                             int64_t num_pages, hipStream_t stream) {
+  const int grid = f8_grid(num_tokens);
+  const int64_t num_slots = num_pages * kPage;
+  if (f32)
+    hipLaunchKernelGGL((fp8_rows_kernel<F32x8, true>), dim3(grid), dim3(256), 0, stream, k,
+                       num_tokens, row_stride, slot_mapping, num_slots, cache, nullptr,
+                       pow2 ? 1 : 0, nullptr, nullptr);
+  else
+    hipLaunchKernelGGL((fp8_rows_kernel<Bf16x8, true>), dim3(grid), dim3(256), 0, stream, k,
+                       num_tokens, row_stride, slot_mapping, num_slots, cache, nullptr,
+                       pow2 ? 1 : 0, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_fp8(const uint8_t* cache, int64_t num_pages, const int32_t* block_table,
+                             int64_t bt_row_stride, const int32_t* seq_lens,
+                             const int64_t* cu_seq_offsets, int batch, int64_t max_seq_len,
+                             int64_t total_tokens, uint8_t* k_values, float* k_scales,
+                             hipStream_t stream) {
+  const int64_t pages = (max_seq_len + kPage - 1) / kPage;
+  hipLaunchKernelGGL(gather_fp8_kernel, dim3((unsigned)pages, (unsigned)batch), dim3(512), 0,
+                     stream, cache, num_pages, block_table, bt_row_stride, seq_lens,
+                     cu_seq_offsets, total_tokens, k_values, k_scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_logits_paged_fp8(const uint8_t* q_values, const float* weights,
+                                   const uint8_t* cache, int64_t num_pages,
+                                   const int32_t* block_table, int64_t bt_row_stride,
+                                   const int32_t* context_lens, int B, int next_n, int H,
+                                   int64_t max_context_len, float* logits, int64_t ld, int clean,
+                                   hipStream_t stream) {
+#define MXIDX_F8P(nh)                                                                          \
+  case nh:                                                                                     \
+    return launch_paged_fp8_nh<nh>(q_values, weights, cache, num_pages, block_table,           \
+                                   bt_row_stride, context_lens, B, next_n, max_context_len,    \
+                                   logits, ld, clean, stream);
+  switch (H / 16) {
+    MXIDX_F8P(1)
+    MXIDX_F8P(2)
+    MXIDX_F8P(3)
+    MXIDX_F8P(4)
+    MXIDX_F8P(5)
+    MXIDX_F8P(6)
+    MXIDX_F8P(7)
+    MXIDX_F8P(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MXIDX_F8P
+}
+
+hipError_t launch_logits_prefill_fp8(const uint8_t* q_values, const float* weights,
+                                     const uint8_t* k_values, const float* k_scales,
+                                     const int32_t* ks, const int32_t* ke, int64_t T, int H,
+                                     int64_t S, float* logits, int64_t ld, int clean,
+                                     hipStream_t stream) {
+#define MXIDX_F8X(nh, rw)                                                                        \
+  case nh:                                                                                       \
+    return launch_prefill_fp8_cfg<nh, rw>(q_values, weights, k_values, k_scales, ks, ke, T, S,  \
+                                          logits, ld, clean, stream);
+  switch (H / 16) {
+    MXIDX_F8X(1, 4)
+    MXIDX_F8X(2, 4)
+    MXIDX_F8X(3, 2)
+    MXIDX_F8X(4, 2)
+    MXIDX_F8X(5, 1)
+    MXIDX_F8X(6, 1)
+    MXIDX_F8X(7, 1)
+    MXIDX_F8X(8, 1)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MXIDX_F8X
+}
+
+}  // namespace mxidx

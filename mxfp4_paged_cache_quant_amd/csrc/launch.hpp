@@ -49,6 +49,30 @@ hipError_t launch_logits_paged_insert(const void* q, const void* k_new, bool f32
                                       int64_t max_context_len, float* logits, int64_t ld,
                                       int clean, hipStream_t stream);
 
+// FP8 (E4M3) indexer cache (fp8.hip): rows of 128 E4M3 values + an fp32 scale.
+hipError_t launch_quantize_fp8(const void* x, bool f32, int64_t rows, int64_t row_stride, bool pow2,
+                               uint8_t* values, float* scales, const float* w_in, float* w_out,
+                               hipStream_t stream);
+hipError_t launch_insert_fp8(const void* k, bool f32, int64_t num_tokens, int64_t row_stride,
+                             bool pow2, const int64_t* slot_mapping, uint8_t* cache,
+                             int64_t num_pages, hipStream_t stream);
+hipError_t launch_gather_fp8(const uint8_t* cache, int64_t num_pages, const int32_t* block_table,
+                             int64_t bt_row_stride, const int32_t* seq_lens,
+                             const int64_t* cu_seq_offsets, int batch, int64_t max_seq_len,
+                             int64_t total_tokens, uint8_t* k_values, float* k_scales,
+                             hipStream_t stream);
+hipError_t launch_logits_paged_fp8(const uint8_t* q_values, const float* weights,
+                                   const uint8_t* cache, int64_t num_pages,
+                                   const int32_t* block_table, int64_t bt_row_stride,
+                                   const int32_t* context_lens, int B, int next_n, int H,
+                                   int64_t max_context_len, float* logits, int64_t ld, int clean,
+                                   hipStream_t stream);
+hipError_t launch_logits_prefill_fp8(const uint8_t* q_values, const float* weights,
+                                     const uint8_t* k_values, const float* k_scales,
+                                     const int32_t* ks, const int32_t* ke, int64_t T, int H,
+                                     int64_t S, float* logits, int64_t ld, int clean,
+                                     hipStream_t stream);
+
 hipError_t launch_topk_merge(const float* values, const int32_t* indices, int world, int k_in,
                              int64_t rows, int interleave, int k, int32_t* out_idx,
                              hipStream_t stream);

@@ -165,12 +165,15 @@ def scale_offset(page, off, page_size=PAGE_SIZE):
 
 
 def write_rows(cache, codes, scales, slot_mapping, page_size=PAGE_SIZE):
-    """Scatter encoded rows into a copy of ``cache`` (slot = page * P + offset;
-    negative slots write nothing)."""
+    """Scatter encoded rows into a copy of ``cache`` [num_pages, P * 132]
+    (slot = page * P + offset).  Negative slots write nothing (P3
+    "_kpool_compress_insert": -1 = no write), and so do slots beyond the cache
+    (the safety reading the MXFP4 insert takes too)."""
     out = np.array(cache, dtype=np.uint8, copy=True).reshape(-1)
+    num_slots = out.size // ROW_BYTES
     sbytes = np.asarray(scales, dtype="<f4").view(np.uint8).reshape(-1, 4)
     slots = np.asarray(slot_mapping, dtype=np.int64)
-    for i in np.nonzero(slots >= 0)[0]:
+    for i in np.nonzero((slots >= 0) & (slots < num_slots))[0]:
         page, off = divmod(int(slots[i]), page_size)
         v0 = value_offset(page, off, page_size)
         s0 = scale_offset(page, off, page_size)

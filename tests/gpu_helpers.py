@@ -49,13 +49,15 @@ def oracle_q(case):
     return c.reshape(-1, H, 64), s.reshape(-1, H, 4)
 
 
-def check_logits(gpu, ref, bound, what=""):
-    """Masked entries must agree exactly (-inf / -inf); visible ones within tolerance."""
+def check_logits(gpu, ref, bound, what="", abs_factor=None):
+    """Masked entries must agree exactly (-inf / -inf); visible ones within tolerance
+    (the MXFP4 rule, or the FP8 one with abs_factor=tolerance.ABS_FACTOR_FP8)."""
     from oracle import tolerance
     gpu = np.asarray(gpu, dtype=np.float64)
     vis = np.isfinite(ref)
     assert np.array_equal(np.isneginf(gpu) & ~vis, ~vis), f"{what}: mask mismatch"
-    ok = tolerance.logits_close(gpu[vis], ref[vis], bound[vis])
+    factor = tolerance.ABS_FACTOR if abs_factor is None else abs_factor
+    ok = tolerance.logits_close(gpu[vis], ref[vis], bound[vis], abs_factor=factor)
     if not ok.all():
         bad = np.argwhere(vis)[~ok][:5]
         raise AssertionError(f"{what}: {int((~ok).sum())} logits out of tolerance, e.g. at "
@@ -70,7 +72,7 @@ def check_topk_sets(g_logits, ks, ke, k, out_idx, what=""):
         assert sorted(out_idx[r].tolist()) == sorted(ref_sets[r].tolist()), f"{what} top-k row {r}"
 
 
-def check_topk_end_to_end(ref_rows, bound_rows, ks, ke, k, idx_rows, what=""):
+def check_topk_end_to_end(ref_rows, bound_rows, ks, ke, k, idx_rows, what="", abs_factor=None):
     """End-to-end margin rule of GPU top-k rows against the oracle's float64
     logits of the same rows; returns how many rows needed the exact set."""
     from oracle import tolerance, topk as otk
@@ -82,7 +84,8 @@ def check_topk_end_to_end(ref_rows, bound_rows, ks, ke, k, idx_rows, what=""):
             assert np.all(np.asarray(idx_rows[j]) == -1), f"{what}: empty row {j} returned columns"
             exact_rows += 1
             continue
-        tol = tolerance.REL * abs(vk) + tolerance.ABS_FACTOR * float(bound_rows[j][vis].max())
+        factor = tolerance.ABS_FACTOR if abs_factor is None else abs_factor
+        tol = tolerance.REL * abs(vk) + factor * float(bound_rows[j][vis].max())
         ok, exact_req = tolerance.topk_end_to_end_ok(idx_rows[j], ref_rows[j], int(ks[j]),
                                                      int(ke[j]), k, tol)
         assert ok, f"{what}: end-to-end top-k, row {j}"

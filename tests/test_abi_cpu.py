@@ -38,7 +38,7 @@ def _has_gpu():
 
 def test_header_declarations_are_exported(L):
     text = open(HEADER).read()
-    declared = set(re.findall(r"\b(idx_[a-z_]+)\s*\(", text))
+    declared = set(re.findall(r"\b(idx_[a-z0-9_]+)\s*\(", text))
     assert declared == set(mx.EXPORTS), declared ^ set(mx.EXPORTS)
     for name in declared:
         assert hasattr(L, name)
@@ -228,3 +228,34 @@ def test_topk_noalloc_argument_validation(L):
     assert 0 < L.idx_topk_workspace_bytes(64, 131072) <= mx.TOPK_NOALLOC_MAX_WORKSPACE
     if not _has_gpu():
         assert f(P, 64, 131072, None, P, 2048, P2, None) == ERR_NO_DEVICE
+
+
+def test_fp8_argument_validation(L):
+    q = L.idx_quantize_fp8
+    assert q(P, 0, 4, 128, 2, P, P2, None, None, None) == ERR_ARG         # bad scale format
+    assert q(P, 0, 4, 128, 0, P, P2, P, None, None) == ERR_ARG            # w_in without w_out
+    assert q(P, 0, 4, 128, 0, MIS, P2, None, None, None) == ERR_ARG       # misaligned values
+    assert q(P, 2, 4, 128, 0, P, P2, None, None, None) == ERR_ARG         # bad dtype
+    assert q(None, 0, 0, 128, 1, None, None, None, None, None) == OK      # no rows
+    ins = L.idx_insert_fp8
+    assert ins(P, 0, 4, 128, 0, P, P2, 4, 32, None) == ERR_ARG            # page size
+    assert ins(P, 0, 4, 128, 3, P, P2, 4, 64, None) == ERR_ARG            # scale format
+    assert ins(P, 0, 4, 128, 0, None, P2, 4, 64, None) == ERR_ARG         # null slots
+    assert ins(None, 0, 0, 128, 0, None, None, 0, 64, None) == OK
+    g = L.idx_gather_fp8
+    assert g(P, 4, 64, P, 1, P, P, 1, 65, 65, P, P2, None) == ERR_ARG     # bt stride < pages
+    assert g(P, 4, 64, P, 2, P, P, 1, 65, 65, P, MIS, None) == ERR_ARG    # misaligned scales
+    assert g(P, 4, 64, P, 2, P, P, 0, 65, 65, P, P2, None) == OK          # no sequences
+    pf = L.idx_logits_prefill_fp8
+    for H in (0, 8, 24, 144):
+        assert pf(P, P, P, P, None, P, 4, H, 64, P, 64, 1, None) == ERR_ARG
+    assert pf(P, MIS, P, P, None, P, 4, 32, 64, P, 64, 1, None) == ERR_ARG  # misaligned weights
+    assert pf(P, P, P, P, None, P, 4, 32, 64, P, 63, 1, None) == ERR_ARG    # ld < S
+    assert pf(P, P, P, P, None, P, 0, 32, 64, P, 64, 1, None) == OK
+    pg = L.idx_logits_paged_fp8
+    assert pg(P, P, P, 4, 64, P, 1, P, 1, 0, 32, 64, P, 64, 1, None) == ERR_ARG   # next_n 0
+    assert pg(P, P, P, 4, 64, P, 1, P, 1, 1, 32, 65, P, 65, 1, None) == ERR_ARG   # bt stride
+    assert pg(P, P, P, 4, 48, P, 1, P, 1, 1, 32, 64, P, 64, 1, None) == ERR_ARG   # page size
+    assert pg(P, P, P, 4, 64, P, 1, P, 0, 1, 32, 64, P, 64, 1, None) == OK        # no sequences
+    if not _has_gpu():
+        assert pg(P, P, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 64, 1, None) == ERR_NO_DEVICE

@@ -156,6 +156,7 @@ def test_cache_layout_offsets_and_round_trip():
     perm = np.array([2, 0, 3])
     slots = perm[np.arange(150) // 64] * 64 + np.arange(150) % 64
     slots[7] = -1                                             # not written
+    slots[8] = num_pages * 64 + 1                             # beyond the cache: not written
     cache = np.full((num_pages, 8448), 0xA5, np.uint8)
     cache = fp8.insert(cache, k, slots)
     codes, scales = fp8.quantize_rows(k)
@@ -170,7 +171,7 @@ def test_cache_layout_offsets_and_round_trip():
     assert np.all(cache[1] == 0xA5)                          # unused page untouched
     bt = perm[None, :].astype(np.int32)
     gc, gs = fp8.gather(cache, bt, [150], [0], 150)
-    keep = np.arange(150) != 7
+    keep = (np.arange(150) != 7) & (np.arange(150) != 8)
     assert np.array_equal(gc[keep], codes[keep]) and np.array_equal(gs[keep], scales[keep])
 
 
