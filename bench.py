@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP4_PEAK_TFLOPS = 10100.0      # MI355X dense MXFP4 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA
 
 
 def log(msg):
@@ -52,12 +53,15 @@ def parse():
     ap.add_argument("--prefill", choices=["chunk", "none"], default="chunk")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context decode and long prefill measurements")
-    ap.add_argument("--only", choices=["decode", "prefill", "long_decode", "long_prefill", "copy"],
+    ap.add_argument("--only", choices=["decode", "prefill", "long_decode", "long_prefill", "copy",
+                                       "fp8"],
                     help="run one section only and print its result (for profiler runs)")
     ap.add_argument("--eager", action="store_true",
                     help="launch kernels directly instead of replaying HIP graphs")
     ap.add_argument("--pmc-summarize", nargs=2, metavar=("PMC_DIR", "SECTION"),
                     help="write profiles/pmc_bytes_SECTION.json from rocprofv3 counter runs")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the FP8 indexer-cache measurements")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
@@ -298,6 +302,7 @@ def bench_long_decode():
     import mxfp4_paged_cache_quant_amd as mx
     import workloads
     case = workloads.long_decode()
+    CASES["long_decode"] = case
     B, H, W = len(case["context_lens"]), case["H"], case["width"]
     N = int(np.sum(case["context_lens"]))
     k, slots = dev(case["k"]), dev(case["slot_mapping"])
@@ -409,6 +414,119 @@ def bench_long_prefill():
         "topk_us": round(t_tk, 1), "topk_gbs": round((pairs * 4 + T * case["topk"] * 4) / t_tk / 1e3, 1),
         "p10_p90_us": spread,
     }
+
+
+def bench_fp8(decode_case):
+    """The FP8 (E4M3, 132 B/token) indexer cache that MXFP4 replaces, on the same
+    workloads: the decode step (16 x 8192: new tokens' insert, q quantize with the
+    weight fold, paged logits, top-k) over rotating caches, the long-context paged
+    logits and top-k, and the prefill-chunk and long-prefill logits."""
+    import numpy as np
+    import torch
+    import mxfp4_paged_cache_quant_amd as mx
+    import workloads
+    out = {"bytes_per_token_per_head": {"fp8": 132, "mxfp4": 68},
+           "tokens_per_gib_per_head": {"fp8": round(2 ** 30 / 132), "mxfp4": round(2 ** 30 / 68)}}
+    # --- decode step, 48 rotating FP8 caches (830 MB, > 3x the MALL)
+    case = decode_case
+    B, H, W, K = len(case["context_lens"]), case["H"], case["width"], case["topk"]
+    base = torch.zeros((case["num_pages"], 64 * 132), dtype=torch.uint8, device="cuda")
+    mx.insert_fp8(dev(case["k"]), dev(case["slot_mapping"]), base)
+    last = np.cumsum(case["context_lens"]) - 1
+    k_new, slot_new = dev(case["k"][last]), dev(case["slot_mapping"][last])
+    q, w, bt, ctx = dev(case["q"]), dev(case["w"]), dev(case["block_table"]), dev(case["context_lens"])
+    ke = dev(case["context_lens"].astype(np.int32))
+    n_sets = 48
+    caches = [base.clone() for _ in range(n_sets)]
+    del base
+    qv = torch.empty((B, H, 128), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    wf = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    logits = torch.empty((B, W), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, K), dtype=torch.int32, device="cuda")
+    ops = {
+        "insert_fp8": lambda c: mx.insert_fp8(k_new, slot_new, c),
+        "quantize_fp8": lambda c: mx.quantize_fp8(q, weights=w, values=qv, scales=qs, weights_out=wf),
+        "logits_paged_fp8": lambda c: mx.logits_paged_fp8(qv, wf, c, bt, ctx, 1, W, logits=logits,
+                                                          clean=False),
+        "topk": lambda c: mx.topk(logits, None, ke, K, out=idx),
+    }
+    for fn in ops.values():
+        fn(caches[0])
+    torch.cuda.synchronize()
+    g_step = capture([(lambda c=c, f=f: f(c)) for c in caches for f in ops.values()])
+    step_us = time_graph(g_step, 5) / n_sets * 1e3
+    del g_step
+    per = {}
+    for name, f in ops.items():
+        g = capture([(lambda c=c, f=f: f(c)) for c in caches])
+        per[name] = round(time_graph(g, 10) / n_sets * 1e3, 3)
+        del g
+    scored = int(np.sum(case["context_lens"]))
+    out["decode_16x8192"] = {
+        "step_us": round(step_us, 3), "kernels_us": per,
+        "scored_tokens_per_s": round(scored / (step_us * 1e-6), 1),
+        "logits_paged_gbs": round((scored * 136 + B * H * 132) / per["logits_paged_fp8"] / 1e3, 1),
+    }
+    del caches
+    torch.cuda.empty_cache()
+    # --- long-context decode (64 x U[32K, 128K])
+    lc = CASES.get("long_decode") or workloads.long_decode()
+    B, H, W = len(lc["context_lens"]), lc["H"], lc["width"]
+    N = int(np.sum(lc["context_lens"]))
+    cache = torch.zeros((lc["num_pages"], 64 * 132), dtype=torch.uint8, device="cuda")
+    k, slots = dev(lc["k"]), dev(lc["slot_mapping"])
+    ins = lambda: mx.insert_fp8(k, slots, cache)  # noqa: E731
+    ins()
+    del k
+    qv, _, wf = mx.quantize_fp8(dev(lc["q"]), weights=dev(lc["w"]))
+    bt, ctx = dev(lc["block_table"]), dev(lc["context_lens"])
+    ke = dev(lc["context_lens"].astype(np.int32))
+    logits = torch.empty((B, W), dtype=torch.float32, device="cuda")
+    idx = torch.empty((B, lc["topk"]), dtype=torch.int32, device="cuda")
+    ws = mx.topk_workspace(B, W)
+    lg = lambda: mx.logits_paged_fp8(qv, wf, cache, bt, ctx, 1, W, logits=logits, clean=False)  # noqa: E731
+    tk = lambda: mx.topk_ws(logits, None, ke, lc["topk"], ws, out=idx)  # noqa: E731
+    lg()
+    tk()
+    torch.cuda.synchronize()
+    t_lg, t_tk = time_fn(lg, 10, 4), time_fn(tk, 10, 4)
+    b_lg = N * 136 + B * H * 132
+    out["long_decode"] = {
+        "cache_bytes": lc["num_pages"] * 64 * 132,
+        "logits_paged_us": round(t_lg, 1), "logits_paged_gbs": round(b_lg / t_lg / 1e3, 1),
+        "logits_paged_frac_hbm": round(b_lg / t_lg / 1e3 / HBM_PEAK_GBS, 4),
+        "topk_us": round(t_tk, 1), "decode_step_us": round(t_lg + t_tk, 1),
+        "decode_step_frac_hbm": round((N * 140 + B * H * 132 + B * lc["topk"] * 4)
+                                      / ((t_lg + t_tk) * 1e3) / HBM_PEAK_GBS, 4),
+        "scored_tokens_per_s": round(N / ((t_lg + t_tk) * 1e-6), 1),
+    }
+    del cache, logits, ws
+    torch.cuda.empty_cache()
+    # --- prefill logits: the 8192 chunk and the long prefill
+    for key, getter in (("prefill_chunk", workloads.prefill_chunk),
+                        ("long_prefill", workloads.long_prefill)):
+        pc = CASES.get(key) or getter()
+        T, S, H = pc["T"], pc["S"], pc["H"]
+        cache = torch.zeros((pc["num_pages"], 64 * 132), dtype=torch.uint8, device="cuda")
+        mx.insert_fp8(dev(pc["k"]), dev(pc["slot_mapping"]), cache)
+        kv, ksc = mx.gather_fp8(cache, dev(pc["block_table"]), dev(pc["seq_lens"]),
+                                dev(pc["cu_seq_offsets"]), S, S)
+        qv, _, wf = mx.quantize_fp8(dev(pc["q"]), weights=dev(pc["w"]))
+        ks_, ke_ = dev(pc["ks"]), dev(pc["ke"])
+        logits = torch.empty((T, S), dtype=torch.float32, device="cuda")
+        lgp = lambda: mx.logits_prefill_fp8(qv, wf, kv, ksc, ks_, ke_, logits=logits, clean=False)  # noqa: E731
+        lgp()
+        torch.cuda.synchronize()
+        reps = 10 if key == "prefill_chunk" else 3
+        t = time_fn(lgp, reps, 4 if key == "prefill_chunk" else 2)
+        pairs = int(np.sum(pc["ke"].astype(np.int64) - pc["ks"]))
+        tflops = 2.0 * H * 128 * pairs / (t * 1e-6) / 1e12
+        out[key] = {"logits_us": round(t, 1), "logits_tflops": round(tflops, 1),
+                    "logits_frac_fp8_peak": round(tflops / FP8_PEAK_TFLOPS, 4)}
+        del cache, kv, ksc, qv, wf, logits
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_copy(nbytes=1 << 30, reps=5):
@@ -663,7 +781,8 @@ def main():
     EAGER = args.eager
     if args.only is not None:
         section = {"prefill": lambda: bench_prefill(args), "long_decode": bench_long_decode,
-                   "long_prefill": bench_long_prefill, "copy": bench_copy}
+                   "long_prefill": bench_long_prefill, "copy": bench_copy,
+                   "fp8": lambda: bench_fp8(workloads.paged_decode())}
         if args.only in section:
             print(json.dumps({"section": args.only, "result": section[args.only]()}), flush=True)
             return
@@ -727,6 +846,13 @@ def main():
         log(f"[bench] long prefill: {long_prefill}")
         torch.cuda.empty_cache()
 
+    fp8 = None
+    if not args.no_fp8:
+        log("[bench] FP8 indexer cache (132 B/token) on the same workloads")
+        fp8 = bench_fp8(case)
+        log(f"[bench] fp8: {fp8}")
+        torch.cuda.empty_cache()
+
     copy = bench_copy()
     log(f"[bench] device copy: {copy}")
 
@@ -759,6 +885,7 @@ def main():
         "prefill": prefill,
         "long_decode": long_decode,
         "long_prefill": long_prefill,
+        "fp8": fp8,
         "device_copy": copy,
         "cpu_baseline": cpu,
     }
