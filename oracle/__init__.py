@@ -60,6 +60,9 @@ independently of its code.  Function -> pin (test file):
 * fp8.write_rows / insert / gather -- hand-worked 132-byte offsets, canaries,
   slot -1, round trip; fp8.mqa_logits / paged_mqa_logits -- exact rational
   arithmetic, a closed form, 2**m scaling, paged == dense (test_oracle_fp8)
+* rope.apply_rope / quantize_rope -- hand-worked rotations, exact rational
+  fp32 rounding of every product and sum (a fused-multiply-add copy must
+  fail), identities, the complex-rotation closed form (test_oracle_rope)
 
 The pins of the comparison rules and of A are also run against copies of the
 functions with one planted mistake each, and must reject every copy.  The
@@ -68,4 +71,4 @@ of zero, scale byte order) are pinned by the hand-worked bytes derived from the
 adopted reading.
 """
 
-from . import mxfp4, paged_cache, logits, topk, tolerance, fp8  # noqa: F401
+from . import mxfp4, paged_cache, logits, topk, tolerance, fp8, rope  # noqa: F401
