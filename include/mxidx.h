@@ -5,6 +5,7 @@
  * is stored in MXFP4:
  *
  *   idx_quantize        rows of 128 values -> MXFP4 rows (the FP4 query)
+ *   idx_quantize_rope   the same after the query's RoPE (fused)
  *   idx_insert          K rows -> MXFP4 -> paged cache through a slot mapping
  *   idx_gather          paged cache -> contiguous MXFP4 K (prefill)
  *   idx_logits_prefill  logit[t,s] = sum_h w[t,h] * max(0, q[t,h] . k[s]), dense K
@@ -124,6 +125,29 @@ int idx_init(int device);
  * Bytes are bit-exact to the encode rule above. */
 int idx_quantize(const void* x, int dtype, int64_t rows, int64_t row_stride,
                  uint8_t* values, uint8_t* scales, hipStream_t stream);
+
+/* idx_quantize_rope -- the query's rotary position embedding fused into its
+ * MXFP4 encode (the fused q-rope-mxfp4 kernel that P1 "Notes" proposes; the
+ * pages give no RoPE layout, so this call takes the following one).
+ *   x: [T*H, row_stride] rows as for idx_quantize; row r = t*H + h belongs to
+ *      query token t = r / H.
+ *   cos_table, sin_table: [table_rows, rope_dim/2] fp32, contiguous, 16-byte
+ *      aligned; positions: [T] int64 choosing token t's table row (NULL: row t,
+ *      which needs table_rows >= T).  A row whose position lies outside
+ *      [0, table_rows) is encoded unrotated.
+ *   rope_dim: the first rope_dim of the 128 dims are rotated, 0 <= rope_dim <=
+ *      128, a multiple of 16 (0: idx_quantize's bytes).
+ *   rope_mode: IDX_ROPE_NEOX rotates the pairs (j, j + rope_dim/2),
+ *      IDX_ROPE_INTERLEAVED the pairs (2j, 2j+1), each by angle j:
+ *      a' = a*cos - b*sin, b' = b*cos + a*sin, every product and sum rounded to
+ *      fp32 (no fused multiply-add); the rotated row is then encoded as an
+ *      fp32 row by the rule above.
+ *   values [T*H, 64], scales [T*H, 4] uint8 out. */
+typedef enum { IDX_ROPE_NEOX = 0, IDX_ROPE_INTERLEAVED = 1 } idx_rope_mode;
+int idx_quantize_rope(const void* x, int dtype, int64_t T, int H, int64_t row_stride,
+                      const float* cos_table, const float* sin_table, int64_t table_rows,
+                      const int64_t* positions, int rope_dim, int rope_mode, uint8_t* values,
+                      uint8_t* scales, hipStream_t stream);
 
 /* idx_insert -- quantize K rows and scatter them into the paged cache
  * (the indexer K quant-and-cache kernel of P1 "Changes"; slot -1 = no write,

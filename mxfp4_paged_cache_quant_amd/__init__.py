@@ -17,6 +17,7 @@ __all__ = [
     "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged",
     "logits_paged_insert", "topk", "topk_workspace_bytes", "topk_workspace", "topk_ws",
     "topk_noalloc", "topk_merge", "TOPK_NOALLOC_MAX_WORKSPACE",
+    "quantize_rope", "ROPE_NEOX", "ROPE_INTERLEAVED",
     "quantize_fp8", "insert_fp8", "gather_fp8", "logits_prefill_fp8", "logits_paged_fp8",
     "FP8_ROW_BYTES", "FP8_SCALE_F32", "FP8_SCALE_POW2",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
@@ -32,6 +33,7 @@ MAX_HEADS = 128
 TOPK_NOALLOC_MAX_WORKSPACE = 36 << 20
 FP8_ROW_BYTES = 132
 FP8_SCALE_F32, FP8_SCALE_POW2 = 0, 1
+ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 
 IDX_BF16, IDX_F32 = 0, 1
 
@@ -49,6 +51,8 @@ EXPORTS = {
     "idx_init": (_int, [_int]),
     "idx_arch_supported": (_int, [ctypes.c_char_p]),
     "idx_quantize": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "idx_quantize_rope": (_int, [_c_void_p, _int, _i64, _int, _i64, _c_void_p, _c_void_p, _i64,
+                                 _c_void_p, _int, _int, _c_void_p, _c_void_p, _c_void_p]),
     "idx_insert": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int, _c_void_p]),
     "idx_insert_quantize": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int,
                                    _c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
@@ -191,6 +195,42 @@ def quantize(x, values=None, scales=None, stream=None):
         raise MxidxError("values/scales must be contiguous [rows, 64] / [rows, 4]")
     _check(lib().idx_quantize(_ptr(x), code, rows, stride, _ptr(values), _ptr(scales), _stream(stream)),
            "idx_quantize")
+    return values, scales
+
+
+def quantize_rope(q, cos, sin, rope_dim, mode="neox", positions=None, values=None, scales=None,
+                  stream=None):
+    """RoPE on the first ``rope_dim`` dims of each head of q [T, H, 128] (cos / sin
+    fp32 [table_rows, rope_dim/2], table row positions[t] or t; ``mode`` "neox" or
+    "interleaved"), then MXFP4: returns (values u8 [T, H, 64], scales u8 [T, H, 4])."""
+    torch = _torch()
+    if q.dim() != 3:
+        raise MxidxError("q must be [T, H, 128]")
+    T, H = q.shape[0], q.shape[1]
+    rows, stride, code = _rows_view(q, "q")
+    for name, t in (("cos", cos), ("sin", sin)):
+        _dev(t, name, torch.float32)
+        if not t.is_contiguous() or t.dim() != 2 or t.shape[1] != rope_dim // 2:
+            raise MxidxError(f"{name} must be a contiguous fp32 [table_rows, rope_dim/2]")
+    if cos.shape != sin.shape:
+        raise MxidxError("cos and sin tables must have the same shape")
+    if positions is not None:
+        _dev(positions, "positions", torch.int64)
+        if positions.numel() != T or not positions.is_contiguous():
+            raise MxidxError("positions must be a contiguous int64 [T]")
+    if values is None:
+        values = torch.empty((T, H, CODE_BYTES), dtype=torch.uint8, device=q.device)
+    if scales is None:
+        scales = torch.empty((T, H, SCALE_BYTES), dtype=torch.uint8, device=q.device)
+    _dev(values, "values", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    if values.numel() != rows * CODE_BYTES or scales.numel() != rows * SCALE_BYTES or \
+            not values.is_contiguous() or not scales.is_contiguous():
+        raise MxidxError("values/scales must be contiguous [T, H, 64] / [T, H, 4]")
+    mode_code = {"neox": ROPE_NEOX, "interleaved": ROPE_INTERLEAVED}[mode]
+    _check(lib().idx_quantize_rope(_ptr(q), code, T, H, stride, _ptr(cos), _ptr(sin), cos.shape[0],
+                                   _ptr(positions), rope_dim, mode_code, _ptr(values), _ptr(scales),
+                                   _stream(stream)), "idx_quantize_rope")
     return values, scales
 
 

@@ -100,6 +100,31 @@ int idx_quantize(const void* x, int dtype, int64_t rows, int64_t row_stride, uin
   return launched(mxidx::launch_quantize(x, dtype == IDX_F32, rows, row_stride, values, scales, stream));
 }
 
+int idx_quantize_rope(const void* x, int dtype, int64_t T, int H, int64_t row_stride,
+                      const float* cos_table, const float* sin_table, int64_t table_rows,
+                      const int64_t* positions, int rope_dim, int rope_mode, uint8_t* values,
+                      uint8_t* scales, hipStream_t stream) {
+  if (T < 0 || H < 1 || T > ((int64_t)1 << 40)) return IDX_ERR_ARG;
+  const int64_t rows = T * H;
+  int st = check_rows_input(x, dtype, rows, row_stride);
+  if (st != IDX_OK) return st;
+  if (rope_dim < 0 || rope_dim > IDX_HEAD_DIM || rope_dim % 16 != 0) return IDX_ERR_ARG;
+  if (rope_mode != IDX_ROPE_NEOX && rope_mode != IDX_ROPE_INTERLEAVED) return IDX_ERR_ARG;
+  if (table_rows < 0) return IDX_ERR_ARG;
+  if (rows == 0) return IDX_OK;
+  if (!values || !scales || !aligned(values, 4)) return IDX_ERR_ARG;
+  if (rope_dim > 0) {
+    if (!cos_table || !sin_table || !aligned(cos_table, 16) || !aligned(sin_table, 16))
+      return IDX_ERR_ARG;
+    if (positions ? !aligned(positions, 8) : table_rows < T) return IDX_ERR_ARG;
+  }
+  if ((st = gate_current()) != IDX_OK) return st;
+  return launched(mxidx::launch_quantize_rope(x, dtype == IDX_F32, rows, row_stride, H, cos_table,
+                                              sin_table, table_rows, positions, rope_dim,
+                                              rope_mode == IDX_ROPE_INTERLEAVED, values, scales,
+                                              stream));
+}
+
 int idx_insert(const void* k, int dtype, int64_t num_tokens, int64_t k_row_stride,
                const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages, int page_size,
                hipStream_t stream) {

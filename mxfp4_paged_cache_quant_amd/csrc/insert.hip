@@ -15,6 +15,7 @@
 // which divides by the power-of-two scale and rounds to nearest even, keeping
 // the sign of zero.  Each lane stores 4 code bytes (a row's 64 code bytes are
 // one coalesced 64-byte segment); lanes 0,4,8,12 of a row store the 4 scale bytes.
+// The query encoder can rotate the rows first (RoPE, in fp32).
 #include "common.hpp"
 #include "launch.hpp"
 #include "mxfp4_encode.hpp"
@@ -39,6 +40,15 @@ struct Bf16In {
     }
     return m << 16;
   }
+  // the 8 elements as fp32 values (exact)
+  __device__ __forceinline__ void values(float (&f)[8]) const {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
   __device__ __forceinline__ uint32_t encode(float scale) const {
     uint32_t out = 0;
     out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, v.x), scale, 0);
@@ -55,6 +65,11 @@ struct F32In {
     const float* p = static_cast<const float*>(base) + row * stride + 8 * sub;
     lo = *reinterpret_cast<const uint4*>(p);
     hi = *reinterpret_cast<const uint4*>(p + 4);
+  }
+  __device__ __forceinline__ void values(float (&f)[8]) const {
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = __uint_as_float(w[i]);
   }
   __device__ __forceinline__ uint32_t amax_bits() const {
     const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -78,10 +93,7 @@ constexpr int kRowsPerBlock = 16;   // 256 threads, 16 lanes per row
 // Encode row `row` of x (16 lanes, lane `sub` takes elements 8*sub..8*sub+7)
 // into 64 code bytes at cdst and 4 scale bytes at sdst.
 template <typename In>
-__device__ __forceinline__ void encode_row(const void* __restrict__ x, int64_t row, int64_t stride,
-                                           int sub, uint8_t* cdst, uint8_t* sdst) {
-  In in;
-  in.load(x, row, stride, sub);
+__device__ __forceinline__ void encode_loaded(const In& in, int sub, uint8_t* cdst, uint8_t* sdst) {
   uint32_t a = in.amax_bits();
   a = max(a, (uint32_t)__shfl_xor((int)a, 1));
   a = max(a, (uint32_t)__shfl_xor((int)a, 2));
@@ -90,6 +102,100 @@ __device__ __forceinline__ void encode_row(const void* __restrict__ x, int64_t r
   const uint32_t codes = in.encode(scale);
   *reinterpret_cast<uint32_t*>(cdst + 4 * sub) = codes;
   if ((sub & 3) == 0) sdst[sub >> 2] = (uint8_t)(E + 127);
+}
+
+template <typename In>
+__device__ __forceinline__ void encode_row(const void* __restrict__ x, int64_t row, int64_t stride,
+                                           int sub, uint8_t* cdst, uint8_t* sdst) {
+  In in;
+  in.load(x, row, stride, sub);
+  encode_loaded(in, sub, cdst, sdst);
+}
+
+// Fused query RoPE + MXFP4 encode (P1 "Notes": a fused q-rope-mxfp4 kernel).
+// Row r = t*H + h of q; the first rope_dim of its 128 elements are rotated in
+// pairs -- (j, j + rope_dim/2) (neox) or (2j, 2j+1) (interleaved) -- by the
+// angle j of table row positions[t] (t when positions is null):
+//   a' = a*cos - b*sin,  b' = b*cos + a*sin,
+// each product and each sum rounded to fp32 (no fused multiply-add), then the
+// row is encoded as an fp32 row.  A row whose position lies outside the table
+// is encoded unrotated.  rope_dim is a multiple of 16, so each lane's 8
+// elements are all rotated or all not, and a neox lane's partner elements sit
+// in one other lane of the row (lane sub +- rope_dim/16), fetched by shuffles.
+__device__ __forceinline__ float rot_a(float a, float b, float c, float s) {
+#pragma clang fp contract(off)
+  return a * c - b * s;
+}
+__device__ __forceinline__ float rot_b(float a, float b, float c, float s) {
+#pragma clang fp contract(off)
+  return b * c + a * s;
+}
+
+template <typename In>
+__global__ __launch_bounds__(256) void mxfp4_rope_rows_kernel(
+    const void* __restrict__ x, int64_t rows, int64_t stride, int H, const float* __restrict__ cos_t,
+    const float* __restrict__ sin_t, int64_t table_rows, const int64_t* __restrict__ positions,
+    int rope_dim, int interleaved, uint8_t* __restrict__ dst_codes, uint8_t* __restrict__ dst_scales) {
+  const int sub = threadIdx.x & 15;
+  const int half = rope_dim >> 1;
+  const int hl = half >> 3;                       // lanes per half of the rotated range
+  for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4); row < rows;
+       row += (int64_t)gridDim.x * kRowsPerBlock) {
+    In in;
+    in.load(x, row, stride, sub);
+    float v[8];
+    in.values(v);
+    if (rope_dim > 0) {                           // uniform over the launch
+      const int64_t t = row / H;
+      const int64_t p = positions ? positions[t] : t;
+      const bool ok = p >= 0 && p < table_rows;   // same for the row's 16 lanes
+      float pv[8];
+      if (!interleaved) {
+        const int partner = sub < hl ? sub + hl : sub - hl;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = __shfl(v[i], partner, 16);
+      }
+      if (ok && sub < (rope_dim >> 3)) {
+        const float* cr = cos_t + p * half;
+        const float* sr = sin_t + p * half;
+        if (interleaved) {
+          // pairs (8sub + 2i, 8sub + 2i + 1), angle index 4sub + i
+          const float4 c = *reinterpret_cast<const float4*>(cr + 4 * sub);
+          const float4 s = *reinterpret_cast<const float4*>(sr + 4 * sub);
+          const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = v[2 * i], b = v[2 * i + 1];
+            v[2 * i] = rot_a(a, b, cc[i], ss[i]);
+            v[2 * i + 1] = rot_b(a, b, cc[i], ss[i]);
+          }
+        } else {
+          // this lane holds elements 8sub..8sub+7: the a's of angles 8sub.. (sub < hl)
+          // or the b's of angles 8(sub - hl).. ; the partner lane holds the others
+          const int j0 = 8 * (sub < hl ? sub : sub - hl);
+          const float4 c0 = *reinterpret_cast<const float4*>(cr + j0);
+          const float4 c1 = *reinterpret_cast<const float4*>(cr + j0 + 4);
+          const float4 s0 = *reinterpret_cast<const float4*>(sr + j0);
+          const float4 s1 = *reinterpret_cast<const float4*>(sr + j0 + 4);
+          const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+          const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+          if (sub < hl) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = rot_a(v[i], pv[i], cc[i], ss[i]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = rot_b(pv[i], v[i], cc[i], ss[i]);
+          }
+        }
+      }
+    }
+    F32In r;
+    r.lo = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                      __float_as_uint(v[3]));
+    r.hi = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                      __float_as_uint(v[7]));
+    encode_loaded(r, sub, dst_codes + row * kCodeBytes, dst_scales + row * kScaleBytes);
+  }
 }
 
 // Paged destination of a slot: codes at page*4352 + off*64, scales at
@@ -187,6 +293,22 @@ hipError_t launch_quantize(const void* x, bool f32, int64_t rows, int64_t row_st
   else
     hipLaunchKernelGGL((mxfp4_rows_kernel<Bf16In, false>), dim3(grid), dim3(256), 0, stream, x, rows,
                        row_stride, nullptr, 0, values, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rope(const void* x, bool f32, int64_t rows, int64_t row_stride, int H,
+                                const float* cos_t, const float* sin_t, int64_t table_rows,
+                                const int64_t* positions, int rope_dim, bool interleaved,
+                                uint8_t* values, uint8_t* scales, hipStream_t stream) {
+  const int grid = grid_for_rows(rows);
+  if (f32)
+    hipLaunchKernelGGL((mxfp4_rope_rows_kernel<F32In>), dim3(grid), dim3(256), 0, stream, x, rows,
+                       row_stride, H, cos_t, sin_t, table_rows, positions, rope_dim,
+                       interleaved ? 1 : 0, values, scales);
+  else
+    hipLaunchKernelGGL((mxfp4_rope_rows_kernel<Bf16In>), dim3(grid), dim3(256), 0, stream, x, rows,
+                       row_stride, H, cos_t, sin_t, table_rows, positions, rope_dim,
+                       interleaved ? 1 : 0, values, scales);
   return hipGetLastError();
 }
 

@@ -11,6 +11,13 @@ namespace mxidx {
 hipError_t launch_quantize(const void* x, bool f32, int64_t rows, int64_t row_stride,
                            uint8_t* values, uint8_t* scales, hipStream_t stream);
 
+// Query RoPE (first rope_dim dims, neox or interleaved pairs, fp32) fused into
+// the MXFP4 encode; rows = T*H, row r of token r / H.
+hipError_t launch_quantize_rope(const void* x, bool f32, int64_t rows, int64_t row_stride, int H,
+                                const float* cos_t, const float* sin_t, int64_t table_rows,
+                                const int64_t* positions, int rope_dim, bool interleaved,
+                                uint8_t* values, uint8_t* scales, hipStream_t stream);
+
 hipError_t launch_insert(const void* k, bool f32, int64_t num_tokens, int64_t row_stride,
                          const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
                          hipStream_t stream);

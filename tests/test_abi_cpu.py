@@ -259,3 +259,18 @@ def test_fp8_argument_validation(L):
     assert pg(P, P, P, 4, 64, P, 1, P, 0, 1, 32, 64, P, 64, 1, None) == OK        # no sequences
     if not _has_gpu():
         assert pg(P, P, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 64, 1, None) == ERR_NO_DEVICE
+
+
+def test_quantize_rope_argument_validation(L):
+    f = L.idx_quantize_rope
+    assert f(P, 0, 4, 8, 128, P, P2, 4, None, 24, 0, P, P2, None) == ERR_ARG     # rope_dim % 16
+    assert f(P, 0, 4, 8, 128, P, P2, 4, None, 144, 0, P, P2, None) == ERR_ARG    # rope_dim > 128
+    assert f(P, 0, 4, 8, 128, P, P2, 4, None, 64, 2, P, P2, None) == ERR_ARG     # mode
+    assert f(P, 0, 4, 8, 128, P, P2, 3, None, 64, 0, P, P2, None) == ERR_ARG     # table < T, no positions
+    assert f(P, 0, 4, 8, 128, MIS, P2, 4, None, 64, 0, P, P2, None) == ERR_ARG   # misaligned cos
+    assert f(P, 0, 4, 8, 128, None, None, 0, None, 64, 0, P, P2, None) == ERR_ARG  # no tables
+    assert f(P, 0, 4, 0, 128, P, P2, 4, None, 64, 0, P, P2, None) == ERR_ARG     # H = 0
+    assert f(None, 0, 0, 8, 128, None, None, 0, None, 64, 0, None, None, None) == OK   # T = 0
+    if not _has_gpu():
+        assert f(P, 0, 4, 8, 128, None, None, 0, None, 0, 0, P, P2, None) == ERR_NO_DEVICE  # rope_dim 0
+        assert f(P, 0, 4, 8, 128, P, P2, 1, P, 64, 1, P, P2, None) == ERR_NO_DEVICE       # positions
