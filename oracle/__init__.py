@@ -63,6 +63,9 @@ independently of its code.  Function -> pin (test file):
 * rope.apply_rope / quantize_rope -- hand-worked rotations, exact rational
   fp32 rounding of every product and sum (a fused-multiply-add copy must
   fail), identities, the complex-rotation closed form (test_oracle_rope)
+* kpool.write_mask / pool_indices / pooled_rows / insert -- P3's printed
+  bookkeeping worked by hand, plain-loop brute force, closed forms (mean,
+  selection, shift invariance), masked writes only (test_oracle_kpool)
 
 The pins of the comparison rules and of A are also run against copies of the
 functions with one planted mistake each, and must reject every copy.  The
@@ -71,4 +74,4 @@ of zero, scale byte order) are pinned by the hand-worked bytes derived from the
 adopted reading.
 """
 
-from . import mxfp4, paged_cache, logits, topk, tolerance, fp8, rope  # noqa: F401
+from . import mxfp4, paged_cache, logits, topk, tolerance, fp8, rope, kpool  # noqa: F401
