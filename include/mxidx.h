@@ -6,6 +6,7 @@
  *
  *   idx_quantize        rows of 128 values -> MXFP4 rows (the FP4 query)
  *   idx_quantize_rope   the same after the query's RoPE (fused)
+ *   idx_kpool_insert    kpool tokens pooled into one K row, then inserted
  *   idx_insert          K rows -> MXFP4 -> paged cache through a slot mapping
  *   idx_gather          paged cache -> contiguous MXFP4 K (prefill)
  *   idx_logits_prefill  logit[t,s] = sum_h w[t,h] * max(0, q[t,h] . k[s]), dense K
@@ -333,6 +334,38 @@ int idx_logits_paged_fp8(const uint8_t* q_values, const float* weights, const ui
                          int64_t bt_row_stride, const int32_t* context_lens, int B, int next_n,
                          int H, int64_t max_context_len, float* logits, int64_t logits_row_stride,
                          int clean, hipStream_t stream);
+
+/* idx_kpool_insert -- the pooled indexer-K insert of P3
+ * "vllm.models.glm5next.nvidia.sparse_indexer", section "_kpool_compress_insert":
+ * kpool consecutive tokens pooled into one K row, quantized and written at a
+ * pool slot.  As P3 prints it: slot_mapping [n] int64 is pool-granular (only the
+ * last token of a complete pool carries a slot >= 0); position i is written iff
+ * slot_mapping[i] >= 0 and i >= kpool - 1, from the pool of tokens
+ * i - kpool + 1 .. i; with n < kpool nothing is written.  The pooling, which the
+ * page does not print, is read here as a per-dimension softmax gate:
+ *   pooled[d] = sum_j softmax_j(gate_score[i-kpool+1+j, d] + ape[j, d]) * k[i-kpool+1+j, d]
+ * computed in fp32 (maximum subtracted, exp, both sums in token order, one
+ * division) -- so the bytes written may differ from an exact computation's in
+ * the last place of the pooled value, i.e. by one code step where it lies
+ * within that distance of a rounding boundary.
+ *   k:            [n, k_row_stride] bf16 or fp32 (as for idx_insert).
+ *   gate_score:   [n, 128] fp32, ape: [kpool, 128] fp32, both 16-byte aligned.
+ *   kpool:        1 .. IDX_KPOOL_MAX.
+ *   cache_format: IDX_CACHE_MXFP4 (68-byte rows, the cache of idx_insert) or
+ *                 IDX_CACHE_FP8 (132-byte rows, the cache of idx_insert_fp8, with
+ *                 fp8_scale_fmt as there; P3's round_scale = IDX_FP8_SCALE_POW2).
+ *                 fp8_scale_fmt must be valid (it is ignored for MXFP4).
+ *   cache:        [num_pages, 64 * row bytes], 16-byte aligned; slots outside it
+ *                 write nothing.  page_size must be 64.
+ *   compressed:   NULL, or [n, 128] fp32 out (16-byte aligned): the pooled rows
+ *                 of the written positions (P3's return_compressed); other rows
+ *                 are left untouched. */
+typedef enum { IDX_CACHE_MXFP4 = 0, IDX_CACHE_FP8 = 1 } idx_cache_format;
+#define IDX_KPOOL_MAX 1024
+int idx_kpool_insert(const void* k, int dtype, int64_t n, int64_t k_row_stride,
+                     const float* gate_score, const float* ape, const int64_t* slot_mapping,
+                     int kpool, int cache_format, int fp8_scale_fmt, uint8_t* cache,
+                     int64_t num_pages, int page_size, float* compressed, hipStream_t stream);
 
 /* idx_topk -- per-row top-k column indices (top_k_per_row, P3
  * "SparseAttnIndexerKpool"; exact sets as tested in P2 "Validation").

@@ -17,7 +17,7 @@ __all__ = [
     "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged",
     "logits_paged_insert", "topk", "topk_workspace_bytes", "topk_workspace", "topk_ws",
     "topk_noalloc", "topk_merge", "TOPK_NOALLOC_MAX_WORKSPACE",
-    "quantize_rope", "ROPE_NEOX", "ROPE_INTERLEAVED",
+    "quantize_rope", "ROPE_NEOX", "ROPE_INTERLEAVED", "kpool_insert",
     "quantize_fp8", "insert_fp8", "gather_fp8", "logits_prefill_fp8", "logits_paged_fp8",
     "FP8_ROW_BYTES", "FP8_SCALE_F32", "FP8_SCALE_POW2",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
@@ -78,6 +78,8 @@ EXPORTS = {
     "idx_logits_paged_fp8": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _int, _c_void_p, _i64,
                                     _c_void_p, _int, _int, _int, _i64, _c_void_p, _i64, _int,
                                     _c_void_p]),
+    "idx_kpool_insert": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _int,
+                                _int, _int, _c_void_p, _i64, _int, _c_void_p, _c_void_p]),
     "idx_topk": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p]),
     "idx_topk_workspace_bytes": (ctypes.c_size_t, [_i64, _i64]),
     "idx_topk_ws": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p,
@@ -660,6 +662,38 @@ def logits_paged_fp8(q_values, weights, cache, block_table, context_lens, next_n
                                       _ptr(logits), logits.stride(0), 1 if clean else 0,
                                       _stream(stream)), "idx_logits_paged_fp8")
     return logits
+
+
+def kpool_insert(k, gate_score, ape, slot_mapping, cache, kpool, fmt="mxfp4", round_scale=False,
+                 return_compressed=False, stream=None):
+    """Pool kpool consecutive tokens of k [n, 128] (softmax over gate_score [n, 128] +
+    ape [kpool, 128] per dimension) and write the pooled rows of the pool-end
+    positions (slot >= 0, position >= kpool - 1) into ``cache`` (MXFP4
+    [pages, 64*68] or, with fmt="fp8", [pages, 64*132]).  With
+    return_compressed, also returns the fp32 pooled rows [n, 128] (rows of
+    unwritten positions are zero)."""
+    torch = _torch()
+    n, stride, code = _rows_view(k, "k")
+    _dev(gate_score, "gate_score", torch.float32)
+    _dev(ape, "ape", torch.float32)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(cache, "cache", torch.uint8)
+    if gate_score.shape != (n, HEAD_DIM) or not gate_score.is_contiguous():
+        raise MxidxError("gate_score must be a contiguous fp32 [n, 128]")
+    if ape.shape != (kpool, HEAD_DIM) or not ape.is_contiguous():
+        raise MxidxError("ape must be a contiguous fp32 [kpool, 128]")
+    if slot_mapping.numel() != n or not slot_mapping.is_contiguous():
+        raise MxidxError("slot_mapping must be a contiguous int64 [n]")
+    row = {"mxfp4": ROW_BYTES, "fp8": FP8_ROW_BYTES}[fmt]
+    if not cache.is_contiguous() or cache.numel() % (PAGE_SIZE * row) != 0:
+        raise MxidxError(f"cache must be a contiguous uint8 [num_pages, 64*{row}]")
+    comp = torch.zeros((n, HEAD_DIM), dtype=torch.float32, device=k.device) if return_compressed else None
+    _check(lib().idx_kpool_insert(_ptr(k), code, n, stride, _ptr(gate_score), _ptr(ape),
+                                  _ptr(slot_mapping), kpool, 0 if fmt == "mxfp4" else 1,
+                                  FP8_SCALE_POW2 if round_scale else FP8_SCALE_F32, _ptr(cache),
+                                  cache.numel() // (PAGE_SIZE * row), PAGE_SIZE, _ptr(comp),
+                                  _stream(stream)), "idx_kpool_insert")
+    return (cache, comp) if return_compressed else cache
 
 
 def topk_noalloc(logits, ks, ke, k, out=None, stream=None):

@@ -397,6 +397,29 @@ int idx_logits_paged_fp8(const uint8_t* q_values, const float* weights, const ui
                                                  stream));
 }
 
+int idx_kpool_insert(const void* k, int dtype, int64_t n, int64_t k_row_stride,
+                     const float* gate_score, const float* ape, const int64_t* slot_mapping,
+                     int kpool, int cache_format, int fp8_scale_fmt, uint8_t* cache,
+                     int64_t num_pages, int page_size, float* compressed, hipStream_t stream) {
+  int st = check_rows_input(k, dtype, n, k_row_stride);
+  if (st != IDX_OK) return st;
+  if (kpool < 1 || kpool > IDX_KPOOL_MAX) return IDX_ERR_ARG;
+  if (cache_format != IDX_CACHE_MXFP4 && cache_format != IDX_CACHE_FP8) return IDX_ERR_ARG;
+  if (fp8_scale_fmt != IDX_FP8_SCALE_F32 && fp8_scale_fmt != IDX_FP8_SCALE_POW2) return IDX_ERR_ARG;
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0) return IDX_ERR_ARG;
+  if (n < kpool) return IDX_OK;                 // no pool completes
+  if (!gate_score || !aligned(gate_score, 16) || !ape || !aligned(ape, 16) || !slot_mapping ||
+      !aligned(slot_mapping, 8))
+    return IDX_ERR_ARG;
+  if (compressed && !aligned(compressed, 16)) return IDX_ERR_ARG;
+  if (num_pages > 0 && (!cache || !aligned(cache, 16))) return IDX_ERR_ARG;
+  if ((st = gate_current()) != IDX_OK) return st;
+  return launched(mxidx::launch_kpool_insert(k, dtype == IDX_F32, n, k_row_stride, gate_score, ape,
+                                             slot_mapping, kpool, cache_format == IDX_CACHE_FP8,
+                                             fp8_scale_fmt == IDX_FP8_SCALE_POW2, cache, num_pages,
+                                             compressed, stream));
+}
+
 int idx_topk_noalloc(const float* logits, int64_t rows, int64_t logits_row_stride,
                      const int32_t* ks, const int32_t* ke, int k, int32_t* out_idx,
                      hipStream_t stream) {

@@ -1,0 +1,169 @@
+// Pooled ("kpool") indexer-K insert (P3 "vllm.models.glm5next.nvidia.
+// sparse_indexer", section "_kpool_compress_insert"): kpool consecutive tokens
+// are pooled into one K row, which is quantized and written at a pool slot.
+//
+// Bookkeeping, as P3 prints it: slot_mapping is pool-granular (only the last
+// token of a complete pool carries a slot >= 0); every position i is a
+// candidate pool end and is written iff slot_mapping[i] >= 0 and
+// i >= kpool - 1; its pool is tokens i - kpool + 1 .. i; nothing completes when
+// n < kpool.  Pooling (not printed; the reading taken): per dimension d,
+//   pooled[d] = sum_j softmax_j(gate[i-kpool+1+j, d] + ape[j, d]) * k[i-kpool+1+j, d],
+// in fp32: z = gate + ape, the pool's maximum subtracted, exp, and the two
+// sums accumulated over j in order, then one division.  The row is then
+// encoded as the cache's format -- MXFP4 (the block-scaled rule of
+// mxfp4_encode.hpp) or FP8 (fp8_encode.hpp, with P3's round_scale as the
+// power-of-two scale) -- and written to its slot; slots outside the cache
+// write nothing.  The pooled fp32 rows can also be returned (P3's
+// return_compressed).
+//
+// Work mapping: 16 lanes per position, 8 dimensions per lane (the row
+// encoders' layout); each lane streams its 8 dims of the pool's kpool tokens
+// twice (maximum, then the weighted sums) -- 2 kpool short reads that stay
+// in cache for the neighbouring positions, whose pools overlap.
+#include "common.hpp"
+#include "fp8_encode.hpp"
+#include "launch.hpp"
+#include "mxfp4_encode.hpp"
+
+namespace mxidx {
+namespace {
+
+constexpr int kKpRowsPerBlock = 16;
+
+template <bool kF32>
+__device__ __forceinline__ void load8(const void* base, int64_t row, int64_t stride, int sub,
+                                      float (&v)[8]) {
+  if constexpr (kF32) {
+    const float* p = static_cast<const float*>(base) + row * stride + 8 * sub;
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) +
+                                                    row * stride + 8 * sub);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// kFmt 0: MXFP4 cache (68 B rows), 1: FP8 cache (132 B rows).
+template <bool kF32, int kFmt>
+__global__ __launch_bounds__(256) void kpool_insert_kernel(
+    const void* __restrict__ k, int64_t n, int64_t stride, const float* __restrict__ gate,
+    const float* __restrict__ ape, const int64_t* __restrict__ slot_mapping, int kpool,
+    int64_t num_slots, int pow2, uint8_t* __restrict__ cache, float* __restrict__ compressed) {
+  const int sub = threadIdx.x & 15;
+  for (int64_t i = (int64_t)blockIdx.x * kKpRowsPerBlock + (threadIdx.x >> 4); i < n;
+       i += (int64_t)gridDim.x * kKpRowsPerBlock) {
+    const int64_t slot = slot_mapping[i];         // same for the row's 16 lanes
+    if (i < kpool - 1 || slot < 0 || slot >= num_slots) continue;
+    const int64_t first = i - kpool + 1;
+    float m[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) m[d] = neg_inf();
+    for (int j = 0; j < kpool; ++j) {
+      float g[8], a[8];
+      load8f(gate + (first + j) * kHeadDim + 8 * sub, g);
+      load8f(ape + (int64_t)j * kHeadDim + 8 * sub, a);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) m[d] = fmaxf(m[d], g[d] + a[d]);
+    }
+    float ssum[8], acc[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) ssum[d] = acc[d] = 0.f;
+    for (int j = 0; j < kpool; ++j) {
+      float g[8], a[8], kv[8];
+      load8f(gate + (first + j) * kHeadDim + 8 * sub, g);
+      load8f(ape + (int64_t)j * kHeadDim + 8 * sub, a);
+      load8<kF32>(k, first + j, stride, sub, kv);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const float e = expf((g[d] + a[d]) - m[d]);
+        ssum[d] += e;
+        acc[d] += e * kv[d];
+      }
+    }
+    float v[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) v[d] = acc[d] / ssum[d];
+    if (compressed) {
+      float* c = compressed + i * kHeadDim + 8 * sub;
+      *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(c + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    const int64_t page = slot / kPage, off = slot % kPage;
+    uint32_t amax = 0;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) amax = max(amax, __float_as_uint(v[d]) & 0x7fffffffu);
+    if constexpr (kFmt == 0) {
+      // MXFP4: 4 lanes per 32-element block
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+      const int E = block_exponent(amax);
+      const float sc = block_divisor(amax, E);
+      uint32_t out = 0;
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], sc, 0);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], sc, 1);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], sc, 2);
+      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], sc, 3);
+      uint8_t* base = cache + page * kPageBytes;
+      *reinterpret_cast<uint32_t*>(base + off * kCodeBytes + 4 * sub) = out;
+      if ((sub & 3) == 0) base[kPageCodeBytes + off * kScaleBytes + (sub >> 2)] = (uint8_t)(E + 127);
+    } else {
+      // FP8: one scale for the row's 16 lanes
+#pragma unroll
+      for (int msk = 1; msk < 16; msk <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, msk));
+      const float s = fp8_row_scale(amax, pow2 != 0);
+      float y[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) y[d] = v[d] / s;
+      uint8_t* base = cache + page * kF8PageBytes;
+      *reinterpret_cast<uint2*>(base + off * kF8Row + 8 * sub) =
+          make_uint2(pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7]));
+      if (sub == 0) *reinterpret_cast<float*>(base + kF8PageValues + off * 4) = s;
+    }
+  }
+}
+
+template <bool kF32, int kFmt>
+hipError_t launch_kp(const void* k, int64_t n, int64_t stride, const float* gate, const float* ape,
+                     const int64_t* slots, int kpool, int64_t num_pages, bool pow2, uint8_t* cache,
+                     float* compressed, hipStream_t stream) {
+  const int64_t blocks = (n + kKpRowsPerBlock - 1) / kKpRowsPerBlock;
+  const int grid = (int)(blocks < 256 * 32 ? blocks : 256 * 32);
+  hipLaunchKernelGGL((kpool_insert_kernel<kF32, kFmt>), dim3(grid), dim3(256), 0, stream, k, n,
+                     stride, gate, ape, slots, kpool, num_pages * kPage, pow2 ? 1 : 0, cache,
+                     compressed);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_kpool_insert(const void* k, bool f32, int64_t n, int64_t row_stride,
+                               const float* gate, const float* ape, const int64_t* slot_mapping,
+                               int kpool, bool fp8, bool pow2, uint8_t* cache, int64_t num_pages,
+                               float* compressed, hipStream_t stream) {
+  if (f32)
+    return fp8 ? launch_kp<true, 1>(k, n, row_stride, gate, ape, slot_mapping, kpool, num_pages,
+                                    pow2, cache, compressed, stream)
+               : launch_kp<true, 0>(k, n, row_stride, gate, ape, slot_mapping, kpool, num_pages,
+                                    pow2, cache, compressed, stream);
+  return fp8 ? launch_kp<false, 1>(k, n, row_stride, gate, ape, slot_mapping, kpool, num_pages,
+                                   pow2, cache, compressed, stream)
+             : launch_kp<false, 0>(k, n, row_stride, gate, ape, slot_mapping, kpool, num_pages,
+                                   pow2, cache, compressed, stream);
+}
+
+}  // namespace mxidx

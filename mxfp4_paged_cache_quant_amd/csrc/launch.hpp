@@ -80,6 +80,13 @@ hipError_t launch_logits_prefill_fp8(const uint8_t* q_values, const float* weigh
                                      int64_t S, float* logits, int64_t ld, int clean,
                                      hipStream_t stream);
 
+// Pooled (kpool) insert: softmax(gate + ape)-weighted pool of kpool tokens,
+// encoded as MXFP4 (fp8 = false) or FP8 rows, written at pool-end slots.
+hipError_t launch_kpool_insert(const void* k, bool f32, int64_t n, int64_t row_stride,
+                               const float* gate, const float* ape, const int64_t* slot_mapping,
+                               int kpool, bool fp8, bool pow2, uint8_t* cache, int64_t num_pages,
+                               float* compressed, hipStream_t stream);
+
 hipError_t launch_topk_merge(const float* values, const int32_t* indices, int world, int k_in,
                              int64_t rows, int interleave, int k, int32_t* out_idx,
                              hipStream_t stream);

@@ -274,3 +274,17 @@ def test_quantize_rope_argument_validation(L):
     if not _has_gpu():
         assert f(P, 0, 4, 8, 128, None, None, 0, None, 0, 0, P, P2, None) == ERR_NO_DEVICE  # rope_dim 0
         assert f(P, 0, 4, 8, 128, P, P2, 1, P, 64, 1, P, P2, None) == ERR_NO_DEVICE       # positions
+
+
+def test_kpool_insert_argument_validation(L):
+    f = L.idx_kpool_insert
+    assert f(P, 0, 8, 128, P, P2, P, 0, 0, 0, P2, 4, 64, None, None) == ERR_ARG      # kpool 0
+    assert f(P, 0, 8, 128, P, P2, P, 2000, 0, 0, P2, 4, 64, None, None) == ERR_ARG   # kpool too big
+    assert f(P, 0, 8, 128, P, P2, P, 4, 2, 0, P2, 4, 64, None, None) == ERR_ARG      # format
+    assert f(P, 0, 8, 128, P, P2, P, 4, 1, 5, P2, 4, 64, None, None) == ERR_ARG      # fp8 scale format
+    assert f(P, 0, 8, 128, MIS, P2, P, 4, 0, 0, P2, 4, 64, None, None) == ERR_ARG    # misaligned gate
+    assert f(P, 0, 8, 128, P, P2, P, 4, 0, 0, P2, 4, 32, None, None) == ERR_ARG     # page size
+    assert f(P, 0, 8, 128, P, P2, P, 4, 0, 0, P2, 4, 64, MIS, None) == ERR_ARG      # misaligned out
+    assert f(P, 0, 3, 128, None, None, None, 4, 0, 0, None, 4, 64, None, None) == OK  # n < kpool
+    if not _has_gpu():
+        assert f(P, 0, 8, 128, P, P2, P, 4, 1, 1, P2, 4, 64, None, None) == ERR_NO_DEVICE
