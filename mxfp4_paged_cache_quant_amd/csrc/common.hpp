@@ -31,11 +31,13 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, int sa, 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, sa, 0, sb);
 }
 
-// Order-preserving map of fp32 bits to uint32 (larger float -> larger key);
-// -0.0 is first canonicalized to +0.0 so the two compare equal.
+// Order-preserving map of fp32 bits to uint32 (larger float -> larger key),
+// with -0.0 and +0.0 mapped to the same key: non-negative u -> u | 2^31,
+// negative u -> (~u) + 1 = 2^32 - u (so -0.0 -> 2^31, and -x below +0 for every
+// negative x).  Four branch-free instructions: shift, or, shift, xor-add.
 __device__ __forceinline__ uint32_t f32_key(uint32_t u) {
-  u = (u == 0x80000000u) ? 0u : u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t m = (uint32_t)((int32_t)u >> 31);           // all ones for negative
+  return (u ^ (m | 0x80000000u)) + (u >> 31);
 }
 
 // Raw buffer descriptors over a wave-uniform base (kept in scalar registers):
