@@ -10,7 +10,9 @@ plainest reading and states it:
 
 * the caller supplies the angle tables: cos[p, j] and sin[p, j] (float32,
   j < rope_dim / 2) for table row p, and optionally positions[t] choosing the
-  table row of query token t (default: row t);
+  table row of query token t (default: row t); a token whose table row lies
+  outside the table is left unrotated (a safety reading: the pages say
+  nothing of it);
 * the first ``rope_dim`` of the 128 dims of every head are rotated (0 <=
   rope_dim <= 128, a multiple of 16); the others pass through unchanged;
 * pairing: ``neox`` rotates the pairs (j, j + rope_dim/2), ``interleaved``
@@ -54,8 +56,11 @@ def apply_rope(x, cos, sin, rope_dim, mode, positions=None):
     if rope_dim == 0 or T == 0:
         return out
     pos = np.arange(T) if positions is None else np.asarray(positions, dtype=np.int64)
-    c = np.asarray(cos, dtype=np.float32)[pos][:, None, :]      # [T, 1, half]
-    s = np.asarray(sin, dtype=np.float32)[pos][:, None, :]
+    cos = np.asarray(cos, dtype=np.float32)
+    inside = (pos >= 0) & (pos < cos.shape[0])
+    row = np.where(inside, pos, 0)
+    c = cos[row][:, None, :]                                     # [T, 1, half]
+    s = np.asarray(sin, dtype=np.float32)[row][:, None, :]
     ia, ib, _ = rope_pairs(rope_dim, mode)
     a = x[:, :, ia]
     b = x[:, :, ib]
@@ -64,6 +69,7 @@ def apply_rope(x, cos, sin, rope_dim, mode, positions=None):
     bc, as_ = (b * c).astype(np.float32), (a * s).astype(np.float32)
     out[:, :, ia] = (ac - bs).astype(np.float32)
     out[:, :, ib] = (bc + as_).astype(np.float32)
+    out[~inside] = x[~inside]                                    # outside the table: unrotated
     return out
 
 

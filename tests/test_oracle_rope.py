@@ -155,3 +155,18 @@ def test_positions_select_table_rows_and_quantize():
         codes, scales = rope.quantize_rope(x, c, s, 64, mode, positions=pos)
         wc, ws = mxfp4.quantize_rows(a.astype(np.float64))
         assert np.array_equal(codes.reshape(-1, 64), wc) and np.array_equal(scales.reshape(-1, 4), ws)
+
+
+def test_positions_outside_the_table_leave_the_token_unrotated():
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((5, 3, 128)).astype(np.float32).astype(np.float64)
+    c = rng.random((20, 32), dtype=np.float32)
+    s = rng.random((20, 32), dtype=np.float32)
+    pos = np.array([-1, 4, 20, 19, -7])
+    inside = np.array([False, True, False, True, False])
+    for mode in ("neox", "interleaved"):
+        got = rope.apply_rope(x, c, s, 64, mode, positions=pos)
+        assert np.array_equal(got[~inside], x[~inside].astype(np.float32))
+        want = rope.apply_rope(x[inside], c, s, 64, mode, positions=pos[inside])
+        assert np.array_equal(got[inside], want)
+        assert not np.array_equal(got[inside], x[inside].astype(np.float32))
