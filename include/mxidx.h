@@ -14,6 +14,8 @@
  *   idx_topk            per-row top-k column indices over [ks, ke)
  *   idx_topk_ws         the same with a workspace: few long rows split over
  *                       workgroups
+ *   idx_insert_quantize, idx_logits_paged_insert (and their _rope forms, with
+ *                       the query RoPE): a decode step's calls in fewer launches
  *   idx_*_fp8           the FP8 (E4M3) indexer cache the MXFP4 one replaces:
  *                       quantize, insert, gather, dense and paged logits
  *
@@ -150,6 +152,19 @@ int idx_quantize_rope(const void* x, int dtype, int64_t T, int H, int64_t row_st
                       const int64_t* positions, int rope_dim, int rope_mode, uint8_t* values,
                       uint8_t* scales, hipStream_t stream);
 
+/* idx_rope -- the query RoPE of the fused decode-step calls below, with the
+ * meaning of idx_quantize_rope's arguments of the same names (caller-owned
+ * device tables; the struct itself is host memory, read during the call only).
+ * The position of a query token when positions is NULL is stated by each call. */
+typedef struct {
+  const float* cos_table;     /* [table_rows, rope_dim/2] fp32, 16-byte aligned */
+  const float* sin_table;     /* [table_rows, rope_dim/2] fp32, 16-byte aligned */
+  int64_t table_rows;
+  const int64_t* positions;   /* per query token, or NULL */
+  int rope_dim;               /* 0..128, a multiple of 16; 0 rotates nothing */
+  int rope_mode;              /* idx_rope_mode */
+} idx_rope;
+
 /* idx_insert -- quantize K rows and scatter them into the paged cache
  * (the indexer K quant-and-cache kernel of P1 "Changes"; slot -1 = no write,
  * P3 "_kpool_compress_insert").
@@ -180,6 +195,23 @@ int idx_insert_quantize(const void* k, int k_dtype, int64_t num_tokens, int64_t 
                         int page_size, const void* q, int q_dtype, int64_t q_rows,
                         int64_t q_row_stride, uint8_t* q_values, uint8_t* q_scales,
                         hipStream_t stream);
+
+/* idx_insert_quantize_rope -- idx_insert_quantize with the query rows rotated
+ * before their encode (the fused q-rope-mxfp4 step of P1 "Notes" inside the
+ * decode step's one encode launch).
+ *   q_rows = T * q_heads: row r belongs to query token t = r / q_heads;
+ *   rope: required; token t takes table row positions[t] (NULL: row t, which
+ *         needs table_rows >= T); rows outside the table are not rotated.
+ * The outputs are byte-identical to idx_insert followed by idx_quantize_rope
+ * (rope_dim 0: to idx_insert_quantize).  Errors: those of idx_insert_quantize,
+ * plus IDX_ERR_ARG for a missing or invalid rope block or q_rows not a
+ * multiple of q_heads. */
+int idx_insert_quantize_rope(const void* k, int k_dtype, int64_t num_tokens,
+                             int64_t k_row_stride, const int64_t* slot_mapping, uint8_t* cache,
+                             int64_t num_pages, int page_size, const void* q, int q_dtype,
+                             int64_t q_rows, int64_t q_row_stride, int q_heads,
+                             const idx_rope* rope, uint8_t* q_values, uint8_t* q_scales,
+                             hipStream_t stream);
 
 /* idx_gather -- paged cache -> contiguous MXFP4 K (the cp_gather that P1's
  * live-validation comment names as sharing the cache layout).
@@ -266,6 +298,28 @@ int idx_logits_paged_insert(const void* q, const void* k_new, int dtype, const f
                             const int32_t* context_lens, int B, int next_n, int H,
                             int64_t max_context_len, float* logits, int64_t logits_row_stride,
                             int clean, hipStream_t stream);
+
+/* idx_logits_paged_insert_rope -- idx_logits_paged_insert with the query rows
+ * rotated (idx_rope) before the in-kernel encode: the decode step of P1
+ * "Notes"' fused q-rope-mxfp4 kernel, its K quant-and-cache and its paged
+ * logits in one launch.
+ *   rope: required.  positions, when given, is [B*next_n] int64 (row
+ *         b*next_n + i takes table row positions[b*next_n + i]); NULL puts the
+ *         row at its token's position context_lens[b] - next_n + i.  Rows whose
+ *         position lies outside [0, table_rows) are not rotated.  Neox pairing
+ *         needs rope_dim 0, 64 or 128 here (each lane's partner block is then
+ *         one other lane's); interleaved takes any multiple of 16.
+ * Equal, byte for byte and bit for bit, to idx_insert of the new tokens,
+ * idx_quantize_rope of q with those positions, then idx_logits_paged.  Errors:
+ * those of idx_logits_paged_insert, plus IDX_ERR_ARG for a missing or invalid
+ * rope block or an unsupported neox rope_dim. */
+int idx_logits_paged_insert_rope(const void* q, const void* k_new, int dtype,
+                                 const float* weights, uint8_t* cache, int64_t num_pages,
+                                 int page_size, const int32_t* block_table, int64_t bt_row_stride,
+                                 const int32_t* context_lens, int B, int next_n, int H,
+                                 int64_t max_context_len, float* logits,
+                                 int64_t logits_row_stride, int clean, const idx_rope* rope,
+                                 hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * FP8 indexer cache: the format the MXFP4 cache replaces (P1 "Benefit": 132

@@ -17,7 +17,8 @@ __all__ = [
     "quantize", "insert", "insert_quantize", "gather", "logits_prefill", "logits_paged",
     "logits_paged_insert", "topk", "topk_workspace_bytes", "topk_workspace", "topk_ws",
     "topk_noalloc", "topk_merge", "TOPK_NOALLOC_MAX_WORKSPACE",
-    "quantize_rope", "ROPE_NEOX", "ROPE_INTERLEAVED", "kpool_insert",
+    "quantize_rope", "insert_quantize_rope", "logits_paged_insert_rope", "ROPE_NEOX",
+    "ROPE_INTERLEAVED", "kpool_insert",
     "quantize_fp8", "insert_fp8", "gather_fp8", "logits_prefill_fp8", "logits_paged_fp8",
     "FP8_ROW_BYTES", "FP8_SCALE_F32", "FP8_SCALE_POW2",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
@@ -36,6 +37,13 @@ FP8_SCALE_F32, FP8_SCALE_POW2 = 0, 1
 ROPE_NEOX, ROPE_INTERLEAVED = 0, 1
 
 IDX_BF16, IDX_F32 = 0, 1
+
+
+class _Rope(ctypes.Structure):
+    """The C ABI's idx_rope block (include/mxidx.h)."""
+    _fields_ = [("cos_table", ctypes.c_void_p), ("sin_table", ctypes.c_void_p),
+                ("table_rows", ctypes.c_int64), ("positions", ctypes.c_void_p),
+                ("rope_dim", ctypes.c_int), ("rope_mode", ctypes.c_int)]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmxidx.so")
@@ -56,6 +64,9 @@ EXPORTS = {
     "idx_insert": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int, _c_void_p]),
     "idx_insert_quantize": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64, _int,
                                    _c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p]),
+    "idx_insert_quantize_rope": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _i64,
+                                        _int, _c_void_p, _int, _i64, _i64, _int, _c_void_p,
+                                        _c_void_p, _c_void_p, _c_void_p]),
     "idx_gather": (_int, [_c_void_p, _i64, _int, _c_void_p, _i64, _c_void_p, _c_void_p, _int, _i64,
                           _i64, _c_void_p, _c_void_p, _c_void_p]),
     "idx_logits_prefill": (_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
@@ -66,6 +77,9 @@ EXPORTS = {
     "idx_logits_paged_insert": (_int, [_c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _i64, _int,
                                        _c_void_p, _i64, _c_void_p, _int, _int, _int, _i64,
                                        _c_void_p, _i64, _int, _c_void_p]),
+    "idx_logits_paged_insert_rope": (_int, [_c_void_p, _c_void_p, _int, _c_void_p, _c_void_p, _i64,
+                                            _int, _c_void_p, _i64, _c_void_p, _int, _int, _int,
+                                            _i64, _c_void_p, _i64, _int, _c_void_p, _c_void_p]),
     "idx_quantize_fp8": (_int, [_c_void_p, _int, _i64, _i64, _int, _c_void_p, _c_void_p, _c_void_p,
                                 _c_void_p, _c_void_p]),
     "idx_insert_fp8": (_int, [_c_void_p, _int, _i64, _i64, _int, _c_void_p, _c_void_p, _i64, _int,
@@ -200,6 +214,26 @@ def quantize(x, values=None, scales=None, stream=None):
     return values, scales
 
 
+def _check_rope_tables(cos, sin, rope_dim, positions, tokens):
+    torch = _torch()
+    for name, t in (("cos", cos), ("sin", sin)):
+        _dev(t, name, torch.float32)
+        if not t.is_contiguous() or t.dim() != 2 or t.shape[1] != rope_dim // 2:
+            raise MxidxError(f"{name} must be a contiguous fp32 [table_rows, rope_dim/2]")
+    if cos.shape != sin.shape:
+        raise MxidxError("cos and sin tables must have the same shape")
+    if positions is not None:
+        _dev(positions, "positions", torch.int64)
+        if positions.numel() != tokens or not positions.is_contiguous():
+            raise MxidxError(f"positions must be a contiguous int64 [{tokens}]")
+
+
+def _rope_block(cos, sin, rope_dim, mode, positions):
+    """The idx_rope block of a fused call (the tensors must outlive the call)."""
+    return _Rope(_ptr(cos), _ptr(sin), cos.shape[0], _ptr(positions), rope_dim,
+                 {"neox": ROPE_NEOX, "interleaved": ROPE_INTERLEAVED}[mode])
+
+
 def quantize_rope(q, cos, sin, rope_dim, mode="neox", positions=None, values=None, scales=None,
                   stream=None):
     """RoPE on the first ``rope_dim`` dims of each head of q [T, H, 128] (cos / sin
@@ -210,16 +244,7 @@ def quantize_rope(q, cos, sin, rope_dim, mode="neox", positions=None, values=Non
         raise MxidxError("q must be [T, H, 128]")
     T, H = q.shape[0], q.shape[1]
     rows, stride, code = _rows_view(q, "q")
-    for name, t in (("cos", cos), ("sin", sin)):
-        _dev(t, name, torch.float32)
-        if not t.is_contiguous() or t.dim() != 2 or t.shape[1] != rope_dim // 2:
-            raise MxidxError(f"{name} must be a contiguous fp32 [table_rows, rope_dim/2]")
-    if cos.shape != sin.shape:
-        raise MxidxError("cos and sin tables must have the same shape")
-    if positions is not None:
-        _dev(positions, "positions", torch.int64)
-        if positions.numel() != T or not positions.is_contiguous():
-            raise MxidxError("positions must be a contiguous int64 [T]")
+    _check_rope_tables(cos, sin, rope_dim, positions, T)
     if values is None:
         values = torch.empty((T, H, CODE_BYTES), dtype=torch.uint8, device=q.device)
     if scales is None:
@@ -278,6 +303,42 @@ def insert_quantize(k, slot_mapping, cache, q, q_values=None, q_scales=None, str
                                      num_pages, PAGE_SIZE, _ptr(q), q_code, q_rows, q_stride,
                                      _ptr(q_values), _ptr(q_scales), _stream(stream)),
            "idx_insert_quantize")
+    return q_values, q_scales
+
+
+def insert_quantize_rope(k, slot_mapping, cache, q, cos, sin, rope_dim, mode="neox",
+                         positions=None, q_values=None, q_scales=None, stream=None):
+    """insert(k, slot_mapping, cache) and quantize_rope(q [T, H, 128], ...) in one
+    launch; returns (q_values [T, H, 64], q_scales [T, H, 4])."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise MxidxError("q must be [T, H, 128]")
+    T, H = q.shape[0], q.shape[1]
+    rows, stride, code = _rows_view(k, "k")
+    q_rows, q_stride, q_code = _rows_view(q, "q")
+    _check_rope_tables(cos, sin, rope_dim, positions, T)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(cache, "cache", torch.uint8)
+    if slot_mapping.numel() != rows or not slot_mapping.is_contiguous():
+        raise MxidxError("slot_mapping must be a contiguous int64 [N]")
+    if not cache.is_contiguous() or cache.numel() % (PAGE_SIZE * ROW_BYTES) != 0:
+        raise MxidxError("cache must be a contiguous uint8 [num_pages, 64*68]")
+    if q_values is None:
+        q_values = torch.empty((T, H, CODE_BYTES), dtype=torch.uint8, device=q.device)
+    if q_scales is None:
+        q_scales = torch.empty((T, H, SCALE_BYTES), dtype=torch.uint8, device=q.device)
+    _dev(q_values, "q_values", torch.uint8)
+    _dev(q_scales, "q_scales", torch.uint8)
+    if q_values.numel() != q_rows * CODE_BYTES or q_scales.numel() != q_rows * SCALE_BYTES or \
+            not q_values.is_contiguous() or not q_scales.is_contiguous():
+        raise MxidxError("q_values/q_scales must be contiguous [T, H, 64] / [T, H, 4]")
+    rope = _rope_block(cos, sin, rope_dim, mode, positions)
+    num_pages = cache.numel() // (PAGE_SIZE * ROW_BYTES)
+    _check(lib().idx_insert_quantize_rope(_ptr(k), code, rows, stride, _ptr(slot_mapping),
+                                          _ptr(cache), num_pages, PAGE_SIZE, _ptr(q), q_code,
+                                          q_rows, q_stride, H, ctypes.addressof(rope),
+                                          _ptr(q_values), _ptr(q_scales), _stream(stream)),
+           "idx_insert_quantize_rope")
     return q_values, q_scales
 
 
@@ -385,12 +446,10 @@ def logits_paged(q_values, q_scales, weights, cache, block_table, context_lens, 
     return logits
 
 
-def logits_paged_insert(q, k_new, weights, cache, block_table, context_lens, next_n,
-                        max_context_len, logits=None, clean=True, stream=None):
-    """One decode step in one launch: the new tokens' K (k_new [B*next_n, 128], the
-    last next_n positions of each sequence) into their block-table slots, q
-    [B*next_n, H, 128] encoded to MXFP4, and the decode logits [B*next_n,
-    max_context_len] of the updated cache (as insert + quantize + logits_paged)."""
+def _paged_insert_args(q, k_new, weights, cache, block_table, context_lens, next_n,
+                       max_context_len, logits, clean):
+    """Checks of the one-launch decode step; returns (dtype code, rows, heads,
+    batch, logits, num_pages)."""
     torch = _torch()
     for name, t in (("q", q), ("k_new", k_new)):
         _dev(t, name)
@@ -430,12 +489,46 @@ def logits_paged_insert(q, k_new, weights, cache, block_table, context_lens, nex
             logits.shape[1] < max_context_len:
         raise MxidxError("logits must be [>=rows, >=max_context_len] with contiguous rows")
     num_pages = cache.numel() // (PAGE_SIZE * ROW_BYTES)
+    return code, R, H, B, logits, num_pages
+
+
+def logits_paged_insert(q, k_new, weights, cache, block_table, context_lens, next_n,
+                        max_context_len, logits=None, clean=True, stream=None):
+    """One decode step in one launch: the new tokens' K (k_new [B*next_n, 128], the
+    last next_n positions of each sequence) into their block-table slots, q
+    [B*next_n, H, 128] encoded to MXFP4, and the decode logits [B*next_n,
+    max_context_len] of the updated cache (as insert + quantize + logits_paged)."""
+    code, R, H, B, logits, num_pages = _paged_insert_args(
+        q, k_new, weights, cache, block_table, context_lens, next_n, max_context_len, logits,
+        clean)
     _check(lib().idx_logits_paged_insert(_ptr(q), _ptr(k_new), code, _ptr(weights), _ptr(cache),
                                          num_pages, PAGE_SIZE, _ptr(block_table),
                                          block_table.stride(0), _ptr(context_lens), B, next_n, H,
                                          int(max_context_len), _ptr(logits), logits.stride(0),
                                          1 if clean else 0, _stream(stream)),
            "idx_logits_paged_insert")
+    return logits
+
+
+def logits_paged_insert_rope(q, k_new, weights, cache, block_table, context_lens, next_n,
+                             max_context_len, cos, sin, rope_dim, mode="neox", positions=None,
+                             logits=None, clean=True, stream=None):
+    """logits_paged_insert with q rotated first (as quantize_rope; positions
+    [B*next_n] int64, or None: each row at its token's position
+    context_lens[b] - next_n + i).  Neox pairing takes rope_dim 64 or 128 here."""
+    code, R, H, B, logits, num_pages = _paged_insert_args(
+        q, k_new, weights, cache, block_table, context_lens, next_n, max_context_len, logits,
+        clean)
+    _check_rope_tables(cos, sin, rope_dim, positions, R)
+    rope = _rope_block(cos, sin, rope_dim, mode, positions)
+    _check(lib().idx_logits_paged_insert_rope(_ptr(q), _ptr(k_new), code, _ptr(weights),
+                                              _ptr(cache), num_pages, PAGE_SIZE,
+                                              _ptr(block_table), block_table.stride(0),
+                                              _ptr(context_lens), B, next_n, H,
+                                              int(max_context_len), _ptr(logits),
+                                              logits.stride(0), 1 if clean else 0,
+                                              ctypes.addressof(rope), _stream(stream)),
+           "idx_logits_paged_insert_rope")
     return logits
 
 

@@ -62,7 +62,7 @@ int check_rows_input(const void* x, int dtype, int64_t rows, int64_t row_stride)
 
 extern "C" {
 
-int idx_version(void) { return 105; }
+int idx_version(void) { return 106; }
 
 int idx_arch_supported(const char* gcn_arch_name) {
   // "gfx950" alone or followed by target features ("gfx950:sramecc+:xnack-")
@@ -119,10 +119,31 @@ int idx_quantize_rope(const void* x, int dtype, int64_t T, int H, int64_t row_st
     if (positions ? !aligned(positions, 8) : table_rows < T) return IDX_ERR_ARG;
   }
   if ((st = gate_current()) != IDX_OK) return st;
-  return launched(mxidx::launch_quantize_rope(x, dtype == IDX_F32, rows, row_stride, H, cos_table,
-                                              sin_table, table_rows, positions, rope_dim,
-                                              rope_mode == IDX_ROPE_INTERLEAVED, values, scales,
-                                              stream));
+  const mxidx::RopeSpec rs{cos_table, sin_table, table_rows, positions, rope_dim,
+                          rope_mode == IDX_ROPE_INTERLEAVED};
+  return launched(mxidx::launch_quantize_rope(x, dtype == IDX_F32, rows, row_stride, H, rs, values,
+                                              scales, stream));
+}
+
+// The checks of an idx_rope block common to the fused calls: the rotated
+// prefix, the pairing, and the tables when something is rotated.
+static int check_rope(const idx_rope* r) {
+  if (!r) return IDX_ERR_ARG;
+  if (r->rope_dim < 0 || r->rope_dim > IDX_HEAD_DIM || r->rope_dim % 16 != 0) return IDX_ERR_ARG;
+  if (r->rope_mode != IDX_ROPE_NEOX && r->rope_mode != IDX_ROPE_INTERLEAVED) return IDX_ERR_ARG;
+  if (r->table_rows < 0) return IDX_ERR_ARG;
+  if (r->rope_dim > 0) {
+    if (!r->cos_table || !r->sin_table || !aligned(r->cos_table, 16) ||
+        !aligned(r->sin_table, 16))
+      return IDX_ERR_ARG;
+    if (r->positions && !aligned(r->positions, 8)) return IDX_ERR_ARG;
+  }
+  return IDX_OK;
+}
+
+static mxidx::RopeSpec rope_spec(const idx_rope* r) {
+  return mxidx::RopeSpec{r->cos_table, r->sin_table, r->table_rows, r->positions, r->rope_dim,
+                         r->rope_mode == IDX_ROPE_INTERLEAVED};
 }
 
 int idx_insert(const void* k, int dtype, int64_t num_tokens, int64_t k_row_stride,
@@ -160,6 +181,39 @@ int idx_insert_quantize(const void* k, int k_dtype, int64_t num_tokens, int64_t 
                                                 slot_mapping, cache, num_pages, q,
                                                 q_dtype == IDX_F32, q_rows, q_row_stride, q_values,
                                                 q_scales, stream));
+}
+
+int idx_insert_quantize_rope(const void* k, int k_dtype, int64_t num_tokens,
+                             int64_t k_row_stride, const int64_t* slot_mapping, uint8_t* cache,
+                             int64_t num_pages, int page_size, const void* q, int q_dtype,
+                             int64_t q_rows, int64_t q_row_stride, int q_heads,
+                             const idx_rope* rope, uint8_t* q_values, uint8_t* q_scales,
+                             hipStream_t stream) {
+  int st = check_rows_input(k, k_dtype, num_tokens, k_row_stride);
+  if (st != IDX_OK) return st;
+  if ((st = check_rows_input(q, q_dtype, q_rows, q_row_stride)) != IDX_OK) return st;
+  if ((st = check_rope(rope)) != IDX_OK) return st;
+  if (q_heads < 1 || q_rows % q_heads != 0) return IDX_ERR_ARG;
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0) return IDX_ERR_ARG;
+  if (num_tokens > 0) {
+    if (!slot_mapping || !aligned(slot_mapping, 8)) return IDX_ERR_ARG;
+    if (num_pages > 0 && (!cache || !aligned(cache, 4))) return IDX_ERR_ARG;
+  }
+  if (q_rows > 0 && (!q_values || !q_scales || !aligned(q_values, 4))) return IDX_ERR_ARG;
+  // default positions (token t at table row t) need a row for every token
+  if (rope->rope_dim > 0 && !rope->positions && rope->table_rows < q_rows / q_heads)
+    return IDX_ERR_ARG;
+  if (num_tokens == 0 && q_rows == 0) return IDX_OK;
+  if ((st = gate_current()) != IDX_OK) return st;
+  if (rope->rope_dim == 0)
+    return launched(mxidx::launch_insert_quantize(k, k_dtype == IDX_F32, num_tokens, k_row_stride,
+                                                  slot_mapping, cache, num_pages, q,
+                                                  q_dtype == IDX_F32, q_rows, q_row_stride,
+                                                  q_values, q_scales, stream));
+  return launched(mxidx::launch_insert_quantize_rope(
+      k, k_dtype == IDX_F32, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
+      q_dtype == IDX_F32, q_rows, q_row_stride, q_heads, rope_spec(rope), q_values, q_scales,
+      stream));
 }
 
 int idx_gather(const uint8_t* cache, int64_t num_pages, int page_size, const int32_t* block_table,
@@ -253,6 +307,40 @@ int idx_logits_paged_insert(const void* q, const void* k_new, int dtype, const f
   return launched(mxidx::launch_logits_paged_insert(
       q, k_new, dtype == IDX_F32, weights, cache, num_pages, block_table, bt_row_stride,
       context_lens, B, next_n, H, max_context_len, logits, logits_row_stride, clean, stream));
+}
+
+int idx_logits_paged_insert_rope(const void* q, const void* k_new, int dtype,
+                                 const float* weights, uint8_t* cache, int64_t num_pages,
+                                 int page_size, const int32_t* block_table, int64_t bt_row_stride,
+                                 const int32_t* context_lens, int B, int next_n, int H,
+                                 int64_t max_context_len, float* logits,
+                                 int64_t logits_row_stride, int clean, const idx_rope* rope,
+                                 hipStream_t stream) {
+  int st = check_rope(rope);
+  if (st != IDX_OK) return st;
+  // the in-wave rotation takes neox partners from one other lane block
+  if (rope->rope_mode == IDX_ROPE_NEOX && rope->rope_dim != 0 && rope->rope_dim != 64 &&
+      rope->rope_dim != 128)
+    return IDX_ERR_ARG;
+  if (dtype != IDX_BF16 && dtype != IDX_F32) return IDX_ERR_ARG;
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0 || B < 0 || B > IDX_MAX_DECODE_SEQS ||
+      next_n < 1 || next_n > 16 || !heads_ok(H) || max_context_len < 0 ||
+      max_context_len > 0x7fffffffLL - IDX_PAGE_SIZE)
+    return IDX_ERR_ARG;
+  if (B == 0 || max_context_len == 0) return IDX_OK;
+  const int64_t pages_per_seq = (max_context_len + IDX_PAGE_SIZE - 1) / IDX_PAGE_SIZE;
+  if (bt_row_stride < pages_per_seq || logits_row_stride < max_context_len || num_pages < 1 ||
+      (int64_t)B * pages_per_seq > 0x7fffffffLL)
+    return IDX_ERR_ARG;
+  if (!q || !aligned(q, 16) || !k_new || !aligned(k_new, 16) || !weights || !aligned(weights, 16) ||
+      !cache || !aligned(cache, 16) || !block_table || !context_lens || !logits ||
+      !aligned(logits, 4))
+    return IDX_ERR_ARG;
+  if ((st = gate_current()) != IDX_OK) return st;
+  return launched(mxidx::launch_logits_paged_insert_rope(
+      q, k_new, dtype == IDX_F32, weights, cache, num_pages, block_table, bt_row_stride,
+      context_lens, B, next_n, H, max_context_len, logits, logits_row_stride, clean,
+      rope_spec(rope), stream));
 }
 
 int idx_topk_merge(const float* values, const int32_t* indices, int world, int64_t rows, int k_in,

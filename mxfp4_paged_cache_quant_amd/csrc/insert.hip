@@ -131,71 +131,85 @@ __device__ __forceinline__ float rot_b(float a, float b, float c, float s) {
   return b * c + a * s;
 }
 
-template <typename In>
-__global__ __launch_bounds__(256) void mxfp4_rope_rows_kernel(
-    const void* __restrict__ x, int64_t rows, int64_t stride, int H, const float* __restrict__ cos_t,
-    const float* __restrict__ sin_t, int64_t table_rows, const int64_t* __restrict__ positions,
-    int rope_dim, int interleaved, uint8_t* __restrict__ dst_codes, uint8_t* __restrict__ dst_scales) {
-  const int sub = threadIdx.x & 15;
-  const int half = rope_dim >> 1;
-  const int hl = half >> 3;                       // lanes per half of the rotated range
-  for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4); row < rows;
-       row += (int64_t)gridDim.x * kRowsPerBlock) {
-    In in;
-    in.load(x, row, stride, sub);
-    float v[8];
-    in.values(v);
-    if (rope_dim > 0) {                           // uniform over the launch
-      const int64_t t = row / H;
-      const int64_t p = positions ? positions[t] : t;
-      const bool ok = p >= 0 && p < table_rows;   // same for the row's 16 lanes
-      float pv[8];
-      if (!interleaved) {
-        const int partner = sub < hl ? sub + hl : sub - hl;
+// Rotates the row that 16 lanes hold (lane sub: elements 8sub..8sub+7) by the
+// angles of table row p; a position outside the table leaves it unrotated.
+// Every lane of the row calls it: a neox lane's partners come by shuffles.
+__device__ __forceinline__ void rope_row8(float (&v)[8], int sub, int64_t p, const RopeSpec& rs) {
+  const int half = rs.rope_dim >> 1;
+  const int hl = half >> 3;                     // lanes per half of the rotated range
+  const bool ok = p >= 0 && p < rs.table_rows;  // same for the row's 16 lanes
+  float pv[8];
+  if (!rs.interleaved) {
+    const int partner = sub < hl ? sub + hl : sub - hl;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = __shfl(v[i], partner, 16);
-      }
-      if (ok && sub < (rope_dim >> 3)) {
-        const float* cr = cos_t + p * half;
-        const float* sr = sin_t + p * half;
-        if (interleaved) {
-          // pairs (8sub + 2i, 8sub + 2i + 1), angle index 4sub + i
-          const float4 c = *reinterpret_cast<const float4*>(cr + 4 * sub);
-          const float4 s = *reinterpret_cast<const float4*>(sr + 4 * sub);
-          const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = v[2 * i], b = v[2 * i + 1];
-            v[2 * i] = rot_a(a, b, cc[i], ss[i]);
-            v[2 * i + 1] = rot_b(a, b, cc[i], ss[i]);
-          }
-        } else {
-          // this lane holds elements 8sub..8sub+7: the a's of angles 8sub.. (sub < hl)
-          // or the b's of angles 8(sub - hl).. ; the partner lane holds the others
-          const int j0 = 8 * (sub < hl ? sub : sub - hl);
-          const float4 c0 = *reinterpret_cast<const float4*>(cr + j0);
-          const float4 c1 = *reinterpret_cast<const float4*>(cr + j0 + 4);
-          const float4 s0 = *reinterpret_cast<const float4*>(sr + j0);
-          const float4 s1 = *reinterpret_cast<const float4*>(sr + j0 + 4);
-          const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-          const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-          if (sub < hl) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = rot_a(v[i], pv[i], cc[i], ss[i]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = rot_b(pv[i], v[i], cc[i], ss[i]);
-          }
-        }
-      }
-    }
-    F32In r;
-    r.lo = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                      __float_as_uint(v[3]));
-    r.hi = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
-                      __float_as_uint(v[7]));
-    encode_loaded(r, sub, dst_codes + row * kCodeBytes, dst_scales + row * kScaleBytes);
+    for (int i = 0; i < 8; ++i) pv[i] = __shfl(v[i], partner, 16);
   }
+  if (!ok || sub >= (rs.rope_dim >> 3)) return;
+  const float* cr = rs.cos_t + p * half;
+  const float* sr = rs.sin_t + p * half;
+  if (rs.interleaved) {
+    // pairs (8sub + 2i, 8sub + 2i + 1), angle index 4sub + i
+    const float4 c = *reinterpret_cast<const float4*>(cr + 4 * sub);
+    const float4 s = *reinterpret_cast<const float4*>(sr + 4 * sub);
+    const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = v[2 * i], b = v[2 * i + 1];
+      v[2 * i] = rot_a(a, b, cc[i], ss[i]);
+      v[2 * i + 1] = rot_b(a, b, cc[i], ss[i]);
+    }
+  } else {
+    // this lane holds elements 8sub..8sub+7: the a's of angles 8sub.. (sub < hl)
+    // or the b's of angles 8(sub - hl).. ; the partner lane holds the others
+    const int j0 = 8 * (sub < hl ? sub : sub - hl);
+    const float4 c0 = *reinterpret_cast<const float4*>(cr + j0);
+    const float4 c1 = *reinterpret_cast<const float4*>(cr + j0 + 4);
+    const float4 s0 = *reinterpret_cast<const float4*>(sr + j0);
+    const float4 s1 = *reinterpret_cast<const float4*>(sr + j0 + 4);
+    const float cc[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float ss[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    if (sub < hl) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = rot_a(v[i], pv[i], cc[i], ss[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = rot_b(pv[i], v[i], cc[i], ss[i]);
+    }
+  }
+}
+
+// Row `row` of q (token row / H) rotated, then encoded as an fp32 row.
+template <typename In>
+__device__ __forceinline__ void rope_encode_row(const void* __restrict__ x, int64_t row,
+                                                int64_t stride, int H, const RopeSpec& rs,
+                                                int sub, uint8_t* cdst, uint8_t* sdst) {
+  In in;
+  in.load(x, row, stride, sub);
+  float v[8];
+  in.values(v);
+  if (rs.rope_dim > 0) {   // uniform over the launch; no table or position read at 0
+    const int64_t t = row / H;
+    rope_row8(v, sub, rs.positions ? rs.positions[t] : t, rs);
+  }
+  F32In r;
+  r.lo = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3]));
+  r.hi = make_uint4(__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]),
+                    __float_as_uint(v[7]));
+  encode_loaded(r, sub, cdst, sdst);
+}
+
+template <typename In>
+__global__ __launch_bounds__(256) void mxfp4_rope_rows_kernel(const void* __restrict__ x,
+                                                               int64_t rows, int64_t stride, int H,
+                                                               RopeSpec rs,
+                                                               uint8_t* __restrict__ dst_codes,
+                                                               uint8_t* __restrict__ dst_scales) {
+  const int sub = threadIdx.x & 15;
+  for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4); row < rows;
+       row += (int64_t)gridDim.x * kRowsPerBlock)
+    rope_encode_row<In>(x, row, stride, H, rs, sub, dst_codes + row * kCodeBytes,
+                        dst_scales + row * kScaleBytes);
 }
 
 // Paged destination of a slot: codes at page*4352 + off*64, scales at
@@ -240,12 +254,12 @@ __global__ __launch_bounds__(256) void mxfp4_rows_kernel(const void* __restrict_
 // Both encodes of a decode step in one launch: workgroups [0, k_blocks) put
 // the K rows into their cache slots, the others write the query rows
 // contiguously.  Each part is a grid-stride loop over its own workgroups.
-template <typename KIn, typename QIn>
+template <typename KIn, typename QIn, bool kRope>
 __global__ __launch_bounds__(256) void insert_quantize_kernel(
     const void* __restrict__ k, int64_t k_rows, int64_t k_stride,
     const int64_t* __restrict__ slot_mapping, int64_t num_slots, uint8_t* __restrict__ cache,
     int k_blocks, const void* __restrict__ q, int64_t q_rows, int64_t q_stride,
-    uint8_t* __restrict__ q_values, uint8_t* __restrict__ q_scales) {
+    uint8_t* __restrict__ q_values, uint8_t* __restrict__ q_scales, int q_heads, RopeSpec rs) {
   const int sub = threadIdx.x & 15;
   if ((int)blockIdx.x < k_blocks) {
     for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 4); row < k_rows;
@@ -259,8 +273,14 @@ __global__ __launch_bounds__(256) void insert_quantize_kernel(
     const int64_t qb = (int64_t)blockIdx.x - k_blocks;
     const int64_t q_blocks = (int64_t)gridDim.x - k_blocks;
     for (int64_t row = qb * kRowsPerBlock + (threadIdx.x >> 4); row < q_rows;
-         row += q_blocks * kRowsPerBlock)
-      encode_row<QIn>(q, row, q_stride, sub, q_values + row * kCodeBytes, q_scales + row * kScaleBytes);
+         row += q_blocks * kRowsPerBlock) {
+      if constexpr (kRope)
+        rope_encode_row<QIn>(q, row, q_stride, q_heads, rs, sub, q_values + row * kCodeBytes,
+                             q_scales + row * kScaleBytes);
+      else
+        encode_row<QIn>(q, row, q_stride, sub, q_values + row * kCodeBytes,
+                        q_scales + row * kScaleBytes);
+    }
   }
 }
 
@@ -270,16 +290,31 @@ int grid_for_rows(int64_t rows) {
   return (int)(blocks < cap ? blocks : cap);
 }
 
-template <typename KIn, typename QIn>
+template <typename KIn, typename QIn, bool kRope>
 hipError_t launch_iq(const void* k, int64_t num_tokens, int64_t k_stride, const int64_t* slots,
                      uint8_t* cache, int64_t num_pages, const void* q, int64_t q_rows,
-                     int64_t q_stride, uint8_t* q_values, uint8_t* q_scales, hipStream_t stream) {
+                     int64_t q_stride, uint8_t* q_values, uint8_t* q_scales, int q_heads,
+                     const RopeSpec& rs, hipStream_t stream) {
   const int kb = grid_for_rows(num_tokens);
   const int qb = grid_for_rows(q_rows);
-  hipLaunchKernelGGL((insert_quantize_kernel<KIn, QIn>), dim3(kb + qb), dim3(256), 0, stream, k,
-                     num_tokens, k_stride, slots, num_pages * kPage, cache, kb, q, q_rows, q_stride,
-                     q_values, q_scales);
+  hipLaunchKernelGGL((insert_quantize_kernel<KIn, QIn, kRope>), dim3(kb + qb), dim3(256), 0,
+                     stream, k, num_tokens, k_stride, slots, num_pages * kPage, cache, kb, q,
+                     q_rows, q_stride, q_values, q_scales, q_heads, rs);
   return hipGetLastError();
+}
+
+template <bool kRope>
+hipError_t launch_iq_types(const void* k, bool k_f32, int64_t num_tokens, int64_t k_row_stride,
+                           const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
+                           const void* q, bool q_f32, int64_t q_rows, int64_t q_row_stride,
+                           uint8_t* q_values, uint8_t* q_scales, int q_heads, const RopeSpec& rs,
+                           hipStream_t stream) {
+#define MXIDX_IQ(KT, QT)                                                                        \
+  launch_iq<KT, QT, kRope>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,     \
+                           q_rows, q_row_stride, q_values, q_scales, q_heads, rs, stream)
+  if (k_f32) return q_f32 ? MXIDX_IQ(F32In, F32In) : MXIDX_IQ(F32In, Bf16In);
+  return q_f32 ? MXIDX_IQ(Bf16In, F32In) : MXIDX_IQ(Bf16In, Bf16In);
+#undef MXIDX_IQ
 }
 
 }  // namespace
@@ -297,18 +332,15 @@ hipError_t launch_quantize(const void* x, bool f32, int64_t rows, int64_t row_st
 }
 
 hipError_t launch_quantize_rope(const void* x, bool f32, int64_t rows, int64_t row_stride, int H,
-                                const float* cos_t, const float* sin_t, int64_t table_rows,
-                                const int64_t* positions, int rope_dim, bool interleaved,
-                                uint8_t* values, uint8_t* scales, hipStream_t stream) {
+                                const RopeSpec& rope, uint8_t* values, uint8_t* scales,
+                                hipStream_t stream) {
   const int grid = grid_for_rows(rows);
   if (f32)
     hipLaunchKernelGGL((mxfp4_rope_rows_kernel<F32In>), dim3(grid), dim3(256), 0, stream, x, rows,
-                       row_stride, H, cos_t, sin_t, table_rows, positions, rope_dim,
-                       interleaved ? 1 : 0, values, scales);
+                       row_stride, H, rope, values, scales);
   else
     hipLaunchKernelGGL((mxfp4_rope_rows_kernel<Bf16In>), dim3(grid), dim3(256), 0, stream, x, rows,
-                       row_stride, H, cos_t, sin_t, table_rows, positions, rope_dim,
-                       interleaved ? 1 : 0, values, scales);
+                       row_stride, H, rope, values, scales);
   return hipGetLastError();
 }
 
@@ -331,17 +363,21 @@ hipError_t launch_insert_quantize(const void* k, bool k_f32, int64_t num_tokens,
                                   uint8_t* cache, int64_t num_pages, const void* q, bool q_f32,
                                   int64_t q_rows, int64_t q_row_stride, uint8_t* q_values,
                                   uint8_t* q_scales, hipStream_t stream) {
-  if (k_f32 && q_f32)
-    return launch_iq<F32In, F32In>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
-                                   q_rows, q_row_stride, q_values, q_scales, stream);
-  if (k_f32)
-    return launch_iq<F32In, Bf16In>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
-                                    q_rows, q_row_stride, q_values, q_scales, stream);
-  if (q_f32)
-    return launch_iq<Bf16In, F32In>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
-                                    q_rows, q_row_stride, q_values, q_scales, stream);
-  return launch_iq<Bf16In, Bf16In>(k, num_tokens, k_row_stride, slot_mapping, cache, num_pages, q,
-                                   q_rows, q_row_stride, q_values, q_scales, stream);
+  const RopeSpec none{};
+  return launch_iq_types<false>(k, k_f32, num_tokens, k_row_stride, slot_mapping, cache, num_pages,
+                                q, q_f32, q_rows, q_row_stride, q_values, q_scales, 1, none,
+                                stream);
+}
+
+hipError_t launch_insert_quantize_rope(const void* k, bool k_f32, int64_t num_tokens,
+                                       int64_t k_row_stride, const int64_t* slot_mapping,
+                                       uint8_t* cache, int64_t num_pages, const void* q,
+                                       bool q_f32, int64_t q_rows, int64_t q_row_stride,
+                                       int q_heads, const RopeSpec& rope, uint8_t* q_values,
+                                       uint8_t* q_scales, hipStream_t stream) {
+  return launch_iq_types<true>(k, k_f32, num_tokens, k_row_stride, slot_mapping, cache, num_pages,
+                               q, q_f32, q_rows, q_row_stride, q_values, q_scales, q_heads, rope,
+                               stream);
 }
 
 }  // namespace mxidx

@@ -11,12 +11,23 @@ namespace mxidx {
 hipError_t launch_quantize(const void* x, bool f32, int64_t rows, int64_t row_stride,
                            uint8_t* values, uint8_t* scales, hipStream_t stream);
 
+// Query RoPE of a fused encode: fp32 angle tables [table_rows, rope_dim/2],
+// per-token table rows (null: the call's default position), the rotated
+// prefix of the 128 dims (a multiple of 16) and the pairing.
+struct RopeSpec {
+  const float* cos_t;
+  const float* sin_t;
+  int64_t table_rows;
+  const int64_t* positions;
+  int rope_dim;
+  bool interleaved;
+};
+
 // Query RoPE (first rope_dim dims, neox or interleaved pairs, fp32) fused into
-// the MXFP4 encode; rows = T*H, row r of token r / H.
+// the MXFP4 encode; rows = T*H, row r of token r / H (default position: t).
 hipError_t launch_quantize_rope(const void* x, bool f32, int64_t rows, int64_t row_stride, int H,
-                                const float* cos_t, const float* sin_t, int64_t table_rows,
-                                const int64_t* positions, int rope_dim, bool interleaved,
-                                uint8_t* values, uint8_t* scales, hipStream_t stream);
+                                const RopeSpec& rope, uint8_t* values, uint8_t* scales,
+                                hipStream_t stream);
 
 hipError_t launch_insert(const void* k, bool f32, int64_t num_tokens, int64_t row_stride,
                          const int64_t* slot_mapping, uint8_t* cache, int64_t num_pages,
@@ -27,6 +38,13 @@ hipError_t launch_insert_quantize(const void* k, bool k_f32, int64_t num_tokens,
                                   uint8_t* cache, int64_t num_pages, const void* q, bool q_f32,
                                   int64_t q_rows, int64_t q_row_stride, uint8_t* q_values,
                                   uint8_t* q_scales, hipStream_t stream);
+// The same with the query rows (q_rows = T * q_heads) rotated first.
+hipError_t launch_insert_quantize_rope(const void* k, bool k_f32, int64_t num_tokens,
+                                       int64_t k_row_stride, const int64_t* slot_mapping,
+                                       uint8_t* cache, int64_t num_pages, const void* q,
+                                       bool q_f32, int64_t q_rows, int64_t q_row_stride,
+                                       int q_heads, const RopeSpec& rope, uint8_t* q_values,
+                                       uint8_t* q_scales, hipStream_t stream);
 
 hipError_t launch_gather(const uint8_t* cache, int64_t num_pages, const int32_t* block_table,
                          int64_t bt_row_stride, const int32_t* seq_lens,
@@ -55,6 +73,16 @@ hipError_t launch_logits_paged_insert(const void* q, const void* k_new, bool f32
                                       const int32_t* context_lens, int B, int next_n, int H,
                                       int64_t max_context_len, float* logits, int64_t ld,
                                       int clean, hipStream_t stream);
+// The same with the query rows rotated before their encode (neox pairs need
+// rope_dim 64 or 128; default position of row b*next_n + i: its token's
+// position context_lens[b] - next_n + i).
+hipError_t launch_logits_paged_insert_rope(const void* q, const void* k_new, bool f32,
+                                           const float* weights, uint8_t* cache,
+                                           int64_t num_pages, const int32_t* block_table,
+                                           int64_t bt_row_stride, const int32_t* context_lens,
+                                           int B, int next_n, int H, int64_t max_context_len,
+                                           float* logits, int64_t ld, int clean,
+                                           const RopeSpec& rope, hipStream_t stream);
 
 // FP8 (E4M3) indexer cache (fp8.hip): rows of 128 E4M3 values + an fp32 scale.
 hipError_t launch_quantize_fp8(const void* x, bool f32, int64_t rows, int64_t row_stride, bool pow2,

@@ -91,8 +91,9 @@ struct PackedQuery {
   static constexpr bool kInsert = false;
   template <int NH>
   using Fetched = QueryRegs<NH>;
+  static constexpr bool kRope = false;
   template <int NH>
-  __device__ __forceinline__ QueryRegs<NH> fetch(int64_t r, int g, int n) const {
+  __device__ __forceinline__ QueryRegs<NH> fetch(int64_t r, int g, int n, int64_t) const {
     return load_query<NH>(q_values, q_scales, weights, r, g, n);
   }
   template <int NH>
@@ -101,25 +102,120 @@ struct PackedQuery {
   }
 };
 
+// Angle operands of one query row for a lane's 32-element block: cosines and
+// sines of the block's angles (neox: 32 consecutive angles, interleaved: 16)
+// and whether the row is rotated (its position lies inside the table).
+template <bool kOn>
+struct RopeRegs {};
+template <>
+struct RopeRegs<true> {
+  float4 c[8];
+  float4 s[8];
+  int on;
+};
+
+__device__ __forceinline__ float comp(const float4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// The word of lane l ^ 16 (K 16) or l ^ 32 (K 32), by gfx950's lane swaps
+// (see reduce_tiles for their lane mapping).
+template <int K>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int g) {
+  if constexpr (K == 32) {
+    const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return g < 2 ? s[1] : s[0];
+  } else {
+    const auto s = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (g & 1) ? s[0] : s[1];
+  }
+}
+
+// One product pair of a rotation, each product and the sum rounded to fp32:
+// x*c + y*s.  With s negated this is a*cos - b*sin exactly (a negated
+// product is exact), so both halves of a pair take this one form.
+__device__ __forceinline__ float rot_sum(float x, float c, float y, float s) {
+#pragma clang fp contract(off)
+  return x * c + y * s;
+}
+
+// Neox pairs (j, j + rope_dim/2) with rope_dim 64 (K 16: blocks 0 and 1) or
+// 128 (K 32: blocks g and g ^ 2): element e of this lane's block pairs with
+// element e of the partner lane's, at the e-th of the lane's angles.
+template <int K, typename Blk>
+__device__ __forceinline__ void rope_neox(const Blk& b, const RopeRegs<true>& r, int g, float (&o)[32]) {
+  const bool rot = K == 32 || g < 2;           // rope_dim 64: blocks 2, 3 pass
+  const bool is_a = K == 32 ? g < 2 : g == 0;  // this lane holds the pairs' first elements
+  const uint32_t flip = is_a ? 0x80000000u : 0u;
+#pragma unroll
+  for (int k = 0; k < 32 / Blk::kPerWord; ++k) {
+    const uint32_t w = b.word(k);
+    const uint32_t pw = lane_xor<K>(w, g);
+#pragma unroll
+    for (int h = 0; h < Blk::kPerWord; ++h) {
+      const int e = k * Blk::kPerWord + h;
+      const float x = Blk::elem(w, h), y = Blk::elem(pw, h);
+      const float c = comp(r.c[e >> 2], e & 3);
+      const float s = __uint_as_float(__float_as_uint(comp(r.s[e >> 2], e & 3)) ^ flip);
+      o[e] = rot ? rot_sum(x, c, y, s) : x;
+    }
+  }
+}
+
+// Interleaved pairs (2j, 2j + 1): pair m of this lane's block is angle
+// 16g + m, rotated while that angle is below rope_dim/2.
+template <typename Blk>
+__device__ __forceinline__ void rope_interleaved(const Blk& b, const RopeRegs<true>& r, int g,
+                                                 int half, float (&o)[32]) {
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    float a, bb;
+    if constexpr (Blk::kPerWord == 2) {
+      const uint32_t w = b.word(m);
+      a = Blk::elem(w, 0);
+      bb = Blk::elem(w, 1);
+    } else {
+      a = Blk::elem(b.word(2 * m), 0);
+      bb = Blk::elem(b.word(2 * m + 1), 0);
+    }
+    const float c = comp(r.c[m >> 2], m & 3), s = comp(r.s[m >> 2], m & 3);
+    const bool rot = 16 * g + m < half;
+    o[2 * m] = rot ? rot_sum(a, c, bb, -s) : a;
+    o[2 * m + 1] = rot ? rot_sum(bb, c, a, s) : bb;
+  }
+}
+
 // Query source of the fused decode step: q rows in bf16 / fp32 (Blk), encoded
 // to MXFP4 in the wave -- lane (g, n) encodes block g of head 16*grp + n, the
 // block it supplies to the MFMA -- with the rule and conversion of the row
 // encoders, so the operands equal those of the separate encode.  The new
-// tokens' K rows come with it (kInsert).
-template <typename Blk>
-struct RawQuery {
+// tokens' K rows come with it (kInsert).  With kRopeOn the rows are first
+// rotated (RopeSpec; neox needs rope_dim 64 or 128) at position P, in fp32,
+// and encoded as fp32 rows: the bytes of the separate RoPE encode.  The angle
+// loads are issued with the query rows, ahead of the page loads.
+template <bool kOn>
+struct RopeField {};      // empty without RoPE: the kernel arguments stay as they were
+template <>
+struct RopeField<true> {
+  RopeSpec rope;
+};
+
+template <typename Blk, bool kRopeOn = false>
+struct RawQuery : RopeField<kRopeOn> {
   const void* q;          // [rows, H, 128]
   const void* k_new;      // [rows, 128]: row b*next_n + i is token L_b - next_n + i
   const float* weights;
   static constexpr bool kInsert = true;
+  static constexpr bool kRope = kRopeOn;
   using Block = Blk;
   template <int NH>
   struct Fetched {
     Blk blk[NH];
     float4 w[NH];
+    RopeRegs<kRopeOn> r;
   };
   template <int NH>
-  __device__ __forceinline__ Fetched<NH> fetch(int64_t r, int g, int n) const {
+  __device__ __forceinline__ Fetched<NH> fetch(int64_t r, int g, int n, int64_t P) const {
     constexpr int H = 16 * NH;
     constexpr int kRow = kHeadDim * Blk::kElemBytes;
     Fetched<NH> f;
@@ -130,11 +226,59 @@ struct RawQuery {
       f.blk[grp].load(rs, (uint32_t)((16 * grp + n) * kRow + g * kBlock * Blk::kElemBytes));
       f.w[grp] = *reinterpret_cast<const float4*>(weights + r * H + 16 * grp + 4 * g);
     }
+    if constexpr (kRopeOn) {
+      // the table row P, bounded at rope_dim/2 angles (angles past it read 0,
+      // without an access); a position outside the table rotates nothing
+      const int half = this->rope.rope_dim >> 1;
+      const bool on = P >= 0 && P < this->rope.table_rows;   // wave-uniform
+      f.r.on = on ? 1 : 0;
+      const int64_t prow = on ? P : 0;
+      const int bytes = on ? 4 * half : 0;
+      const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(this->rope.cos_t + prow * half, bytes);
+      const __amdgpu_buffer_rsrc_t rn = buffer_rsrc(this->rope.sin_t + prow * half, bytes);
+      const int base = this->rope.interleaved ? 16 * g
+                                              : (this->rope.rope_dim == 128 ? 32 * (g & 1) : 0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint4 c = load16(rc, 4u * (uint32_t)(base + 4 * k));
+        const uint4 s = load16(rn, 4u * (uint32_t)(base + 4 * k));
+        f.r.c[k] = make_float4(__uint_as_float(c.x), __uint_as_float(c.y), __uint_as_float(c.z),
+                               __uint_as_float(c.w));
+        f.r.s[k] = make_float4(__uint_as_float(s.x), __uint_as_float(s.y), __uint_as_float(s.z),
+                               __uint_as_float(s.w));
+      }
+    }
     return f;
   }
   template <int NH>
   __device__ __forceinline__ QueryRegs<NH> finish(const Fetched<NH>& f) const {
     QueryRegs<NH> q;
+    if constexpr (kRopeOn) {
+      if (f.r.on) {                      // wave-uniform
+        const int g = (int)(threadIdx.x & 63) >> 4;
+#pragma unroll
+        for (int grp = 0; grp < NH; ++grp) {
+          float o[32];
+          if (this->rope.interleaved)
+            rope_interleaved(f.blk[grp], f.r, g, this->rope.rope_dim >> 1, o);
+          else if (this->rope.rope_dim == 128)
+            rope_neox<32>(f.blk[grp], f.r, g, o);
+          else
+            rope_neox<16>(f.blk[grp], f.r, g, o);
+          F32Block ob;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            ob.v[i] = make_uint4(__float_as_uint(o[4 * i]), __float_as_uint(o[4 * i + 1]),
+                                 __float_as_uint(o[4 * i + 2]), __float_as_uint(o[4 * i + 3]));
+          const uint32_t a = ob.amax_bits();
+          const int E = block_exponent(a);
+          q.a[grp] = ob.encode(block_divisor(a, E));
+          q.sa[grp] = E + 127;
+          q.w[grp] = f.w[grp];
+        }
+        return q;
+      }
+    }
 #pragma unroll
     for (int grp = 0; grp < NH; ++grp) {
       const uint32_t a = f.blk[grp].amax_bits();
@@ -206,6 +350,27 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
       buffer_rsrc(block_table + (int64_t)b * bt_row_stride + lp0, 4 * bt_count), 4u * lane, 0, 0);
   const uint32_t ctx_raw =
       __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(context_lens + b, 4), 0, 0, 0);
+  // RoPE positions of the sequence's rows, in the same round trip: lane i <
+  // next_n reads positions[row0 + i] (null: row i is at its token's position
+  // context_len - next_n + i).
+  uint32_t pos_lo = 0, pos_hi = 0;
+  if constexpr (QS::kRope) {
+    if (qs.rope.positions) {   // uniform
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(qs.rope.positions + row0, 8 * next_n);
+      pos_lo = __builtin_amdgcn_raw_buffer_load_b32(rs, 8u * lane, 0, 0);
+      pos_hi = __builtin_amdgcn_raw_buffer_load_b32(rs, 8u * lane + 4u, 0, 0);
+    }
+  }
+  auto row_pos = [&](int i) -> int64_t {
+    if constexpr (QS::kRope) {
+      if (qs.rope.positions)
+        return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)pos_hi, i) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane((int)pos_lo, i));
+      return (int64_t)(int32_t)__builtin_amdgcn_readfirstlane(ctx_raw) - next_n + i;
+    } else {
+      return 0;
+    }
+  };
   // The new token's K row is issued right behind the table loads.  The asm
   // below waits for the table only (counters retire in order, later loads stay
   // in flight) and, clobbering memory when inserting, keeps every load on its
@@ -232,13 +397,13 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     asm volatile("" ::"v"(bt_lane) : "memory");
     if (NN > 0)
 #pragma unroll
-      for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n);
+      for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n, row_pos(i));
     asm volatile("" ::: "memory");
   } else {
     asm volatile("" ::"v"(bt_lane));   // keeps the table load here, not sunk past the branch below
     if (NN > 0)
 #pragma unroll
-      for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n);
+      for (int i = 0; i < kRowsHeld; ++i) qf[i] = qs.template fetch<NH>(row0 + i, g, n, 0);
   }
   const int64_t ctx = (int32_t)__builtin_amdgcn_readfirstlane(ctx_raw);
   // context lengths beyond the row width are a precondition violation; clamp so
@@ -378,7 +543,7 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     for (int i = 0; i < next_n; ++i) {
       const int64_t r = row0 + i;
       const int64_t ke = L - next_n + i + 1;
-      const QueryRegs<NH> q = qs.template finish<NH>(qs.template fetch<NH>(r, g, n));
+      const QueryRegs<NH> q = qs.template finish<NH>(qs.template fetch<NH>(r, g, n, row_pos(i)));
 #pragma unroll
       for (int p = 0; p < kPagesPerWave; ++p)
         if (page_ok[p]) store(r, (lp0 + p) * kPage, ke, page_score<NH>(pg[p], q, lane));
@@ -400,9 +565,26 @@ hipError_t launch_nh(QS qs, const uint8_t* cache, int64_t num_pages, const int32
 #define MXIDX_PAGED_ROWS(nn)                                                                   \
   hipLaunchKernelGGL((logits_paged_kernel<NH, nn, QS>), grid, dim3(kWave), 0, stream, qs, cache, \
                      num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean, stream_out)
-  // rows held in registers while rows * NH <= 8 (the query operands of 8 head groups)
+  // rows held in registers while rows * NH <= 8 (the query operands of 8 head
+  // groups); <= 4 with RoPE, whose angle registers are held per row too
   bool held = true;
-  if (next_n == 1) {
+  if constexpr (QS::kRope) {
+    if constexpr (NH <= 2) {
+      if (next_n == 1)
+        MXIDX_PAGED_ROWS(1);
+      else if (next_n == 2)
+        MXIDX_PAGED_ROWS(2);
+      else
+        held = false;
+    } else if constexpr (NH <= 4) {
+      if (next_n == 1)
+        MXIDX_PAGED_ROWS(1);
+      else
+        held = false;
+    } else {
+      held = false;
+    }
+  } else if (next_n == 1) {
     MXIDX_PAGED_ROWS(1);
   } else if constexpr (NH <= 4) {
     if (next_n == 2) {
@@ -470,12 +652,32 @@ hipError_t launch_logits_paged_insert(const void* q, const void* k_new, bool f32
                                       int64_t max_context_len, float* logits, int64_t ld,
                                       int clean, hipStream_t stream) {
   if (f32)
-    return launch_source(RawQuery<F32Block>{q, k_new, weights}, cache, num_pages, block_table,
+    return launch_source(RawQuery<F32Block>{{}, q, k_new, weights}, cache, num_pages, block_table,
                          bt_row_stride, context_lens, B, next_n, H, max_context_len, logits, ld,
                          clean, stream);
-  return launch_source(RawQuery<Bf16Block>{q, k_new, weights}, cache, num_pages, block_table,
+  return launch_source(RawQuery<Bf16Block>{{}, q, k_new, weights}, cache, num_pages, block_table,
                        bt_row_stride, context_lens, B, next_n, H, max_context_len, logits, ld,
                        clean, stream);
+}
+
+hipError_t launch_logits_paged_insert_rope(const void* q, const void* k_new, bool f32,
+                                           const float* weights, uint8_t* cache,
+                                           int64_t num_pages, const int32_t* block_table,
+                                           int64_t bt_row_stride, const int32_t* context_lens,
+                                           int B, int next_n, int H, int64_t max_context_len,
+                                           float* logits, int64_t ld, int clean,
+                                           const RopeSpec& rope, hipStream_t stream) {
+  if (rope.rope_dim == 0)
+    return launch_logits_paged_insert(q, k_new, f32, weights, cache, num_pages, block_table,
+                                      bt_row_stride, context_lens, B, next_n, H, max_context_len,
+                                      logits, ld, clean, stream);
+  if (f32)
+    return launch_source(RawQuery<F32Block, true>{{rope}, q, k_new, weights}, cache, num_pages,
+                         block_table, bt_row_stride, context_lens, B, next_n, H, max_context_len,
+                         logits, ld, clean, stream);
+  return launch_source(RawQuery<Bf16Block, true>{{rope}, q, k_new, weights}, cache, num_pages,
+                       block_table, bt_row_stride, context_lens, B, next_n, H, max_context_len,
+                       logits, ld, clean, stream);
 }
 
 }  // namespace mxidx

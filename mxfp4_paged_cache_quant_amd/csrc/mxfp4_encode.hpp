@@ -50,7 +50,16 @@ __device__ __forceinline__ void pin(int x) { asm volatile("" ::"v"(x)); }
 // One 32-element bf16 block held by one lane: 64 bytes, four 16-byte loads.
 struct Bf16Block {
   static constexpr int kElemBytes = 2;
+  static constexpr int kPerWord = 2;   // elements per 32-bit word
   uint4 v[4];
+  // word k (elements 2k, 2k+1) and element h of a word, as fp32 (exact)
+  __device__ __forceinline__ uint32_t word(int k) const {
+    const uint4& q = v[k >> 2];
+    return (k & 3) == 0 ? q.x : (k & 3) == 1 ? q.y : (k & 3) == 2 ? q.z : q.w;
+  }
+  static __device__ __forceinline__ float elem(uint32_t w, int h) {
+    return __uint_as_float(h ? (w & 0xffff0000u) : (w << 16));
+  }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = load16(rs, off + 16u * i);
@@ -89,7 +98,13 @@ struct Bf16Block {
 // One 32-element fp32 block held by one lane: 128 bytes, eight 16-byte loads.
 struct F32Block {
   static constexpr int kElemBytes = 4;
+  static constexpr int kPerWord = 1;
   uint4 v[8];
+  __device__ __forceinline__ uint32_t word(int k) const {
+    const uint4& q = v[k >> 2];
+    return (k & 3) == 0 ? q.x : (k & 3) == 1 ? q.y : (k & 3) == 2 ? q.z : q.w;
+  }
+  static __device__ __forceinline__ float elem(uint32_t w, int) { return __uint_as_float(w); }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = load16(rs, off + 16u * i);

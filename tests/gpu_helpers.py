@@ -91,3 +91,40 @@ def check_topk_end_to_end(ref_rows, bound_rows, ks, ke, k, idx_rows, what="", ab
         assert ok, f"{what}: end-to-end top-k, row {j}"
         exact_rows += exact_req
     return exact_rows
+
+
+def split_new_tokens(case, bt):
+    """The cache before the step (every token but the last next_n of each sequence)
+    and the step's new K rows with their slots through block table ``bt`` (-1
+    where the position is < 0 or the table entry is not a page)."""
+    lens = case["context_lens"].astype(np.int64)
+    nn = case["next_n"]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    pre_slots = case["slot_mapping"].copy()
+    B = len(lens)
+    k = case["k"]
+    filler = k[0] if len(k) else np.zeros(128, k.dtype)
+    k_new = np.empty((B * nn, 128), dtype=k.dtype)
+    new_slots = np.full(B * nn, -1, np.int64)
+    for b in range(B):
+        for i in range(nn):
+            pos = lens[b] - nn + i
+            if pos >= 0:
+                k_new[b * nn + i] = k[starts[b] + pos]
+                page = int(bt[b, pos // 64])
+                if 0 <= page < case["num_pages"]:
+                    new_slots[b * nn + i] = page * 64 + pos % 64
+                pre_slots[starts[b] + pos] = -1
+            else:
+                k_new[b * nn + i] = filler
+    return pre_slots, k_new, new_slots
+
+
+def rope_tables(n_rows, rope_dim, base=10000.0):
+    """cos / sin of the standard angle table pos * base**(-2j/rope_dim), rounded to
+    fp32 (an input of the RoPE calls, built here for the tests)."""
+    half = rope_dim // 2
+    j = np.arange(half)
+    inv = base ** (-2.0 * j / max(rope_dim, 1))
+    ang = np.arange(n_rows)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)

@@ -45,7 +45,7 @@ def test_header_declarations_are_exported(L):
 
 
 def test_version_and_strerror(L):
-    assert L.idx_version() == 105
+    assert L.idx_version() == 106
     for st in range(5):
         assert L.idx_strerror(st)
     assert L.idx_strerror(99) == b"unknown status"
@@ -288,3 +288,54 @@ def test_kpool_insert_argument_validation(L):
     assert f(P, 0, 3, 128, None, None, None, 4, 0, 0, None, 4, 64, None, None) == OK  # n < kpool
     if not _has_gpu():
         assert f(P, 0, 8, 128, P, P2, P, 4, 1, 1, P2, 4, 64, None, None) == ERR_NO_DEVICE
+
+
+def _rope(rope_dim=64, mode=0, cos=P, sin=P2, table_rows=8, positions=None):
+    return mx._Rope(cos, sin, table_rows, positions, rope_dim, mode)
+
+
+def test_insert_quantize_rope_argument_validation(L):
+    # idx_insert_quantize_rope(k, k_dtype, n, k_stride, slots, cache, num_pages, page, q, q_dtype,
+    #                          q_rows, q_stride, q_heads, rope, q_values, q_scales, stream)
+    def call(rope, q_rows=16, q_heads=8, n=4):
+        r = rope
+        return L.idx_insert_quantize_rope(P, 0, n, 128, P, P2, 4, 64, P, 0, q_rows, 128, q_heads,
+                                          None if r is None else ctypes.addressof(r), P, P2, None)
+    assert call(None) == ERR_ARG                                 # no rope block
+    assert call(_rope(rope_dim=24)) == ERR_ARG                   # rope_dim % 16
+    assert call(_rope(rope_dim=144)) == ERR_ARG                  # rope_dim > 128
+    assert call(_rope(mode=2)) == ERR_ARG                        # pairing
+    assert call(_rope(cos=MIS)) == ERR_ARG                       # misaligned table
+    assert call(_rope(cos=None)) == ERR_ARG                      # missing table
+    assert call(_rope(positions=MIS)) == ERR_ARG                 # misaligned positions
+    assert call(_rope(table_rows=-1)) == ERR_ARG
+    assert call(_rope(table_rows=1)) == ERR_ARG                  # 2 tokens, 1 table row, no positions
+    assert call(_rope(), q_heads=0) == ERR_ARG
+    assert call(_rope(), q_rows=12, q_heads=8) == ERR_ARG        # rows not a multiple of heads
+    assert call(_rope(), q_rows=0, n=0) == OK                    # nothing to do
+    if not _has_gpu():
+        assert call(_rope()) == ERR_NO_DEVICE
+        assert call(_rope(rope_dim=0, cos=None, sin=None)) == ERR_NO_DEVICE
+        assert call(_rope(table_rows=1, positions=P)) == ERR_NO_DEVICE
+
+
+def test_logits_paged_insert_rope_argument_validation(L):
+    def call(rope, H=32, next_n=1, max_len=64, B=1, dtype=0):
+        return L.idx_logits_paged_insert_rope(P, P, dtype, P, P, 4, 64, P, 1, P, B, next_n, H,
+                                              max_len, P, 64, 1,
+                                              None if rope is None else ctypes.addressof(rope),
+                                              None)
+    assert call(None) == ERR_ARG
+    for dim in (16, 32, 48, 96, 112):                            # neox: 64 or 128 only
+        assert call(_rope(rope_dim=dim, mode=0)) == ERR_ARG
+    assert call(_rope(rope_dim=24, mode=1)) == ERR_ARG
+    assert call(_rope(mode=3)) == ERR_ARG
+    assert call(_rope(sin=MIS)) == ERR_ARG
+    assert call(_rope(positions=MIS)) == ERR_ARG
+    assert call(_rope(), H=24) == ERR_ARG
+    assert call(_rope(), next_n=17) == ERR_ARG
+    assert call(_rope(), dtype=2) == ERR_ARG
+    assert call(_rope(), B=0) == OK
+    if not _has_gpu():
+        for dim, mode in ((64, 0), (128, 0), (0, 0), (48, 1), (16, 1)):
+            assert call(_rope(rope_dim=dim, mode=mode)) == ERR_NO_DEVICE

@@ -15,41 +15,14 @@ import mxfp4_paged_cache_quant_amd as mx
 import workloads
 from oracle import logits as olog, paged_cache as opc
 from tests.gpu_helpers import (CANARY, check_logits, check_topk_end_to_end, check_topk_sets, dev,
-                               exact, host, new_cache, oracle_q)
+                               exact, host, new_cache, oracle_q, split_new_tokens)
 
 pytestmark = pytest.mark.gpu
 
 
-def _split_new_tokens(case, bt):
-    """The cache before the step (every token but the last next_n of each sequence)
-    and the step's new K rows with their slots through block table ``bt`` (-1
-    where the position is < 0 or the table entry is not a page)."""
-    lens = case["context_lens"].astype(np.int64)
-    nn = case["next_n"]
-    starts = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
-    pre_slots = case["slot_mapping"].copy()
-    B = len(lens)
-    k = case["k"]
-    filler = k[0] if len(k) else np.zeros(128, k.dtype)
-    k_new = np.empty((B * nn, 128), dtype=k.dtype)
-    new_slots = np.full(B * nn, -1, np.int64)
-    for b in range(B):
-        for i in range(nn):
-            pos = lens[b] - nn + i
-            if pos >= 0:
-                k_new[b * nn + i] = k[starts[b] + pos]
-                page = int(bt[b, pos // 64])
-                if 0 <= page < case["num_pages"]:
-                    new_slots[b * nn + i] = page * 64 + pos % 64
-                pre_slots[starts[b] + pos] = -1
-            else:
-                k_new[b * nn + i] = filler
-    return pre_slots, k_new, new_slots
-
-
 def _both(case, clean=True, block_table=None):
     bt_np = case["block_table"] if block_table is None else block_table
-    pre_slots, k_new, new_slots = _split_new_tokens(case, bt_np)
+    pre_slots, k_new, new_slots = split_new_tokens(case, bt_np)
     bt = dev(bt_np)
     ctx, w, q = dev(case["context_lens"]), dev(case["w"]), dev(case["q"])
     cache_a = new_cache(case["num_pages"])

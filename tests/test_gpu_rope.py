@@ -11,18 +11,9 @@ import torch
 import mxfp4_paged_cache_quant_amd as mx
 import workloads
 from oracle import mxfp4 as omx, rope as orope
-from tests.gpu_helpers import dev, host
+from tests.gpu_helpers import dev, host, rope_tables
 
 pytestmark = pytest.mark.gpu
-
-
-def _tables(n_rows, rope_dim, base=10000.0):
-    """cos / sin of the standard angle table pos * base**(-2j/rope_dim), rounded to fp32."""
-    half = rope_dim // 2
-    j = np.arange(half)
-    inv = base ** (-2.0 * j / max(rope_dim, 1))
-    ang = np.arange(n_rows)[:, None] * inv[None, :]
-    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
 def _exact(q, dtype):
@@ -37,7 +28,7 @@ def test_rope_quantize_bit_exact(dtype, mode, rope_dim):
     T, H = 300, 32
     x = workloads.draw_values(rng, (T, H, 128), "lognormal")
     q = workloads.bf16_bits(x) if dtype == "bf16" else x
-    cos, sin = _tables(5000, rope_dim)
+    cos, sin = rope_tables(5000, rope_dim)
     pos = rng.integers(0, 5000, size=T).astype(np.int64)
     vals, scales = mx.quantize_rope(dev(q), dev(cos), dev(sin), rope_dim, mode, positions=dev(pos))
     torch.cuda.synchronize()
@@ -51,7 +42,7 @@ def test_rope_without_positions_and_out_of_range_positions():
     rng = np.random.default_rng(5)
     T, H = 40, 16
     q = workloads.bf16_bits(rng.standard_normal((T, H, 128), dtype=np.float32))
-    cos, sin = _tables(64, 64)
+    cos, sin = rope_tables(64, 64)
     vals, scales = mx.quantize_rope(dev(q), dev(cos), dev(sin), 64, "neox")
     wc, ws = orope.quantize_rope(omx.bf16_bits_to_f64(q), cos, sin, 64, "neox")
     torch.cuda.synchronize()
@@ -85,7 +76,7 @@ def test_rope_decode_query_16x32():
     """The decode workload's query (16 tokens x 32 heads, bf16) at positions 8191,
     rotated over its first 64 dims."""
     case = workloads.paged_decode()
-    cos, sin = _tables(8192, 64)
+    cos, sin = rope_tables(8192, 64)
     pos = (case["context_lens"].astype(np.int64) - 1)
     vals, scales = mx.quantize_rope(dev(case["q"]), dev(cos), dev(sin), 64, "neox", positions=dev(pos))
     torch.cuda.synchronize()
