@@ -8,7 +8,9 @@ the 16 new tokens' K -- quantize + scatter --, MXFP4 quantization of the 16x32
 query rows, paged logits over all 131072 cached tokens) -> top-2048 per row.
 Metric: scored cache tokens per second = sum over rows of the visible context /
 step time.  The same step as three calls (idx_insert_quantize, idx_logits_paged,
-idx_topk) is timed beside it.
+idx_topk) is timed beside it, and so is the step with the query RoPE fused into
+its encode (idx_logits_paged_insert_rope: first 64 dims, neox pairs, each row
+at its token's position).
 
 Timing: the step is captured in HIP graphs; W untimed warm-up steps, then
 exactly K steps between two device synchronizations.  The steps rotate over
@@ -94,12 +96,17 @@ class DecodeSet:
         self.qs = torch.empty((B, H, 4), dtype=torch.uint8, device="cuda")
         self.logits = torch.empty((B, case["width"]), dtype=torch.float32, device="cuda")
         self.idx = torch.empty((B, case["topk"]), dtype=torch.int32, device="cuda")
+        self.cos, self.sin = base["cos"], base["sin"]      # read-only angle tables, shared
+
+
+ROPE_DIM = 64          # decode step with the query RoPE fused: first 64 dims, neox pairs
 
 
 def build_decode_sets(case, n_sets):
     import numpy as np
     import torch
     import mxfp4_paged_cache_quant_amd as mx
+    import workloads
     cache = torch.zeros((case["num_pages"], 64 * 68), dtype=torch.uint8, device="cuda")
     mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
     last = np.cumsum(case["context_lens"]) - 1
@@ -108,6 +115,8 @@ def build_decode_sets(case, n_sets):
     base = dict(cache=cache, k_new=dev(case["k"][last]), slot_new=dev(case["slot_mapping"][last]),
                 q=dev(case["q"]), w=dev(case["w"]), bt=dev(case["block_table"]),
                 ctx=dev(case["context_lens"]), ke=dev(ke))
+    cos, sin = workloads.rope_tables(int(case["width"]), ROPE_DIM)
+    base["cos"], base["sin"] = dev(cos), dev(sin)
     sets = [DecodeSet(base, case) for _ in range(n_sets)]
     torch.cuda.synchronize()
     return sets
@@ -123,6 +132,11 @@ def decode_ops(case):
         "logits_paged_insert": lambda s: mx.logits_paged_insert(s.q, s.k_new, s.w, s.cache, s.bt,
                                                                 s.ctx, 1, W, logits=s.logits,
                                                                 clean=False),
+        # the same with the query rotated first (RoPE over its first ROPE_DIM dims, each
+        # row at its token's position)
+        "logits_paged_insert_rope": lambda s: mx.logits_paged_insert_rope(
+            s.q, s.k_new, s.w, s.cache, s.bt, s.ctx, 1, W, s.cos, s.sin, ROPE_DIM, "neox",
+            logits=s.logits, clean=False),
         # the same as two launches: the encodes, then the logits
         "insert_quantize": lambda s: mx.insert_quantize(s.k_new, s.slot_new, s.cache, s.q, s.qv, s.qs),
         # clean=False: the top-k reads each row only up to its visible end
@@ -792,6 +806,8 @@ def main():
     elapsed, per_kernel, per_spread = bench_decode(args, case, sets, ["logits_paged_insert", "topk"])
     sep_elapsed, sep_kernel, _ = bench_decode(args, case, sets,
                                               ["insert_quantize", "logits_paged", "topk"])
+    rope_elapsed, rope_kernel, _ = bench_decode(args, case, sets,
+                                                ["logits_paged_insert_rope", "topk"])
     del sets
     ms_per_step = elapsed / args.steps * 1e3
     scored = int(np.sum(case["context_lens"]))
@@ -823,10 +839,15 @@ def main():
                 "us_per_step": round(sep_elapsed / args.steps * 1e6, 3),
                 "kernels_us": {k: round(v, 3) for k, v in sep_kernel.items()}}
     log(f"[bench] decode as three calls: {separate}")
+    with_rope = {"step": "logits_paged_insert_rope+topk", "rope_dim": ROPE_DIM, "pairing": "neox",
+                 "us_per_step": round(rope_elapsed / args.steps * 1e6, 3),
+                 "kernels_us": {k: round(v, 3) for k, v in rope_kernel.items()}}
+    log(f"[bench] decode with the query RoPE fused: {with_rope}")
 
     if args.only == "decode":
         print(json.dumps({"section": "decode", "us_per_step": round(ms_per_step * 1e3, 3),
-                          "kernels_us": per_kernel, "separate": separate}), flush=True)
+                          "kernels_us": per_kernel, "separate": separate,
+                          "with_rope": with_rope}), flush=True)
         return
 
     prefill = None
@@ -882,6 +903,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "decode_separate_calls": separate,
+        "decode_with_rope": with_rope,
         "prefill": prefill,
         "long_decode": long_decode,
         "long_prefill": long_prefill,

@@ -504,6 +504,9 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
       pg[p].scale[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, off_scale + 64u * j, 0, kNonTemporal);
     }
   }
+  // The RoPE encode below branches on the row's position: without a clobber the
+  // compiler sinks the page loads past it, behind the wait for the angles.
+  if constexpr (QS::kRope) asm volatile("" ::: "memory");
   // Keep the preloaded K rows live until here in every wave: a wave without a
   // new token would otherwise reuse their registers while the loads are in
   // flight, which waits for every load before the page loads can issue.

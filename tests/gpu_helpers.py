@@ -6,6 +6,7 @@ import numpy as np
 import torch
 
 import mxfp4_paged_cache_quant_amd as mx
+import workloads
 from oracle import mxfp4 as omx
 
 CANARY = 0xA5
@@ -120,11 +121,4 @@ def split_new_tokens(case, bt):
     return pre_slots, k_new, new_slots
 
 
-def rope_tables(n_rows, rope_dim, base=10000.0):
-    """cos / sin of the standard angle table pos * base**(-2j/rope_dim), rounded to
-    fp32 (an input of the RoPE calls, built here for the tests)."""
-    half = rope_dim // 2
-    j = np.arange(half)
-    inv = base ** (-2.0 * j / max(rope_dim, 1))
-    ang = np.arange(n_rows)[:, None] * inv[None, :]
-    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+rope_tables = workloads.rope_tables

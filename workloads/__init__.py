@@ -186,3 +186,13 @@ def long_prefill(seed=4):
     return prefill_case(seed, T=16384, S=122880, H=64, k_dist="student_t3",
                         q_dist="student_t3", topk=2048, spare_pages=0,
                         n_sample_rows=256, name="long_prefill_16384x122880")
+
+
+def rope_tables(n_rows, rope_dim, base=10000.0):
+    """RoPE angle tables, an input of the RoPE calls: cos / sin of
+    pos * base**(-2j/rope_dim) for pos < n_rows, j < rope_dim/2, rounded to fp32."""
+    half = rope_dim // 2
+    j = np.arange(half)
+    inv = base ** (-2.0 * j / max(rope_dim, 1))
+    ang = np.arange(n_rows)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
