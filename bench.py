@@ -697,13 +697,25 @@ KERNEL_SOURCES = {          # kernel-name prefix -> the source it is compiled fr
 
 
 def _source_hash(kernel):
+    """16 hex digits of the sha256 of the kernel's source file and of the local
+    headers it includes, recursively; launch.hpp (host-side launcher
+    declarations, no device code) is left out."""
     import hashlib
+    import re
+    csrc = os.path.join(ROOT, "mxfp4_paged_cache_quant_amd", "csrc")
     for prefix, src in KERNEL_SOURCES.items():
         if kernel.startswith(prefix):
-            path = os.path.join(ROOT, "mxfp4_paged_cache_quant_amd", "csrc", src)
-            h = hashlib.sha256(open(path, "rb").read())
-            for common in ("common.hpp", "logits_reduce.hpp", "mxfp4_encode.hpp"):
-                h.update(open(os.path.join(os.path.dirname(path), common), "rb").read())
+            h = hashlib.sha256()
+            seen, todo = set(), [src]
+            while todo:
+                name = todo.pop(0)
+                path = os.path.join(csrc, name)
+                if name in seen or name == "launch.hpp" or not os.path.exists(path):
+                    continue
+                seen.add(name)
+                text = open(path, "rb").read()
+                h.update(text)
+                todo += re.findall(r'#include "([^"]+)"', text.decode())
             return h.hexdigest()[:16]
     return None
 
@@ -720,6 +732,12 @@ def _mean_counter(csv_path):
     for r in csv.DictReader(open(csv_path)):
         agg[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+# bench.py arguments of the counter runs, per section (eager launches: the
+# counters are collected per dispatch)
+PMC_ARGS = {"copy": "--eager", "decode": "--eager --steps 96 --warmup 16 --sets 32 --kernel-reps 2",
+            "long_decode": "--eager", "long_prefill": "--eager"}
 
 
 def pmc_summarize(root, section):
@@ -745,8 +763,9 @@ def pmc_summarize(root, section):
                       "traffic_bytes": round(fetch[k] * 1024 * f_scale + write[k] * 1024 * w_scale),
                       "source_sha256_16": src}
     out = {"section": section,
-           "commands": [f"rocprofv3 --pmc {c} -f csv -d <dir>/{sec}_{c} -o run -- python3 bench.py "
-                        f"--only {sec} --eager" for sec in ("copy", section)
+           "commands": [f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 180 rocprofv3 --pmc {c} "
+                        f"-f csv -d <dir>/{sec}_{c} -o run -- python3 <repo>/bench.py --only {sec} "
+                        f"{PMC_ARGS.get(sec, '--eager')}" for sec in ("copy", section)
                         for c in ("FETCH_SIZE", "WRITE_SIZE")],
            "calibration": {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
                            "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
