@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context decode and long prefill measurements")
     ap.add_argument("--only", choices=["decode", "prefill", "long_decode", "long_prefill", "copy",
-                                       "fp8"],
+                                       "fp8", "kpool"],
                     help="run one section only and print its result (for profiler runs)")
     ap.add_argument("--eager", action="store_true",
                     help="launch kernels directly instead of replaying HIP graphs")
@@ -543,6 +543,48 @@ def bench_fp8(decode_case):
     return out
 
 
+KPOOL = 4                  # tokens pooled per K row (the calls' index_kpool; the pages fix no value)
+KPOOL_TOKENS = 1 << 20
+
+
+def bench_kpool():
+    """Pooled K insert (idx_kpool_insert): 1,048,576 bf16 tokens with fp32 gate scores,
+    kpool 4, i.e. 262,144 pool rows written through a permuted page order, as MXFP4
+    and as FP8 rows.  HBM-bound: every token's K (256 B) and gate row (512 B) and
+    slot (8 B) are read once, each pool row is written once."""
+    import numpy as np
+    import torch
+    import mxfp4_paged_cache_quant_amd as mx
+    n, kp = KPOOL_TOKENS, KPOOL
+    gen = torch.Generator(device="cuda").manual_seed(2026)
+    k = torch.randn((n, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    gate = torch.randn((n, 128), generator=gen, device="cuda")
+    ape = torch.randn((kp, 128), generator=gen, device="cuda") * 0.1
+    rows = n // kp
+    pages = rows // 64
+    # pool-granular slots: the last token of pool j carries its slot, the others -1
+    perm = np.random.default_rng(7).permutation(pages)
+    pool = np.arange(rows)
+    slots_np = np.full(n, -1, np.int64)
+    slots_np[pool * kp + kp - 1] = perm[pool // 64] * 64 + pool % 64
+    slots = dev(slots_np)
+    out = {"workload": f"kpool_insert_{n}_tokens_kpool{kp}", "tokens": n, "kpool": kp,
+           "pool_rows": rows}
+    for fmt, row in (("mxfp4", 68), ("fp8", 132)):
+        cache = torch.zeros((pages, 64 * row), dtype=torch.uint8, device="cuda")
+        f = lambda cache=cache, fmt=fmt: mx.kpool_insert(k, gate, ape, slots, cache, kp, fmt)
+        f()
+        torch.cuda.synchronize()
+        sp = {}
+        t = time_fn(f, 10, 2, sp, fmt)
+        alg = n * (256 + 512 + 8) + rows * row + kp * 512
+        gbs = alg / (t * 1e-6) / 1e9
+        out[fmt] = {"us": round(t, 1), "p10_p90_us": sp[fmt], "alg_bytes": alg,
+                    "gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del cache
+    return out
+
+
 def bench_copy(nbytes=1 << 30, reps=5):
     """A plain device copy of known size: the HBM rate torch's copy kernel reaches,
     and the reference for scaling the profiler's byte counters."""
@@ -814,7 +856,7 @@ def main():
     EAGER = args.eager
     if args.only is not None:
         section = {"prefill": lambda: bench_prefill(args), "long_decode": bench_long_decode,
-                   "long_prefill": bench_long_prefill, "copy": bench_copy,
+                   "long_prefill": bench_long_prefill, "copy": bench_copy, "kpool": bench_kpool,
                    "fp8": lambda: bench_fp8(workloads.paged_decode())}
         if args.only in section:
             print(json.dumps({"section": args.only, "result": section[args.only]()}), flush=True)
@@ -886,6 +928,13 @@ def main():
         log(f"[bench] long prefill: {long_prefill}")
         torch.cuda.empty_cache()
 
+    kpool = None
+    if not args.no_long:
+        log("[bench] kpool insert, 1M tokens, kpool 4")
+        kpool = bench_kpool()
+        log(f"[bench] kpool: {kpool}")
+        torch.cuda.empty_cache()
+
     fp8 = None
     if not args.no_fp8:
         log("[bench] FP8 indexer cache (132 B/token) on the same workloads")
@@ -926,6 +975,7 @@ def main():
         "prefill": prefill,
         "long_decode": long_decode,
         "long_prefill": long_prefill,
+        "kpool_insert": kpool,
         "fp8": fp8,
         "device_copy": copy,
         "cpu_baseline": cpu,

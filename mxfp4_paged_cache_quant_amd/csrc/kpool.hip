@@ -16,10 +16,14 @@
 // write nothing.  The pooled fp32 rows can also be returned (P3's
 // return_compressed).
 //
-// Work mapping: 16 lanes per position, 8 dimensions per lane (the row
+// Work mapping: 16 lanes per written row, 8 dimensions per lane (the row
 // encoders' layout); each lane streams its 8 dims of the pool's kpool tokens
-// twice (maximum, then the weighted sums) -- 2 kpool short reads that stay
-// in cache for the neighbouring positions, whose pools overlap.
+// twice (maximum, then the weighted sums; the second read hits the cache).
+// Only one position in kpool ends a pool, so positions are not mapped to lane
+// groups directly: each wave reads the slots of 64 consecutive positions,
+// ballots the ones that write, and its four 16-lane groups take those four at
+// a time (mapped directly, kpool 4 left three groups in four idle and the
+// kernel bound by the idle groups' issue slots).
 #include "common.hpp"
 #include "fp8_encode.hpp"
 #include "launch.hpp"
@@ -28,7 +32,8 @@
 namespace mxidx {
 namespace {
 
-constexpr int kKpRowsPerBlock = 16;
+constexpr int kKpPositionsPerBlock = 256;   // 4 waves x 64 positions per step
+constexpr int kKpHeld = 4;                   // pools up to this size are held in registers
 
 template <bool kF32>
 __device__ __forceinline__ void load8(const void* base, int64_t row, int64_t stride, int sub,
@@ -58,21 +63,52 @@ __device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
   v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
-// kFmt 0: MXFP4 cache (68 B rows), 1: FP8 cache (132 B rows).
+// The pooled row of the pool ending at position i, encoded and written to
+// `slot` (in the cache); run by the 16 lanes of one group, lane `sub` holding
+// dimensions 8*sub .. 8*sub+7.  kFmt 0: MXFP4 cache (68 B rows), 1: FP8 cache
+// (132 B rows).
 template <bool kF32, int kFmt>
-__global__ __launch_bounds__(256) void kpool_insert_kernel(
-    const void* __restrict__ k, int64_t n, int64_t stride, const float* __restrict__ gate,
-    const float* __restrict__ ape, const int64_t* __restrict__ slot_mapping, int kpool,
-    int64_t num_slots, int pow2, uint8_t* __restrict__ cache, float* __restrict__ compressed) {
-  const int sub = threadIdx.x & 15;
-  for (int64_t i = (int64_t)blockIdx.x * kKpRowsPerBlock + (threadIdx.x >> 4); i < n;
-       i += (int64_t)gridDim.x * kKpRowsPerBlock) {
-    const int64_t slot = slot_mapping[i];         // same for the row's 16 lanes
-    if (i < kpool - 1 || slot < 0 || slot >= num_slots) continue;
-    const int64_t first = i - kpool + 1;
-    float m[8];
+__device__ __forceinline__ void pool_row(const void* __restrict__ k, int64_t stride,
+                                         const float* __restrict__ gate,
+                                         const float* __restrict__ ape, int kpool, int64_t i,
+                                         int64_t slot, int sub, int pow2,
+                                         uint8_t* __restrict__ cache,
+                                         float* __restrict__ compressed) {
+  const int64_t first = i - kpool + 1;
+  float m[8], ssum[8], acc[8];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) m[d] = neg_inf();
+  for (int d = 0; d < 8; ++d) {
+    m[d] = neg_inf();
+    ssum[d] = acc[d] = 0.f;
+  }
+  if (kpool <= kKpHeld) {
+    // the whole pool's rows loaded before any is used: one memory round trip
+    float z[kKpHeld][8], kv[kKpHeld][8];
+#pragma unroll
+    for (int j = 0; j < kKpHeld; ++j)
+      if (j < kpool) {
+        float a[8];
+        load8f(gate + (first + j) * kHeadDim + 8 * sub, z[j]);
+        load8f(ape + (int64_t)j * kHeadDim + 8 * sub, a);
+        load8<kF32>(k, first + j, stride, sub, kv[j]);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) z[j][d] = z[j][d] + a[d];
+      }
+#pragma unroll
+    for (int j = 0; j < kKpHeld; ++j)
+      if (j < kpool)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) m[d] = fmaxf(m[d], z[j][d]);
+#pragma unroll
+    for (int j = 0; j < kKpHeld; ++j)
+      if (j < kpool)
+#pragma unroll
+        for (int d = 0; d < 8; ++d) {
+          const float e = expf(z[j][d] - m[d]);
+          ssum[d] += e;
+          acc[d] += e * kv[j][d];
+        }
+  } else {
     for (int j = 0; j < kpool; ++j) {
       float g[8], a[8];
       load8f(gate + (first + j) * kHeadDim + 8 * sub, g);
@@ -80,9 +116,6 @@ __global__ __launch_bounds__(256) void kpool_insert_kernel(
 #pragma unroll
       for (int d = 0; d < 8; ++d) m[d] = fmaxf(m[d], g[d] + a[d]);
     }
-    float ssum[8], acc[8];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) ssum[d] = acc[d] = 0.f;
     for (int j = 0; j < kpool; ++j) {
       float g[8], a[8], kv[8];
       load8f(gate + (first + j) * kHeadDim + 8 * sub, g);
@@ -95,44 +128,79 @@ __global__ __launch_bounds__(256) void kpool_insert_kernel(
         acc[d] += e * kv[d];
       }
     }
-    float v[8];
+  }
+  float v[8];
 #pragma unroll
-    for (int d = 0; d < 8; ++d) v[d] = acc[d] / ssum[d];
-    if (compressed) {
-      float* c = compressed + i * kHeadDim + 8 * sub;
-      *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
-      *reinterpret_cast<float4*>(c + 4) = make_float4(v[4], v[5], v[6], v[7]);
-    }
-    const int64_t page = slot / kPage, off = slot % kPage;
-    uint32_t amax = 0;
+  for (int d = 0; d < 8; ++d) v[d] = acc[d] / ssum[d];
+  if (compressed) {
+    float* c = compressed + i * kHeadDim + 8 * sub;
+    *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(c + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  const int64_t page = slot / kPage, off = slot % kPage;
+  uint32_t amax = 0;
 #pragma unroll
-    for (int d = 0; d < 8; ++d) amax = max(amax, __float_as_uint(v[d]) & 0x7fffffffu);
-    if constexpr (kFmt == 0) {
-      // MXFP4: 4 lanes per 32-element block
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-      amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
-      const int E = block_exponent(amax);
-      const float sc = block_divisor(amax, E);
-      uint32_t out = 0;
-      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], sc, 0);
-      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], sc, 1);
-      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], sc, 2);
-      out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], sc, 3);
-      uint8_t* base = cache + page * kPageBytes;
-      *reinterpret_cast<uint32_t*>(base + off * kCodeBytes + 4 * sub) = out;
-      if ((sub & 3) == 0) base[kPageCodeBytes + off * kScaleBytes + (sub >> 2)] = (uint8_t)(E + 127);
-    } else {
-      // FP8: one scale for the row's 16 lanes
+  for (int d = 0; d < 8; ++d) amax = max(amax, __float_as_uint(v[d]) & 0x7fffffffu);
+  if constexpr (kFmt == 0) {
+    // MXFP4: 4 lanes per 32-element block
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
+    const int E = block_exponent(amax);
+    const float sc = block_divisor(amax, E);
+    uint32_t out = 0;
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[0], v[1], sc, 0);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[2], v[3], sc, 1);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[4], v[5], sc, 2);
+    out = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out, v[6], v[7], sc, 3);
+    uint8_t* base = cache + page * kPageBytes;
+    *reinterpret_cast<uint32_t*>(base + off * kCodeBytes + 4 * sub) = out;
+    if ((sub & 3) == 0) base[kPageCodeBytes + off * kScaleBytes + (sub >> 2)] = (uint8_t)(E + 127);
+  } else {
+    // FP8: one scale for the row's 16 lanes
 #pragma unroll
-      for (int msk = 1; msk < 16; msk <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, msk));
-      const float s = fp8_row_scale(amax, pow2 != 0);
-      float y[8];
+    for (int msk = 1; msk < 16; msk <<= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, msk));
+    const float s = fp8_row_scale(amax, pow2 != 0);
+    float y[8];
 #pragma unroll
-      for (int d = 0; d < 8; ++d) y[d] = v[d] / s;
-      uint8_t* base = cache + page * kF8PageBytes;
-      *reinterpret_cast<uint2*>(base + off * kF8Row + 8 * sub) =
-          make_uint2(pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7]));
-      if (sub == 0) *reinterpret_cast<float*>(base + kF8PageValues + off * 4) = s;
+    for (int d = 0; d < 8; ++d) y[d] = v[d] / s;
+    uint8_t* base = cache + page * kF8PageBytes;
+    *reinterpret_cast<uint2*>(base + off * kF8Row + 8 * sub) =
+        make_uint2(pack_fp8x4(y[0], y[1], y[2], y[3]), pack_fp8x4(y[4], y[5], y[6], y[7]));
+    if (sub == 0) *reinterpret_cast<float*>(base + kF8PageValues + off * 4) = s;
+  }
+}
+
+template <bool kF32, int kFmt>
+__global__ __launch_bounds__(256) void kpool_insert_kernel(
+    const void* __restrict__ k, int64_t n, int64_t stride, const float* __restrict__ gate,
+    const float* __restrict__ ape, const int64_t* __restrict__ slot_mapping, int kpool,
+    int64_t num_slots, int pow2, uint8_t* __restrict__ cache, float* __restrict__ compressed) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int grp = lane >> 4;                     // lane group: 16 lanes per written row
+  const int sub = lane & 15;
+  const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t base = wave * kWave; base < n; base += waves * kWave) {
+    // the slots of 64 consecutive positions, one per lane; the writing ones balloted
+    const int64_t i = base + lane;
+    const int64_t slot = i < n ? slot_mapping[i] : -1;
+    uint64_t todo = __ballot(i >= kpool - 1 && slot >= 0 && slot < num_slots);
+    while (todo) {                               // wave-uniform
+      // the next four writing positions, one per group (bit < 0: none left)
+      int bit = -1;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int b = todo ? __builtin_ctzll(todo) : -1;
+        if (g == grp) bit = b;
+        todo &= todo - 1;
+      }
+      // the group's slot, from the lane that read it (every lane takes part)
+      const int src = bit < 0 ? lane : bit;
+      const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)slot, src);
+      const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)((uint64_t)slot >> 32), src);
+      if (bit >= 0)                              // uniform over the group
+        pool_row<kF32, kFmt>(k, stride, gate, ape, kpool, base + bit,
+                             (int64_t)(((uint64_t)hi << 32) | lo), sub, pow2, cache, compressed);
     }
   }
 }
@@ -141,7 +209,7 @@ template <bool kF32, int kFmt>
 hipError_t launch_kp(const void* k, int64_t n, int64_t stride, const float* gate, const float* ape,
                      const int64_t* slots, int kpool, int64_t num_pages, bool pow2, uint8_t* cache,
                      float* compressed, hipStream_t stream) {
-  const int64_t blocks = (n + kKpRowsPerBlock - 1) / kKpRowsPerBlock;
+  const int64_t blocks = (n + kKpPositionsPerBlock - 1) / kKpPositionsPerBlock;
   const int grid = (int)(blocks < 256 * 32 ? blocks : 256 * 32);
   hipLaunchKernelGGL((kpool_insert_kernel<kF32, kFmt>), dim3(grid), dim3(256), 0, stream, k, n,
                      stride, gate, ape, slots, kpool, num_pages * kPage, pow2 ? 1 : 0, cache,

@@ -148,3 +148,37 @@ def test_kpool_fewer_tokens_than_a_pool_writes_nothing():
                     dev(np.array([0, 1, 2], np.int64)), cache, 4)
     torch.cuda.synchronize()
     assert torch.all(cache == CANARY)
+
+
+def test_kpool_one_million_tokens_sampled():
+    """The bench's size (1,048,576 bf16 tokens, kpool 4, 262,143 pool rows over
+    permuted pages, pool ends shifted by two positions from the chunk start), checked
+    on 512 sampled pool rows against the oracle's pool of the same four tokens."""
+    n, kp = 1 << 20, 4
+    rng = np.random.default_rng(404)
+    x = workloads.draw_values(rng, (n, 128), "lognormal")
+    k = workloads.bf16_bits(x)
+    gate = (3 * rng.standard_normal((n, 128))).astype(np.float32)
+    ape = rng.standard_normal((kp, 128)).astype(np.float32)
+    ends = np.arange(kp + 1, n, kp)                  # positions 5, 9, ...: pools 2..5, 6..9, ...
+    num_pages = -(-len(ends) // 64)
+    slots = np.full(n, -1, np.int64)
+    slots[ends] = rng.permutation(num_pages * 64)[:len(ends)]
+    cache = torch.full((num_pages, 64 * 68), CANARY, dtype=torch.uint8, device="cuda")
+    mx.kpool_insert(dev(k), dev(gate), dev(ape), dev(slots), cache, kp)
+    torch.cuda.synchronize()
+    flat = host(cache).reshape(-1)
+    for i in np.sort(rng.choice(ends, 512, replace=False)):
+        sl = slice(i - kp + 1, i + 1)
+        kx = omx.bf16_bits_to_f64(k[sl])
+        pooled = okp.pooled_rows(kx, gate[sl], ape, kp)[-1]
+        d = _delta(kx, gate[sl], ape, kp)[-1]
+        p, o = divmod(int(slots[i]), 64)
+        c0, s0 = p * 4352 + o * 64, p * 4352 + 4096 + o * 4
+        _check_mxfp4_row(flat[c0:c0 + 64], flat[s0:s0 + 4], pooled, d)
+    # the one slot no pool maps to keeps the canary
+    unused = np.setdiff1d(np.arange(num_pages * 64), slots[ends])
+    for s_ in unused:
+        p, o = divmod(int(s_), 64)
+        assert np.all(flat[p * 4352 + o * 64:p * 4352 + o * 64 + 64] == CANARY)
+        assert np.all(flat[p * 4352 + 4096 + o * 4:p * 4352 + 4096 + o * 4 + 4] == CANARY)
