@@ -263,10 +263,25 @@ __global__ __launch_bounds__(kWave) void logits_paged_fp8_kernel(
     const int live = __builtin_amdgcn_readfirstlane((p < np && valid) ? 1 : 0);
     const int64_t page = __builtin_amdgcn_readfirstlane(live ? pid : 0);
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(cache + page * kF8PageBytes, live ? kF8PageBytes : 0);
+    // Lane (g, n) takes the 32 bytes 32g.. of key n as two 16-byte loads, so each
+    // load instruction touches every 64-byte line of the 2 KB tile at half width
+    // and the next touches the same lines.  Large batches load through the caches
+    // (as non-temporal loads the second touch refetched the lines: 153 -> 134 us
+    // on the long-context batch); small ones, whose logits stay in the caches for
+    // the top-k, keep the non-temporal loads (cached, the 16 x 8192 decode step
+    // took 18.2 us instead of 16.8).
+    if (stream_out) {                            // wave-uniform
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pg[p].v[j][0] = ld16<kNonTemporal>(rs, off_v + 2048u * j);
-      pg[p].v[j][1] = ld16<kNonTemporal>(rs, off_v + 2048u * j + 16u);
+      for (int j = 0; j < 4; ++j) {
+        pg[p].v[j][0] = ld16<0>(rs, off_v + 2048u * j);
+        pg[p].v[j][1] = ld16<0>(rs, off_v + 2048u * j + 16u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        pg[p].v[j][0] = ld16<kNonTemporal>(rs, off_v + 2048u * j);
+        pg[p].v[j][1] = ld16<kNonTemporal>(rs, off_v + 2048u * j + 16u);
+      }
     }
     pg[p].scale = __uint_as_float(
         __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(kF8PageValues + 4 * lane), 0, kNonTemporal));
