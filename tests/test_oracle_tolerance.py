@@ -8,10 +8,11 @@ Each is pinned here against values fixed independently of its code:
 * logits_close: boundary cases whose float64 arithmetic is exact (powers of
   two for the relative term, A = 2**21 * 2**m for the absolute one), so the
   exact tolerance and the first float64 past it are known;
-* topk_end_to_end_ok: hand-worked rows whose verdicts follow from the rule
-  read off the benchmark spec's margin clause (every column clearly above the k-th
-  value present, none clearly below it, exact sets only when the k / k+1 margin
-  exceeds twice the tolerance);
+* topk_end_to_end_ok: hand-worked rows whose outcomes follow from the
+  ordering-margin rule (P2 "Enable SM86 MXFP4 sparse-indexer cache", section
+  "Validation": exact top-k sets with an ordering margin) -- every column
+  clearly above the k-th value present, none clearly below it, exact sets only
+  when the k / k+1 margin exceeds twice the tolerance;
 * kth_value: a plain Python sort;
 * the A bound: exact rational arithmetic (fractions.Fraction) over the bit
   fields of the MXFP4 rows.
@@ -94,7 +95,7 @@ def logits_close_failures(fn):
     # NaN and inf never pass against a finite reference
     expect("nan", float("nan"), 1.0, 1.0, False)
     expect("inf", float("inf"), 1.0, 2.0 ** 40, False)
-    # elementwise: one call over many entries agrees with the scalar verdicts
+    # elementwise: one call over many entries agrees with the scalar outcomes
     g = np.array([1.0, _next_up(1.0), -1.0, 0.5])
     got = np.asarray(fn(g, np.zeros(4), np.full(4, 2.0 ** 21)))
     if got.tolist() != [True, False, True, True]:
@@ -170,7 +171,7 @@ ROW2 = np.array([10.0, 5.0, 4.95, 4.88, 1.0])
 
 
 def e2e_failures(fn):
-    """Hand-worked verdicts for a topk_end_to_end_ok implementation; returns the
+    """Hand-worked outcomes for a topk_end_to_end_ok implementation; returns the
     checks it gets wrong.  Each case is (name, idx, ks, ke, k, tol, ok, exact)."""
     cases = [
         # k = 3: v_k = 3+1e-9 (c3), v_k+1 = 3 (c2), margin 1e-9
@@ -223,7 +224,7 @@ def e2e_failures(fn):
         for name, idx, ks, ke, k, tol, ok, exact in table:
             try:
                 got_ok, got_exact = fn(np.array(idx), row, ks, ke, k, tol)
-            except Exception:                       # a crash is a wrong verdict too
+            except Exception:                       # a crash is a wrong outcome too
                 bad.append(name)
                 continue
             if bool(got_ok) != ok or (exact is not None and bool(got_exact) != exact):
@@ -232,7 +233,7 @@ def e2e_failures(fn):
 
 
 def test_hand_worked_rows_by_plain_sort():
-    """The verdict table's k-th values, from a plain Python sort of ROW."""
+    """The outcome table's k-th values, from a plain Python sort of ROW."""
     def ranked(ks, ke):
         return sorted(range(ks, ke), key=lambda c: (-ROW[c], c))
     assert ranked(0, 8)[:4] == [0, 5, 3, 2]
