@@ -51,7 +51,12 @@
 namespace mxidx {
 namespace {
 
+// Pages per wave: 3 (13 KB of cache in flight) for batches that fill the chip;
+// a small batch (at most ~2 waves per SIMD at 3 pages) runs one-row decode with
+// the query source's kSmallPages (fewer pages: less work after the last page
+// arrives; 16 x 8192, one launch: 4.65 -> 4.47 us at 2 pages).
 constexpr int kPagesPerWave = 3;
+constexpr int64_t kSmallGrid = 2048;
 constexpr int64_t kCachedLogitsBytes = 4 << 20;
 struct PageRegs {
   uint4 code[4];      // tile j: block g of token 16*j + n
@@ -92,6 +97,7 @@ struct PackedQuery {
   template <int NH>
   using Fetched = QueryRegs<NH>;
   static constexpr bool kRope = false;
+  static constexpr int kSmallPages = 1;    // 16 x 8192: 4.33 -> 4.24 us
   template <int NH>
   __device__ __forceinline__ QueryRegs<NH> fetch(int64_t r, int g, int n, int64_t) const {
     return load_query<NH>(q_values, q_scales, weights, r, g, n);
@@ -207,6 +213,9 @@ struct RawQuery : RopeField<kRopeOn> {
   const float* weights;
   static constexpr bool kInsert = true;
   static constexpr bool kRope = kRopeOn;
+  // each wave also encodes the query rows: 2 pages per wave for small batches,
+  // 3 with RoPE, whose per-wave rotation more waves would repeat (6.74 / 6.83 us)
+  static constexpr int kSmallPages = kRopeOn ? 3 : 2;
   using Block = Blk;
   template <int NH>
   struct Fetched {
@@ -327,7 +336,7 @@ __device__ __forceinline__ float page_score(const PageRegs& pg, const QueryRegs<
 // NN == 0: any next_n, one row at a time.  QS: the query source; with
 // QS::kInsert the wave holding a new token's page also encodes that token,
 // writes it to its cache slot and scores the page with it.
-template <int NH, int NN, typename QS>
+template <int NH, int NN, int PPW, typename QS>
 __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     QS qs, const uint8_t* cache, int64_t num_pages,   // written when inserting: no restrict
     const int32_t* __restrict__ block_table, int64_t bt_row_stride,
@@ -337,15 +346,15 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
   const int lane = threadIdx.x;
   const int g = lane >> 4;       // 32-element block this lane supplies / head quad it receives
   const int n = lane & 15;       // token within a 16-token tile / head within a group
-  const int64_t lp0 = (int64_t)blockIdx.x * kPagesPerWave;
+  const int64_t lp0 = (int64_t)blockIdx.x * PPW;
   const int64_t wpages = (width + kPage - 1) / kPage;
   const int64_t row0 = (int64_t)b * next_n;
 
   // Context length and the wave's block-table entries in one round trip: both
   // as vector loads (a scalar load of the length would have to retire before
-  // the table load could issue).  Lane p < kPagesPerWave reads the entry of page lp0 + p;
+  // the table load could issue).  Lane p < PPW reads the entry of page lp0 + p;
   // the other lanes fall outside the descriptor and read 0 without an access.
-  const int bt_count = (int)min((int64_t)kPagesPerWave, wpages - lp0);
+  const int bt_count = (int)min((int64_t)PPW, wpages - lp0);
   const int bt_lane = (int)__builtin_amdgcn_raw_buffer_load_b32(
       buffer_rsrc(block_table + (int64_t)b * bt_row_stride + lp0, 4 * bt_count), 4u * lane, 0, 0);
   const uint32_t ctx_raw =
@@ -429,10 +438,10 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     if (clean)
       for (int i = 0; i < next_n; ++i)
 #pragma unroll
-        for (int p = 0; p < kPagesPerWave; ++p) store(row0 + i, (lp0 + p) * kPage, 0, 0.f);
+        for (int p = 0; p < PPW; ++p) store(row0 + i, (lp0 + p) * kPage, 0, 0.f);
     return;
   }
-  const int np = (int)min((int64_t)kPagesPerWave, (L - lp0 * kPage + kPage - 1) / kPage);
+  const int np = (int)min((int64_t)PPW, (L - lp0 * kPage + kPage - 1) / kPage);
 
   if constexpr (QS::kInsert) {
     // New token i sits at position P = context_len - next_n + i.  The wave
@@ -485,12 +494,12 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     }
   }
 
-  PageRegs pg[kPagesPerWave];
-  bool page_ok[kPagesPerWave];   // false: invalid block-table entry, the page is skipped
+  PageRegs pg[PPW];
+  bool page_ok[PPW];   // false: invalid block-table entry, the page is skipped
   const uint32_t off_code = 64u * n + 16u * g;
   const uint32_t off_scale = kPageCodeBytes + 4u * n;
 #pragma unroll
-  for (int p = 0; p < kPagesPerWave; ++p) {
+  for (int p = 0; p < PPW; ++p) {
     const int pid = __builtin_amdgcn_readlane(bt_lane, p);
     const bool valid = pid >= 0 && pid < num_pages;
     page_ok[p] = p >= np || valid;
@@ -532,15 +541,15 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
     }
 
   if (NN > 0) {
-    float out[kRowsHeld][kPagesPerWave];
+    float out[kRowsHeld][PPW];
 #pragma unroll
     for (int i = 0; i < kRowsHeld; ++i)
 #pragma unroll
-      for (int p = 0; p < kPagesPerWave; ++p) out[i][p] = page_score<NH>(pg[p], qr[i], lane);
+      for (int p = 0; p < PPW; ++p) out[i][p] = page_score<NH>(pg[p], qr[i], lane);
 #pragma unroll
     for (int i = 0; i < kRowsHeld; ++i)
 #pragma unroll
-      for (int p = 0; p < kPagesPerWave; ++p)
+      for (int p = 0; p < PPW; ++p)
         if (page_ok[p]) store(row0 + i, (lp0 + p) * kPage, L - NN + i + 1, out[i][p]);
   } else {
     for (int i = 0; i < next_n; ++i) {
@@ -548,7 +557,7 @@ __global__ __launch_bounds__(kWave) void logits_paged_kernel(
       const int64_t ke = L - next_n + i + 1;
       const QueryRegs<NH> q = qs.template finish<NH>(qs.template fetch<NH>(r, g, n, row_pos(i)));
 #pragma unroll
-      for (int p = 0; p < kPagesPerWave; ++p)
+      for (int p = 0; p < PPW; ++p)
         if (page_ok[p]) store(r, (lp0 + p) * kPage, ke, page_score<NH>(pg[p], q, lane));
     }
   }
@@ -564,10 +573,22 @@ hipError_t launch_nh(QS qs, const uint8_t* cache, int64_t num_pages, const int32
   // larger outputs stream past them (cached, the 33.5 MB of the 64 x 131072
   // batch slowed the logits from 64.7 to 69.3 us).
   const int stream_out = (int64_t)B * next_n * width * 4 > kCachedLogitsBytes ? 1 : 0;
-  const dim3 grid((unsigned)((pages + kPagesPerWave - 1) / kPagesPerWave), (unsigned)B);
+  const int64_t groups = (pages + kPagesPerWave - 1) / kPagesPerWave;
+  if constexpr (!QS::kRope || NH <= 4) {        // (RoPE holds one row up to 4 head groups)
+    if (next_n == 1 && (int64_t)B * groups < kSmallGrid) {
+      constexpr int P = QS::kSmallPages;
+      const dim3 small_grid((unsigned)((pages + P - 1) / P), (unsigned)B);
+      hipLaunchKernelGGL((logits_paged_kernel<NH, 1, P, QS>), small_grid, dim3(kWave), 0, stream,
+                         qs, cache, num_pages, bt, bt_stride, ctx, next_n, width, logits, ld,
+                         clean, stream_out);
+      return hipGetLastError();
+    }
+  }
+  const dim3 grid((unsigned)groups, (unsigned)B);
 #define MXIDX_PAGED_ROWS(nn)                                                                   \
-  hipLaunchKernelGGL((logits_paged_kernel<NH, nn, QS>), grid, dim3(kWave), 0, stream, qs, cache, \
-                     num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean, stream_out)
+  hipLaunchKernelGGL((logits_paged_kernel<NH, nn, kPagesPerWave, QS>), grid, dim3(kWave), 0,     \
+                     stream, qs, cache, num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, \
+                     clean, stream_out)
   // rows held in registers while rows * NH <= 8 (the query operands of 8 head
   // groups); <= 4 with RoPE, whose angle registers are held per row too
   bool held = true;
