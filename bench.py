@@ -283,6 +283,9 @@ def bench_prefill(args):
     for name, fn in ops.items():
         per[name] = time_fn(fn, 10, 4, spread, name)
     step_us = sum(per.values())
+    # the same logits with clean = 1 (columns outside [ks, ke) written as -inf); not in the step
+    t_clean = time_fn(lambda: mx.logits_prefill(qv, qs, kv, ksc, w, ks, ke, logits=logits,
+                                                clean=True), 10, 4)
     pairs = int(np.sum(case["ke"].astype(np.int64) - case["ks"]))
     flops = 2.0 * H * 128 * pairs
     tflops = flops / (per["logits_prefill"] * 1e-6) / 1e12
@@ -291,6 +294,7 @@ def bench_prefill(args):
         "logits_flop": flops, "logits_us": round(per["logits_prefill"], 2),
         "logits_tflops": round(tflops, 1),
         "logits_frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
+        "logits_clean1_us": round(t_clean, 2),
         "step_us": round(step_us, 2),
         "kernels_us": {k2: round(v, 2) for k2, v in per.items()},
         "kernels_p10_p90_us": spread,
@@ -650,8 +654,9 @@ def host_info():
 
 def cpu_baseline(case, seconds, prefill_case=None, long_prefill_case=None):
     """The oracle (never tuned for this) on bounded samples: decode steps of the
-    16 x 8192 workload (the headline metric), sampled query rows of the 8192
-    prefill chunk and the 256 sampled rows of the long prefill (throughput and
+    16 x 8192 workload (the headline metric), the whole tiny workload, three
+    sequences of the long-context batch, sampled query rows of the 8192 prefill
+    chunk and the 256 sampled rows of the long prefill (throughput and
     extrapolated totals, labelled as such)."""
     import numpy as np
     from oracle import logits as olog, mxfp4 as omx, paged_cache as opc, topk as otk
@@ -707,6 +712,58 @@ def cpu_baseline(case, seconds, prefill_case=None, long_prefill_case=None):
                 "logits_tflops": round(2.0 * Hp * 128 * pairs_s / t_q / 1e12, 4),
                 "extrapolated_full_s": round(est, 1), "extrapolated": True}
 
+    # config 0: the tiny workload's whole path (insert, q quantize, paged logits of its
+    # 4 query rows, top-64), repeated for about a second
+    import workloads
+    tc = workloads.tiny()
+    t0, reps = time.perf_counter(), 0
+    while time.perf_counter() - t0 < 1.0:
+        c = opc.insert(np.zeros((tc["num_pages"], 64 * 68), np.uint8), omx.f32_to_f64(tc["k"]),
+                       tc["slot_mapping"])
+        qc, qsc = omx.quantize_rows(omx.f32_to_f64(tc["q"]))
+        Ht = tc["H"]
+        ref = olog.paged_mqa_logits(qc.reshape(-1, Ht, 64), qsc.reshape(-1, Ht, 4), tc["w"], c,
+                                    tc["block_table"], tc["context_lens"], tc["next_n"],
+                                    tc["width"])
+        ke_t = olog.decode_visible_end(tc["context_lens"], tc["next_n"])
+        otk.top_k_per_row(ref.astype(np.float32), np.zeros_like(ke_t), ke_t, tc["topk"])
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    out["tiny"] = {"sample": "the whole tiny path (256 fp32 tokens inserted, 4 query rows x 32 "
+                             "heads quantized, paged logits, top-64), repeated",
+                   "ms_per_step": round(dt * 1e3, 2),
+                   "scored_tokens_per_s": round(float(np.sum(ke_t)) / dt, 1)}
+    long_decode_case = CASES.get("long_decode")
+    if long_decode_case is not None:
+        # config 2: a few sequences of the long-context batch, each with a cache of its own
+        # tokens only (the oracle's insert), its paged logits and top-2048; the batch's time
+        # extrapolated by scored tokens
+        lc = long_decode_case
+        lens = lc["context_lens"].astype(np.int64)
+        starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+        Hl = lc["H"]
+        picks = [int(np.argmin(lens)), int(np.argmax(lens)), len(lens) // 2]
+        t_l, tok_l = 0.0, 0
+        for b in picks:
+            L = int(lens[b])
+            t0 = time.perf_counter()
+            c = opc.insert(np.zeros((lc["num_pages"], 64 * 68), np.uint8),
+                           omx.bf16_bits_to_f64(lc["k"][starts[b]:starts[b] + L]),
+                           lc["slot_mapping"][starts[b]:starts[b] + L])
+            qc, qsc = omx.quantize_rows(omx.bf16_bits_to_f64(lc["q"][b:b + 1]))
+            ref = olog.paged_mqa_logits(qc.reshape(1, Hl, 64), qsc.reshape(1, Hl, 4),
+                                        lc["w"][b:b + 1], c, lc["block_table"][b:b + 1],
+                                        lc["context_lens"][b:b + 1], 1, L)
+            otk.top_k_per_row(ref.astype(np.float32), [0], [L], lc["topk"])
+            t_l += time.perf_counter() - t0
+            tok_l += L
+            del c
+        rate = tok_l / t_l
+        out["long_decode"] = {
+            "sample": f"sequences {picks} of the 64 x U[32K, 128K] batch ({tok_l} scored tokens): "
+                      f"insert of each sequence's own tokens, q quantize, paged logits, top-2048",
+            "sampled_s": round(t_l, 2), "scored_tokens_per_s": round(rate, 1),
+            "extrapolated_full_s": round(float(np.sum(lens)) / rate, 1), "extrapolated": True}
     if prefill_case is not None:
         rows = np.arange(0, prefill_case["T"], 16)
         out["prefill_chunk"] = prefill_leg(
