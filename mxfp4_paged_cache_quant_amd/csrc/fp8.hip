@@ -193,14 +193,25 @@ struct F8Tile {
   float scale;
 };
 
+// Scores of the 64 keys against the query's heads.  The next head group's four
+// MFMAs are issued before the current group's ReLU-weighted sums, so the matrix
+// core works while the vector ALU runs the epilogue; the sums keep the head
+// order, so the result is the same bits as one group at a time.
 template <int NH>
 __device__ __forceinline__ float f8_tile_score(const F8Tile& t, const F8Query<NH>& q) {
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v4f d[2][4];
 #pragma unroll
-  for (int grp = 0; grp < NH; ++grp)
+  for (int j = 0; j < 4; ++j) d[0][j] = mfma_fp8(q.a[0], t.v[j], zero);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] = relu_weighted(mfma_fp8(q.a[grp], t.v[j], zero), q.w[grp], acc[j]);
+  for (int grp = 0; grp < NH; ++grp) {
+    if (grp + 1 < NH)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[(grp + 1) & 1][j] = mfma_fp8(q.a[grp + 1], t.v[j], zero);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = relu_weighted(d[grp & 1][j], q.w[grp], acc[j]);
+  }
   return reduce_tiles(acc) * t.scale;
 }
 
