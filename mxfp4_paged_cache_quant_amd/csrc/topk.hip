@@ -161,6 +161,59 @@ __device__ void select_bin(Shared<BINS>& s, uint32_t need, int parity) {
   __syncthreads();
 }
 
+// select_bin with one barrier: after the wave totals are published, every
+// wave finds the wave whose share of the bins holds the crossing and scans
+// that share itself (two bins per lane at 1024 threads), so the selected bin,
+// the count above it and its own count reach every wave in scalar registers
+// without a second barrier.  The histogram is left as it is (a caller that
+// histograms again must clear it behind a barrier).  Same preconditions.
+template <int NT, int BINS>
+__device__ __forceinline__ void select_bin_wave(Shared<BINS>& s, uint32_t need, int parity,
+                                                uint32_t& bin, uint32_t& above, uint32_t& inbin) {
+  constexpr int per = BINS / NT;
+  constexpr int kWaves = NT / kWave;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int top = BINS - 1 - per * (int)threadIdx.x;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) sum += s.hist[top - j];
+  const uint32_t x = wave_incl_scan(sum);
+  uint32_t* wt = s.wave_tot[parity];
+  if (lane == 63) wt[wid] = x;
+  __syncthreads();
+  // running totals over the waves (lane i: waves 0..i), then the first wave
+  // whose running total reaches `need`
+  const uint32_t w = group_sum<16>(lane < kWaves ? wt[lane & 15] : 0u);
+  const uint64_t hit = __ballot(lane < kWaves && w >= need);
+  const int ws = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+  const uint32_t base = ws ? (uint32_t)__builtin_amdgcn_readlane((int)w, ws - 1) : 0u;
+  const int top2 = BINS - 1 - per * (ws * kWave + lane);
+  uint32_t c[per];
+  uint32_t sum2 = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    c[j] = s.hist[top2 - j];
+    sum2 += c[j];
+  }
+  uint32_t run = base + wave_incl_scan(sum2) - sum2;
+  const uint64_t hl = __ballot(run < need && run + sum2 >= need);
+  const int ls = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hl));
+  uint32_t b = 0, r = 0, n = 0;
+#pragma unroll
+  for (int j = 0; j < per; ++j) {
+    if (run < need && run + c[j] >= need) {
+      b = (uint32_t)(top2 - j);
+      r = run;
+      n = c[j];
+    }
+    run += c[j];
+  }
+  bin = (uint32_t)__builtin_amdgcn_readlane((int)b, ls);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)r, ls);
+  inbin = (uint32_t)__builtin_amdgcn_readlane((int)n, ls);
+}
+
 template <int NT, int BINS>
 __device__ __forceinline__ void clear_hist(Shared<BINS>& s) {
   for (int i = threadIdx.x; i < BINS; i += NT) s.hist[i] = 0;
@@ -638,19 +691,23 @@ __device__ __forceinline__ void topk_row(Shared<BINS>& s, uint32_t* __restrict__
         const int nsh = L > D ? L - D : 0;
         hist_first(s, key, nv, kmin, nsh, wfull);
         __syncthreads();
-        select_bin<NT>(s, (uint32_t)k, parity);
+        uint32_t bin, above, inbin;
+        select_bin_wave<NT>(s, (uint32_t)k, parity, bin, above, inbin);
         parity ^= 1;
-        const uint32_t need = (uint32_t)k - s.sel[1];
-        const uint32_t bin = s.sel[0];
+        const uint32_t need = (uint32_t)k - above;
         if (nsh == 0) {
           u_t = bin;
           need_ties = need;
-        } else if (s.sel[2] <= (uint32_t)kFewTopk) {
+        } else if (inbin <= (uint32_t)kFewTopk) {
           select_few<NT, kFewTopk, false>(s, key, key, nv, (uint32_t)(lo + (int64_t)E * threadIdx.x),
-                                          kmin, nsh, bin, need, (uint32_t)k - need, out, parity,
-                                          wfull);
+                                          kmin, nsh, bin, need, above, out, parity, wfull);
           return;
         } else {
+          // every wave has read its share of the histogram: clear it for the
+          // remaining digits
+          __syncthreads();
+          clear_hist<NT>(s);
+          __syncthreads();
           refine_regs<NT>(s, key, nv, kmin, nsh, bin, need, parity, u_t, need_ties, wfull);
         }
       }
