@@ -397,6 +397,97 @@ def bench_long_decode():
     }
 
 
+def gather_bytes(tokens):
+    """Algorithmic bytes of a gather: 68 B read and 68 B written per token, plus
+    the block-table entries (4 B per page)."""
+    return tokens * 136 + (tokens + 63) // 64 * 4
+
+
+def row_rooflines(case, alg_bytes, per_kernel, rope_kernel, prefill, long_decode, long_prefill,
+                  kpool, fp8):
+    """One roofline entry per hot-path row, on the workload that represents it:
+    algorithmic bytes (or FLOP) per launch from the path's per-unit figures, over
+    the bench's own average launch time."""
+    def hbm(workload, kernel, nbytes, us):
+        if us is None:
+            return None
+        gbs = nbytes / (us * 1e-6) / 1e9
+        return {"workload": workload, "kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "alg_bytes": int(nbytes), "us": round(us, 3)}
+
+    def mfma(workload, kernel, flop, us, peak):
+        tfs = flop / (us * 1e-6) / 1e12
+        return {"workload": workload, "kernel": kernel, "bound": "mfma", "achieved": round(tfs, 1),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(tfs / peak, 4), "flop": flop,
+                "us": round(us, 3)}
+
+    B, H = len(case["context_lens"]), case["H"]
+    scored = int(case["context_lens"].sum())
+    out = {"a7_topk_decode": hbm(case["name"], "topk", alg_bytes["topk"], per_kernel["topk"]),
+           "a6_logits_paged_decode_step": hbm(case["name"], "logits_paged_insert",
+                                              alg_bytes["logits_paged_insert"],
+                                              per_kernel["logits_paged_insert"])}
+    rope_us = rope_kernel.get("logits_paged_insert_rope")
+    # the fused step's bytes plus each row's table row of rope_dim/2 cosines and sines
+    out["next2_rope_decode_step"] = hbm(case["name"], "logits_paged_insert_rope",
+                                        alg_bytes["logits_paged_insert"] + B * ROPE_DIM * 4,
+                                        rope_us)
+    if prefill is not None:
+        T, Hp = prefill["T"], prefill["heads"]
+        out["a3_q_quantize"] = hbm(prefill["workload"], "quantize", T * Hp * (256 + 68),
+                                   prefill["kernels_us"]["quantize"])
+        out["a5_logits_prefill_chunk"] = mfma(prefill["workload"], "logits_prefill",
+                                              prefill["logits_flop"], prefill["logits_us"],
+                                              FP4_PEAK_TFLOPS)
+    if long_decode is not None:
+        lc = CASES["long_decode"]
+        N, Bl, H = long_decode["tokens"], len(lc["context_lens"]), lc["H"]
+        out["a1_a2_insert"] = hbm(long_decode["workload"], "insert", N * (256 + 8 + 68),
+                                  long_decode["insert_us"])
+        out["a6_logits_paged"] = hbm(long_decode["workload"], "logits_paged",
+                                     N * 72 + Bl * H * 72, long_decode["logits_paged_us"])
+        out["a7_topk_long_rows"] = hbm(long_decode["workload"], "topk_ws",
+                                       N * 4 + Bl * 2048 * 4, long_decode["topk_us"])
+        if long_decode["mtp2_logits_paged_us"] is not None:
+            # each page read once for both rows; two rows of logits and queries
+            out["next3_logits_paged_next_n2"] = hbm(long_decode["workload"], "logits_paged",
+                                                    N * 68 + (2 * N - Bl) * 4 + 2 * Bl * H * 72,
+                                                    long_decode["mtp2_logits_paged_us"])
+    if long_prefill is not None:
+        out["a5_logits_prefill"] = mfma(long_prefill["workload"], "logits_prefill",
+                                        long_prefill["logits_flop"], long_prefill["logits_us"],
+                                        FP4_PEAK_TFLOPS)
+        lp = CASES["long_prefill"]
+        out["a7_topk_prefill_rows"] = hbm(long_prefill["workload"], "topk",
+                                          long_prefill["causal_pairs"] * 4 + lp["T"] * lp["topk"] * 4,
+                                          long_prefill["topk_us"])
+        if long_prefill.get("gather_us") is not None:
+            out["a4_gather"] = hbm(long_prefill["workload"], "gather",
+                                   gather_bytes(CASES["long_prefill"]["S"]), long_prefill["gather_us"])
+    if kpool is not None:
+        kp = kpool["mxfp4"]
+        out["next4_kpool_insert"] = {"workload": kpool["workload"], "kernel": "kpool_insert",
+                                     "bound": "hbm", "achieved": kp["gbs"], "peak": HBM_PEAK_GBS,
+                                     "unit": "GB/s", "frac": kp["frac_hbm"],
+                                     "alg_bytes": kp["alg_bytes"], "us": kp["us"]}
+    if fp8 is not None:
+        fl = fp8["long_decode"]
+        out["next1_fp8_logits_paged"] = {"workload": "long_decode_64xU32K-128K (FP8 cache)",
+                                         "kernel": "logits_paged_fp8", "bound": "hbm",
+                                         "achieved": fl["logits_paged_gbs"], "peak": HBM_PEAK_GBS,
+                                         "unit": "GB/s", "frac": fl["logits_paged_frac_hbm"],
+                                         "us": fl["logits_paged_us"]}
+        fp_ = fp8["long_prefill"]
+        out["next1_fp8_logits_prefill"] = {"workload": "long_prefill_16384x122880 (FP8)",
+                                           "kernel": "logits_prefill_fp8", "bound": "mfma",
+                                           "achieved": fp_["logits_tflops"],
+                                           "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                           "frac": fp_["logits_frac_fp8_peak"],
+                                           "us": fp_["logits_us"]}
+    return out
+
+
 def bench_long_prefill():
     """16384 queries over 122880 cached tokens, 64 heads: logits and top-k."""
     import numpy as np
@@ -416,12 +507,16 @@ def bench_long_prefill():
     idx = torch.empty((T, case["topk"]), dtype=torch.int32, device="cuda")
     lg = lambda: mx.logits_prefill(qv, qs, kv, ksc, w, ks, ke, logits=logits, clean=False)  # noqa: E731
     tk = lambda: mx.topk(logits, ks, ke, case["topk"], out=idx)  # noqa: E731
+    bt, sl, cu = dev(case["block_table"]), dev(case["seq_lens"]), dev(case["cu_seq_offsets"])
+    ga = lambda: mx.gather(cache, bt, sl, cu, S, S, k_values=kv, k_scales=ksc)  # noqa: E731
     lg()
     tk()
+    ga()
     torch.cuda.synchronize()
     spread = {}
     t_lg = time_fn(lg, 3, 2, spread, "logits_prefill")
     t_tk = time_fn(tk, 3, 2, spread, "topk")
+    t_ga = None if EAGER else time_fn(ga, 10, 4)
     pairs = int(np.sum(case["ke"].astype(np.int64) - case["ks"]))
     flops = 2.0 * H * 128 * pairs
     tflops = flops / (t_lg * 1e-6) / 1e12
@@ -430,6 +525,8 @@ def bench_long_prefill():
         "logits_us": round(t_lg, 1), "logits_tflops": round(tflops, 1),
         "logits_frac_fp4_peak": round(tflops / FP4_PEAK_TFLOPS, 4),
         "topk_us": round(t_tk, 1), "topk_gbs": round((pairs * 4 + T * case["topk"] * 4) / t_tk / 1e3, 1),
+        "gather_us": None if t_ga is None else round(t_ga, 2),
+        "gather_gbs": None if t_ga is None else round(gather_bytes(S) / t_ga / 1e3, 1),
         "p10_p90_us": spread,
     }
 
@@ -1026,6 +1123,8 @@ def main():
                    "step": "logits_paged_insert(16 new tokens' K, 512 q rows, paged logits; one launch)+topk",
                    "rotating_sets": args.sets, "hip_graph": True, "parallelism": "none"},
         "roofline": roofline,
+        "rooflines": row_rooflines(case, alg_bytes, per_kernel, rope_kernel, prefill, long_decode,
+                                   long_prefill, kpool, fp8),
         "kernels": kernels,
         "decode_separate_calls": separate,
         "decode_with_rope": with_rope,
