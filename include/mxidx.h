@@ -215,7 +215,9 @@ int idx_insert_quantize_rope(const void* k, int k_dtype, int64_t num_tokens,
 
 /* idx_gather -- paged cache -> contiguous MXFP4 K (the cp_gather that P1's
  * live-validation comment names as sharing the cache layout).
- *   block_table:    [batch, bt_row_stride] int32 page ids.
+ *   block_table:    [batch, bt_row_stride] int32 page ids, bt_row_stride >=
+ *                   ceil(max_seq_len / page_size); the first that many entries of
+ *                   each row are read (those past a sequence's pages are unused).
  *   seq_lens:       [batch] int32; token j < seq_lens[b] of sequence b is read
  *                   from page block_table[b, j / page_size], offset j % page_size.
  *   cu_seq_offsets: [batch] int64; that token lands in output row

@@ -25,11 +25,22 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
   const int64_t lp = blockIdx.x;               // logical page of sequence b
   const int64_t j = lp * kPage + (threadIdx.x >> 2);
   const int part = threadIdx.x & 3;
-  if (j >= (int64_t)seq_lens[b]) return;
-  const int64_t page = block_table[(int64_t)b * bt_row_stride + lp];
-  if (page < 0 || page >= num_pages) return;
-  const int64_t row = cu_seq_offsets[b] + j;
-  if (row < 0 || row >= total_tokens) return;
+  // the three index loads in one round trip, as vector loads (scalar loads
+  // return out of order, so each test would wait for every load before it);
+  // the table entry exists for every launched page: the row stride covers
+  // max_seq_len's pages
+  const int32_t len = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(seq_lens + b, 4), 0, 0, 0);
+  const int32_t page32 = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
+      buffer_rsrc(block_table + (int64_t)b * bt_row_stride + lp, 4), 0, 0, 0);
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(cu_seq_offsets + b, 8);
+  const uint32_t f_lo = __builtin_amdgcn_raw_buffer_load_b32(ro, 0, 0, 0);
+  const uint32_t f_hi = __builtin_amdgcn_raw_buffer_load_b32(ro, 4, 0, 0);
+  const int64_t page = __builtin_amdgcn_readfirstlane(page32);
+  const int64_t row = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)f_hi) << 32) |
+                                (uint32_t)__builtin_amdgcn_readfirstlane((int)f_lo)) + j;
+  if (j >= __builtin_amdgcn_readfirstlane(len) || page < 0 || page >= num_pages || row < 0 ||
+      row >= total_tokens)
+    return;
   const int off = (int)(j % kPage);
   const uint8_t* pbase = cache + page * kPageBytes;
   const uint4 c = *reinterpret_cast<const uint4*>(pbase + off * kCodeBytes + part * 16);
