@@ -256,3 +256,87 @@ def test_fp8_prefill_chunk_8192_sampled_rows():
     check_topk_sets(g, case["ks"][rows], case["ke"][rows], case["topk"], sub, "fp8 chunk")
     check_topk_end_to_end(ref, bound, case["ks"][rows], case["ke"][rows], case["topk"], sub,
                           "fp8 chunk", abs_factor=F8)
+
+
+def test_fp8_long_context_decode_sampled():
+    """The long-context batch (64 x U[32K, 128K], lognormal K block scales) on the
+    FP8 cache in the launch configuration the bench times (clean = 0, the split
+    top-k): the cached bytes of 4096 sampled tokens against the oracle's encoding,
+    the logits of the longest sequence and one more against the oracle (over the
+    GPU's cache bytes), columns past each context untouched, and the top-k sets
+    of those rows exact and by the margin rule."""
+    case = workloads.long_decode()
+    B, W = len(case["context_lens"]), case["width"]
+    cache = torch.zeros((case["num_pages"], 64 * 132), dtype=torch.uint8, device="cuda")
+    mx.insert_fp8(dev(case["k"]), dev(case["slot_mapping"]), cache)
+    qv, wf, qc, wref = _fp8_query(case)
+    logits = torch.full((B, W), float("nan"), dtype=torch.float32, device="cuda")
+    mx.logits_paged_fp8(qv, wf, cache, dev(case["block_table"]), dev(case["context_lens"]), 1, W,
+                        logits=logits, clean=False)
+    ke = case["context_lens"].astype(np.int32)
+    idx = mx.topk_ws(logits, None, dev(ke), case["topk"], mx.topk_workspace(B, W))
+    torch.cuda.synchronize()
+    cache_np = host(cache)
+    flat = cache_np.reshape(-1)
+    toks = np.random.default_rng(321).choice(len(case["slot_mapping"]), 4096, replace=False)
+    codes, scales = of8.quantize_rows(exact({"k": case["k"][toks], "dtype": case["dtype"]}, "k"))
+    sbytes = scales.astype("<f4").view(np.uint8).reshape(-1, 4)
+    for i, sl in enumerate(case["slot_mapping"][toks]):
+        page, off = divmod(int(sl), 64)
+        v0, s0 = of8.value_offset(page, off), of8.scale_offset(page, off)
+        assert np.array_equal(flat[v0:v0 + 128], codes[i]), f"token {toks[i]} values"
+        assert np.array_equal(flat[s0:s0 + 4], sbytes[i]), f"token {toks[i]} scale"
+    seqs = [int(np.argmax(case["context_lens"])), 5]
+    ref, bound = of8.paged_mqa_logits(qc, wref, cache_np, case["block_table"],
+                                      case["context_lens"], 1, W, seqs=seqs, with_bound=True)
+    g = host(logits)
+    for b in seqs:
+        L = int(case["context_lens"][b])
+        assert np.all(np.isnan(g[b, L:])), f"sequence {b}: columns past the context written"
+    check_logits(np.where(np.isnan(g[seqs]), -np.inf, g[seqs]), ref[seqs], bound[seqs],
+                 "fp8 long-context decode", abs_factor=F8)
+    out = host(idx)[seqs]
+    zeros = np.zeros(len(seqs), np.int32)
+    check_topk_sets(g[seqs], zeros, ke[seqs], case["topk"], out, "fp8 long-context")
+    check_topk_end_to_end(ref[seqs], bound[seqs], zeros, ke[seqs], case["topk"], out,
+                          "fp8 long-context", abs_factor=F8)
+
+
+def test_fp8_long_prefill_sampled_rows():
+    """The long prefill (16,384 queries over 122,880 cached tokens, 64 heads,
+    Student-t inputs) on the FP8 cache in the bench's launch configuration
+    (clean = 0): gathered K bytes against the oracle's encoding, the folded
+    weights of 34 sampled rows, their logits within [ks, ke) and their top-k."""
+    case = workloads.long_prefill()
+    T, S, H = case["T"], case["S"], case["H"]
+    cache = torch.zeros((case["num_pages"], 64 * 132), dtype=torch.uint8, device="cuda")
+    mx.insert_fp8(dev(case["k"]), dev(case["slot_mapping"]), cache)
+    kv, ksc = mx.gather_fp8(cache, dev(case["block_table"]), dev(case["seq_lens"]),
+                            dev(case["cu_seq_offsets"]), S, S)
+    del cache
+    qv, _, wf = mx.quantize_fp8(dev(case["q"]), weights=dev(case["w"]))
+    logits = torch.empty((T, S), dtype=torch.float32, device="cuda")
+    mx.logits_prefill_fp8(qv, wf, kv, ksc, dev(case["ks"]), dev(case["ke"]), logits=logits,
+                          clean=False)
+    idx = mx.topk(logits, dev(case["ks"]), dev(case["ke"]), case["topk"])
+    torch.cuda.synchronize()
+    kc, kscale = of8.quantize_rows(exact(case, "k"))
+    assert np.array_equal(host(kv), kc) and np.array_equal(host(ksc).view(np.uint32),
+                                                           kscale.view(np.uint32))
+    rows = np.unique(np.concatenate([case["sample_rows"][::8], [0, T - 1]]))
+    qc, qsc = of8.quantize_rows(exact({"q": case["q"][rows], "dtype": case["dtype"]}, "q"))
+    wref = of8.fold_weights(case["w"][rows].reshape(-1), qsc).reshape(-1, H)
+    rt = torch.as_tensor(rows, device="cuda")
+    assert np.array_equal(host(qv[rt]).reshape(-1, 128), qc)
+    assert np.array_equal(host(wf[rt]).view(np.uint32), wref.view(np.uint32))
+    ref, bound = of8.mqa_logits(qc.reshape(-1, H, 128), wref, kc, kscale, case["ks"][rows],
+                                case["ke"][rows], chunk=4, with_bound=True)
+    g = host(logits[rt])
+    ks_r, ke_r = case["ks"][rows], case["ke"][rows]
+    cols = np.arange(S)[None, :]
+    inside = (cols >= ks_r[:, None]) & (cols < ke_r[:, None])
+    check_logits(np.where(inside, g, -np.inf), ref, bound, "fp8 long prefill", abs_factor=F8)
+    sub = host(idx)[rows]
+    check_topk_sets(np.where(inside, g, -np.inf), ks_r, ke_r, case["topk"], sub, "fp8 long prefill")
+    check_topk_end_to_end(ref, bound, ks_r, ke_r, case["topk"], sub, "fp8 long prefill",
+                          abs_factor=F8)
