@@ -80,6 +80,19 @@ def test_long_context_decode_64_seqs():
                        check_bytes_tokens=toks, split_topk=True)
 
 
+def test_long_context_decode_next_n2():
+    """Two query rows per sequence (multi-token decode) on the long-context batch
+    -- the same lengths, pages and K as above, rows seeing L - 1 and L tokens --
+    through the kernel the bench times for next_n = 2."""
+    case = workloads.decode_case(2, batch=64, len_range=(32768, 131072), H=32, next_n=2,
+                                 k_dist="lognormal", topk=2048, spare_pages=64, width=131072,
+                                 name="long_decode_64xU32K-128K_next_n2")
+    rng = np.random.default_rng(124)
+    toks = rng.choice(len(case["slot_mapping"]), 1024, replace=False)
+    _decode_case_check(case, sample_seqs=[int(np.argmax(case["context_lens"])), 11],
+                       check_bytes_tokens=toks, split_topk=True)
+
+
 def _prefill_case_check(case, sample_rows):
     cache = new_cache(case["num_pages"], fill=0)
     mx.insert(dev(case["k"]), dev(case["slot_mapping"]), cache)
