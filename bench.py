@@ -534,8 +534,9 @@ def bench_long_prefill():
 def bench_fp8(decode_case):
     """The FP8 (E4M3, 132 B/token) indexer cache that MXFP4 replaces, on the same
     workloads: the decode step (16 x 8192: new tokens' insert, q quantize with the
-    weight fold, paged logits, top-k) over rotating caches, the long-context paged
-    logits and top-k, and the prefill-chunk and long-prefill logits."""
+    weight fold, paged logits, top-k; as four calls and with the encodes and the
+    logits in one launch) over rotating caches, the long-context paged logits and
+    top-k, and the prefill-chunk and long-prefill logits."""
     import numpy as np
     import torch
     import mxfp4_paged_cache_quant_amd as mx
@@ -577,11 +578,29 @@ def bench_fp8(decode_case):
         g = capture([(lambda c=c, f=f: f(c)) for c in caches])
         per[name] = round(time_graph(g, 10) / n_sets * 1e3, 3)
         del g
+    # the same step with the two encodes and the logits in one launch
+    ops1 = {
+        "logits_paged_insert_fp8": lambda c: mx.logits_paged_insert_fp8(
+            q, k_new, w, c, bt, ctx, 1, W, logits=logits, clean=False),
+        "topk": ops["topk"],
+    }
+    for fn in ops1.values():
+        fn(caches[0])
+    torch.cuda.synchronize()
+    g_step = capture([(lambda c=c, f=f: f(c)) for c in caches for f in ops1.values()])
+    step1_us = time_graph(g_step, 5) / n_sets * 1e3
+    del g_step
+    g = capture([(lambda c=c: ops1["logits_paged_insert_fp8"](c)) for c in caches])
+    fused_us = round(time_graph(g, 10) / n_sets * 1e3, 3)
+    del g
     scored = int(np.sum(case["context_lens"]))
     out["decode_16x8192"] = {
         "step_us": round(step_us, 3), "kernels_us": per,
         "scored_tokens_per_s": round(scored / (step_us * 1e-6), 1),
         "logits_paged_gbs": round((scored * 136 + B * H * 132) / per["logits_paged_fp8"] / 1e3, 1),
+        "one_launch": {"step": "logits_paged_insert_fp8+topk", "step_us": round(step1_us, 3),
+                       "kernels_us": {"logits_paged_insert_fp8": fused_us, "topk": per["topk"]},
+                       "scored_tokens_per_s": round(scored / (step1_us * 1e-6), 1)},
     }
     del caches
     torch.cuda.empty_cache()

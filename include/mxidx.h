@@ -391,6 +391,33 @@ int idx_logits_paged_fp8(const uint8_t* q_values, const float* weights, const ui
                          int H, int64_t max_context_len, float* logits, int64_t logits_row_stride,
                          int clean, hipStream_t stream);
 
+/* idx_logits_paged_insert_fp8 -- the FP8 decode step's two encodes and its paged
+ * logits in one launch: equal, byte for byte and bit for bit, to idx_insert_fp8
+ * of the new tokens into their block-table slots, idx_quantize_fp8 of q with the
+ * weights folded (P3 "forward_cuda": FP8 q is a single tensor, its per-token
+ * scale folded into the weights), then idx_logits_paged_fp8 with those rows and
+ * w'.  For decode steps bound by launch count.
+ *   q:         [B*next_n, H, 128] bf16 (IDX_BF16) or fp32 (IDX_F32), contiguous,
+ *              16-byte aligned: the query rows, encoded in the kernel.
+ *   k_new:     [B*next_n, 128] in the same dtype, contiguous, 16-byte aligned:
+ *              row b*next_n + i is the K row of sequence b's token at position
+ *              context_lens[b] - next_n + i, written to page
+ *              block_table[b, pos / 64], offset pos % 64 (positions < 0, pages
+ *              whose table entry is outside [0, num_pages) and pages past
+ *              max_context_len are not written).
+ *   weights:   [B*next_n, H] fp32, not folded (the kernel folds them).
+ *   scale_fmt: IDX_FP8_SCALE_F32 or IDX_FP8_SCALE_POW2, for q and the new K rows.
+ *   cache:     the FP8 cache, updated in place (the new tokens' 132 bytes) and read.
+ *   All other arguments, the logits and the error behaviour are those of
+ *   idx_logits_paged_fp8; the new tokens' pages must not appear in another
+ *   sequence's block table. */
+int idx_logits_paged_insert_fp8(const void* q, const void* k_new, int dtype, const float* weights,
+                                int scale_fmt, uint8_t* cache, int64_t num_pages, int page_size,
+                                const int32_t* block_table, int64_t bt_row_stride,
+                                const int32_t* context_lens, int B, int next_n, int H,
+                                int64_t max_context_len, float* logits,
+                                int64_t logits_row_stride, int clean, hipStream_t stream);
+
 /* idx_kpool_insert -- the pooled indexer-K insert of P3
  * "vllm.models.glm5next.nvidia.sparse_indexer", section "_kpool_compress_insert":
  * kpool consecutive tokens pooled into one K row, quantized and written at a

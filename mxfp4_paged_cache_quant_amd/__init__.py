@@ -20,6 +20,7 @@ __all__ = [
     "quantize_rope", "insert_quantize_rope", "logits_paged_insert_rope", "ROPE_NEOX",
     "ROPE_INTERLEAVED", "kpool_insert",
     "quantize_fp8", "insert_fp8", "gather_fp8", "logits_prefill_fp8", "logits_paged_fp8",
+    "logits_paged_insert_fp8",
     "FP8_ROW_BYTES", "FP8_SCALE_F32", "FP8_SCALE_POW2",
     "HEAD_DIM", "ROW_BYTES", "PAGE_SIZE", "TOPK_MAX", "EXPORTS",
 ]
@@ -92,6 +93,9 @@ EXPORTS = {
     "idx_logits_paged_fp8": (_int, [_c_void_p, _c_void_p, _c_void_p, _i64, _int, _c_void_p, _i64,
                                     _c_void_p, _int, _int, _int, _i64, _c_void_p, _i64, _int,
                                     _c_void_p]),
+    "idx_logits_paged_insert_fp8": (_int, [_c_void_p, _c_void_p, _int, _c_void_p, _int, _c_void_p,
+                                           _i64, _int, _c_void_p, _i64, _c_void_p, _int, _int, _int,
+                                           _i64, _c_void_p, _i64, _int, _c_void_p]),
     "idx_kpool_insert": (_int, [_c_void_p, _int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p, _int,
                                 _int, _int, _c_void_p, _i64, _int, _c_void_p, _c_void_p]),
     "idx_topk": (_int, [_c_void_p, _i64, _i64, _c_void_p, _c_void_p, _int, _c_void_p, _c_void_p]),
@@ -754,6 +758,28 @@ def logits_paged_fp8(q_values, weights, cache, block_table, context_lens, next_n
                                       _ptr(context_lens), B, next_n, H, int(max_context_len),
                                       _ptr(logits), logits.stride(0), 1 if clean else 0,
                                       _stream(stream)), "idx_logits_paged_fp8")
+    return logits
+
+
+def logits_paged_insert_fp8(q, k_new, weights, cache, block_table, context_lens, next_n,
+                            max_context_len, round_scale=False, logits=None, clean=True,
+                            stream=None):
+    """The FP8 decode step in one launch: the new tokens' K (k_new [B*next_n, 128])
+    into their block-table slots of the FP8 cache, q [B*next_n, H, 128] encoded to
+    E4M3 with its scales folded into the weights (weights [B*next_n, H], not
+    folded), and the decode logits (as insert_fp8 + quantize_fp8 + logits_paged_fp8)."""
+    code, R, H, B, logits, _ = _paged_insert_args(
+        q, k_new, weights, cache, block_table, context_lens, next_n, max_context_len, logits,
+        clean)
+    num_pages = _fp8_cache_pages(cache)
+    fmt = FP8_SCALE_POW2 if round_scale else FP8_SCALE_F32
+    _check(lib().idx_logits_paged_insert_fp8(_ptr(q), _ptr(k_new), code, _ptr(weights), fmt,
+                                             _ptr(cache), num_pages, PAGE_SIZE,
+                                             _ptr(block_table), block_table.stride(0),
+                                             _ptr(context_lens), B, next_n, H,
+                                             int(max_context_len), _ptr(logits),
+                                             logits.stride(0), 1 if clean else 0,
+                                             _stream(stream)), "idx_logits_paged_insert_fp8")
     return logits
 
 

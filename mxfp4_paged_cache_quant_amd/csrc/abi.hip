@@ -62,7 +62,7 @@ int check_rows_input(const void* x, int dtype, int64_t rows, int64_t row_stride)
 
 extern "C" {
 
-int idx_version(void) { return 106; }
+int idx_version(void) { return 107; }
 
 int idx_arch_supported(const char* gcn_arch_name) {
   // "gfx950" alone or followed by target features ("gfx950:sramecc+:xnack-")
@@ -483,6 +483,35 @@ int idx_logits_paged_fp8(const uint8_t* q_values, const float* weights, const ui
                                                  bt_row_stride, context_lens, B, next_n, H,
                                                  max_context_len, logits, logits_row_stride, clean,
                                                  stream));
+}
+
+int idx_logits_paged_insert_fp8(const void* q, const void* k_new, int dtype, const float* weights,
+                                int scale_fmt, uint8_t* cache, int64_t num_pages, int page_size,
+                                const int32_t* block_table, int64_t bt_row_stride,
+                                const int32_t* context_lens, int B, int next_n, int H,
+                                int64_t max_context_len, float* logits,
+                                int64_t logits_row_stride, int clean, hipStream_t stream) {
+  if (dtype != IDX_BF16 && dtype != IDX_F32) return IDX_ERR_ARG;
+  if (scale_fmt != IDX_FP8_SCALE_F32 && scale_fmt != IDX_FP8_SCALE_POW2) return IDX_ERR_ARG;
+  if (page_size != IDX_PAGE_SIZE || num_pages < 0 || B < 0 || B > IDX_MAX_DECODE_SEQS ||
+      next_n < 1 || next_n > 16 || !heads_ok(H) || max_context_len < 0 ||
+      max_context_len > 0x7fffffffLL - IDX_PAGE_SIZE)
+    return IDX_ERR_ARG;
+  if (B == 0 || max_context_len == 0) return IDX_OK;
+  const int64_t pages_per_seq = (max_context_len + IDX_PAGE_SIZE - 1) / IDX_PAGE_SIZE;
+  if (bt_row_stride < pages_per_seq || logits_row_stride < max_context_len || num_pages < 1 ||
+      (int64_t)B * pages_per_seq > 0x7fffffffLL)
+    return IDX_ERR_ARG;
+  if (!q || !aligned(q, 16) || !k_new || !aligned(k_new, 16) || !weights || !aligned(weights, 16) ||
+      !cache || !aligned(cache, 16) || !block_table || !context_lens || !logits ||
+      !aligned(logits, 4))
+    return IDX_ERR_ARG;
+  int st = gate_current();
+  if (st != IDX_OK) return st;
+  return launched(mxidx::launch_logits_paged_insert_fp8(
+      q, k_new, dtype == IDX_F32, weights, scale_fmt == IDX_FP8_SCALE_POW2, cache, num_pages,
+      block_table, bt_row_stride, context_lens, B, next_n, H, max_context_len, logits,
+      logits_row_stride, clean, stream));
 }
 
 int idx_kpool_insert(const void* k, int dtype, int64_t n, int64_t k_row_stride,

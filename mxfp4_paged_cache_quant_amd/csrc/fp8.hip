@@ -225,25 +225,152 @@ __device__ __forceinline__ float f8_tile_score(const F8Tile& t, const F8Query<NH
 }
 
 // ---------------------------------------------------------------------------
-// Paged decode: one wave per workgroup over kF8Pages consecutive pages of one
-// sequence (17 KB of cache in flight per wave), pages read through buffer
-// descriptors with a wave-uniform base (a missing page reads zeros, no access),
-// query rows one at a time.
-constexpr int kF8Pages = 2;
+// Query sources of the paged kernel.  F8Packed: rows encoded beforehand (E4M3
+// values and the folded weights).
+struct F8Packed {
+  const uint8_t* q_values;
+  const float* weights;
+  static constexpr bool kInsert = false;
+  static constexpr int kPages = 2;
+  template <int NH>
+  using Fetched = F8Query<NH>;
+  template <int NH>
+  __device__ __forceinline__ F8Query<NH> fetch(int64_t r, int g, int n) const {
+    return load_f8_query<NH>(q_values, weights, r, g, n);
+  }
+  template <int NH>
+  __device__ __forceinline__ F8Query<NH> finish(const F8Query<NH>& f) const {
+    return f;
+  }
+};
 
-template <int NH>
+// The 32 elements 32g..32g+31 of a 128-wide row: loaded as 16-byte words
+// (bf16 or fp32), then read as fp32 values.
+template <bool kF32>
+struct Raw32 {
+  uint4 v[kF32 ? 8 : 4];
+  __device__ __forceinline__ void load(const void* base, int64_t row, int g) {
+    const uint4* p = kF32 ? reinterpret_cast<const uint4*>(static_cast<const float*>(base) +
+                                                            row * kHeadDim + 32 * g)
+                          : reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) +
+                                                           row * kHeadDim + 32 * g);
+#pragma unroll
+    for (int i = 0; i < (kF32 ? 8 : 4); ++i) v[i] = p[i];
+  }
+  __device__ __forceinline__ void values(float (&o)[32]) const {
+#pragma unroll
+    for (int i = 0; i < (kF32 ? 8 : 4); ++i) {
+      const uint32_t u[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (kF32) {
+          o[4 * i + k] = __uint_as_float(u[k]);
+        } else {
+          o[8 * i + 2 * k] = __uint_as_float(u[k] << 16);
+          o[8 * i + 2 * k + 1] = __uint_as_float(u[k] & 0xffff0000u);
+        }
+      }
+    }
+  }
+};
+
+// E4M3 encode of the row whose 4 blocks the lanes g = 0..3 of one column n
+// hold (every lane of the wave takes part): the row encoder's rule -- the scale
+// from the amax over the row, each element x / s correctly rounded in fp32
+// (with power-of-two scales a multiply by the exact reciprocal, the same
+// value), the hardware conversion -- packed in element order.  Returns s.
+__device__ __forceinline__ float encode_block32(const float (&v)[32], bool pow2, uint4 (&out)[2]) {
+  uint32_t a = 0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) a = max(a, __float_as_uint(v[i]) & 0x7fffffffu);
+  a = max(a, (uint32_t)__shfl_xor((int)a, 16));
+  a = max(a, (uint32_t)__shfl_xor((int)a, 32));
+  const float s = fp8_row_scale(a, pow2);
+  float y[32];
+  if (pow2) {
+    const float r = 1.0f / s;                      // exact: s is a power of two
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = v[i] * r;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = v[i] / s;
+  }
+  uint32_t p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p[j] = pack_fp8x4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
+  out[0] = make_uint4(p[0], p[1], p[2], p[3]);
+  out[1] = make_uint4(p[4], p[5], p[6], p[7]);
+  return s;
+}
+
+// F8Raw: bf16 / fp32 query rows encoded in the wave -- lane (g, n) encodes
+// block g of head 16*grp + n, the 32 bytes it supplies to the MFMA -- with the
+// weights folded there (w' = w * s of the head's row, fetched from the lane
+// that holds that row), so the operands equal the separate encode's; the new
+// tokens' K rows come with it (kInsert).
+template <bool kF32>
+struct F8Raw {
+  const void* q;          // [rows, H, 128]
+  const void* k_new;      // [rows, 128]: row b*next_n + i is token L_b - next_n + i
+  const float* weights;   // [rows, H], not folded
+  int pow2;
+  static constexpr bool kInsert = true;
+  static constexpr bool kF32In = kF32;
+  static constexpr int kPages = 3;
+  template <int NH>
+  struct Fetched {
+    Raw32<kF32> blk[NH];
+    float4 w[NH];
+  };
+  template <int NH>
+  __device__ __forceinline__ Fetched<NH> fetch(int64_t r, int g, int n) const {
+    constexpr int H = 16 * NH;
+    Fetched<NH> f;
+#pragma unroll
+    for (int grp = 0; grp < NH; ++grp) {
+      f.blk[grp].load(q, r * H + 16 * grp + n, g);
+      f.w[grp] = *reinterpret_cast<const float4*>(weights + r * H + 16 * grp + 4 * g);
+    }
+    return f;
+  }
+  template <int NH>
+  __device__ __forceinline__ F8Query<NH> finish(const Fetched<NH>& f) const {
+    F8Query<NH> q8;
+    const int g = (int)(threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int grp = 0; grp < NH; ++grp) {
+      float v[32];
+      f.blk[grp].values(v);
+      const float s = encode_block32(v, pow2 != 0, q8.a[grp]);
+      const float s0 = __shfl(s, 4 * g), s1 = __shfl(s, 4 * g + 1);
+      const float s2 = __shfl(s, 4 * g + 2), s3 = __shfl(s, 4 * g + 3);
+      q8.w[grp] = make_float4(f.w[grp].x * s0, f.w[grp].y * s1, f.w[grp].z * s2, f.w[grp].w * s3);
+    }
+    return q8;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Paged decode: one wave per workgroup over PPW (the query source's kPages)
+// consecutive pages of one sequence (17 KB of cache in flight per wave at 2
+// pages), pages read through buffer descriptors with a wave-uniform base (a
+// missing page reads zeros, no access), query rows one at a time.  With a raw
+// query source the wave that holds a new token's page first encodes that token
+// and writes it to its slot.
+
+template <int NH, int PPW, typename QS>
 __global__ __launch_bounds__(kWave) void logits_paged_fp8_kernel(
-    const uint8_t* __restrict__ q_values, const float* __restrict__ weights,
-    const uint8_t* __restrict__ cache, int64_t num_pages, const int32_t* __restrict__ block_table,
+    QS qs, const uint8_t* cache, int64_t num_pages,   // written when inserting: no restrict
+    const int32_t* __restrict__ block_table,
     int64_t bt_row_stride, const int32_t* __restrict__ context_lens, int next_n, int64_t width,
     float* __restrict__ logits, int64_t ld, int clean, int stream_out) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
   const int g = lane >> 4, n = lane & 15;
-  const int64_t lp0 = (int64_t)blockIdx.x * kF8Pages;
+  const int64_t lp0 = (int64_t)blockIdx.x * PPW;
   const int64_t wpages = (width + kPage - 1) / kPage;
   const int64_t row0 = (int64_t)b * next_n;
-  const int bt_count = (int)min((int64_t)kF8Pages, wpages - lp0);
+  const int bt_count = (int)min((int64_t)PPW, wpages - lp0);
   const int bt_lane = (int)__builtin_amdgcn_raw_buffer_load_b32(
       buffer_rsrc(block_table + (int64_t)b * bt_row_stride + lp0, 4 * bt_count), 4u * lane, 0, 0);
   const int64_t ctx = (int32_t)__builtin_amdgcn_readfirstlane(
@@ -267,16 +394,60 @@ __global__ __launch_bounds__(kWave) void logits_paged_fp8_kernel(
     if (clean)
       for (int i = 0; i < next_n; ++i)
 #pragma unroll
-        for (int p = 0; p < kF8Pages; ++p) store(row0 + i, (lp0 + p) * kPage, 0, 0.f);
+        for (int p = 0; p < PPW; ++p) store(row0 + i, (lp0 + p) * kPage, 0, 0.f);
     return;
   }
-  const int np = (int)min((int64_t)kF8Pages, (L - lp0 * kPage + kPage - 1) / kPage);
+  const int np = (int)min((int64_t)PPW, (L - lp0 * kPage + kPage - 1) / kPage);
+  // a raw source's row 0 fetched ahead of the insert and the page loads (and
+  // pinned there): its latency runs under the pages', and it is encoded while
+  // the pages are still in flight (encoded rows keep the compiler's order)
+  typename QS::template Fetched<NH> qf0;
+  if constexpr (QS::kInsert) {
+    qf0 = qs.template fetch<NH>(row0, g, n);
+    asm volatile("" ::: "memory");
+  }
 
-  F8Tile pg[kF8Pages];
-  bool page_ok[kF8Pages];
+  if constexpr (QS::kInsert) {
+    // New token i sits at position P = context_len - next_n + i.  The wave whose
+    // live pages hold it encodes it and writes it to the cache before loading
+    // its pages: lane (g, n_t) later loads exactly the 32 value bytes it stores
+    // here and lane `off` the scale word it stores, so the page loads see the
+    // new token (program order of one lane, one address).  Pages past the row
+    // width belong to no wave: tokens there are not written.
+    for (int i = 0; i < next_n; ++i) {
+      const int64_t P = ctx - next_n + i;
+      const int64_t wp = P - lp0 * kPage;
+      if (P < 0 || wp < 0 || wp >= (int64_t)np * kPage) continue;   // uniform
+      const int p_t = (int)(wp / kPage), off = (int)(wp % kPage);
+      const int64_t dst = __builtin_amdgcn_readlane(bt_lane, p_t);
+      if (dst < 0 || dst >= num_pages) continue;   // invalid table entry: not written
+      Raw32<QS::kF32In> kr;
+      kr.load(qs.k_new, row0 + i, g);
+      float v[32];
+      kr.values(v);
+      uint4 code[2];
+      const float sc = encode_block32(v, qs.pow2 != 0, code);
+      const __amdgpu_buffer_rsrc_t rs =
+          buffer_rsrc(const_cast<uint8_t*>(cache) + dst * kF8PageBytes, kF8PageBytes);
+      const bool col = n == off % 16;
+      const uint32_t voff = (uint32_t)(off * kF8Row + 32 * g);
+      const u32x4 c0 = {code[0].x, code[0].y, code[0].z, code[0].w};
+      const u32x4 c1 = {code[1].x, code[1].y, code[1].z, code[1].w};
+      __builtin_amdgcn_raw_buffer_store_b128(c0, rs, col ? voff : kDropOffset, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(c1, rs, col ? voff + 16u : kDropOffset, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs,
+                                            lane == off ? (uint32_t)(kF8PageValues + 4 * off)
+                                                        : kDropOffset,
+                                            0, 0);
+    }
+    asm volatile("" ::: "memory");   // the page loads stay behind the stores
+  }
+
+  F8Tile pg[PPW];
+  bool page_ok[PPW];
   const uint32_t off_v = (uint32_t)(kF8Row * n + 32 * g);
 #pragma unroll
-  for (int p = 0; p < kF8Pages; ++p) {
+  for (int p = 0; p < PPW; ++p) {
     const int pid = __builtin_amdgcn_readlane(bt_lane, p);
     const bool valid = pid >= 0 && pid < num_pages;
     page_ok[p] = p >= np || valid;
@@ -309,9 +480,11 @@ __global__ __launch_bounds__(kWave) void logits_paged_fp8_kernel(
   for (int i = 0; i < next_n; ++i) {
     const int64_t r = row0 + i;
     const int64_t ke = L - next_n + i + 1;
-    const F8Query<NH> q = load_f8_query<NH>(q_values, weights, r, g, n);
+    const F8Query<NH> q = (QS::kInsert && i == 0)
+                              ? qs.template finish<NH>(qf0)
+                              : qs.template finish<NH>(qs.template fetch<NH>(r, g, n));
 #pragma unroll
-    for (int p = 0; p < kF8Pages; ++p)
+    for (int p = 0; p < PPW; ++p)
       if (page_ok[p]) store(r, (lp0 + p) * kPage, ke, f8_tile_score<NH>(pg[p], q));
   }
 }
@@ -424,17 +597,45 @@ __global__ __launch_bounds__(256) void logits_prefill_fp8_kernel(
   }
 }
 
-template <int NH>
-hipError_t launch_paged_fp8_nh(const uint8_t* qv, const float* w, const uint8_t* cache,
-                               int64_t num_pages, const int32_t* bt, int64_t bt_stride,
-                               const int32_t* ctx, int B, int next_n, int64_t width, float* logits,
-                               int64_t ld, int clean, hipStream_t stream) {
+template <int NH, typename QS>
+hipError_t launch_paged_fp8_nh(QS qs, const uint8_t* cache, int64_t num_pages, const int32_t* bt,
+                               int64_t bt_stride, const int32_t* ctx, int B, int next_n,
+                               int64_t width, float* logits, int64_t ld, int clean,
+                               hipStream_t stream) {
   const int64_t pages = (width + kPage - 1) / kPage;
   const int stream_out = (int64_t)B * next_n * width * 4 > (4 << 20) ? 1 : 0;
-  const dim3 grid((unsigned)((pages + kF8Pages - 1) / kF8Pages), (unsigned)B);
-  hipLaunchKernelGGL((logits_paged_fp8_kernel<NH>), grid, dim3(kWave), 0, stream, qv, w, cache,
-                     num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean, stream_out);
+  constexpr int P = QS::kPages;
+  const dim3 grid((unsigned)((pages + P - 1) / P), (unsigned)B);
+  hipLaunchKernelGGL((logits_paged_fp8_kernel<NH, P, QS>), grid, dim3(kWave), 0, stream,
+                     qs, cache, num_pages, bt, bt_stride, ctx, next_n, width, logits, ld, clean,
+                     stream_out);
   return hipGetLastError();
+}
+
+template <typename QS>
+hipError_t launch_paged_fp8_source(QS qs, const uint8_t* cache, int64_t num_pages,
+                                   const int32_t* block_table, int64_t bt_row_stride,
+                                   const int32_t* context_lens, int B, int next_n, int H,
+                                   int64_t max_context_len, float* logits, int64_t ld, int clean,
+                                   hipStream_t stream) {
+#define MXIDX_F8P(nh)                                                                          \
+  case nh:                                                                                     \
+    return launch_paged_fp8_nh<nh>(qs, cache, num_pages, block_table, bt_row_stride,           \
+                                   context_lens, B, next_n, max_context_len, logits, ld, clean, \
+                                   stream);
+  switch (H / 16) {
+    MXIDX_F8P(1)
+    MXIDX_F8P(2)
+    MXIDX_F8P(3)
+    MXIDX_F8P(4)
+    MXIDX_F8P(5)
+    MXIDX_F8P(6)
+    MXIDX_F8P(7)
+    MXIDX_F8P(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef MXIDX_F8P
 }
 
 template <int NH, int RW>
@@ -500,24 +701,25 @@ hipError_t launch_logits_paged_fp8(const uint8_t* q_values, const float* weights
                                    const int32_t* context_lens, int B, int next_n, int H,
                                    int64_t max_context_len, float* logits, int64_t ld, int clean,
                                    hipStream_t stream) {
-#define MXIDX_F8P(nh)                                                                          \
-  case nh:                                                                                     \
-    return launch_paged_fp8_nh<nh>(q_values, weights, cache, num_pages, block_table,           \
-                                   bt_row_stride, context_lens, B, next_n, max_context_len,    \
-                                   logits, ld, clean, stream);
-  switch (H / 16) {
-    MXIDX_F8P(1)
-    MXIDX_F8P(2)
-    MXIDX_F8P(3)
-    MXIDX_F8P(4)
-    MXIDX_F8P(5)
-    MXIDX_F8P(6)
-    MXIDX_F8P(7)
-    MXIDX_F8P(8)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef MXIDX_F8P
+  return launch_paged_fp8_source(F8Packed{q_values, weights}, cache, num_pages, block_table,
+                                 bt_row_stride, context_lens, B, next_n, H, max_context_len,
+                                 logits, ld, clean, stream);
+}
+
+hipError_t launch_logits_paged_insert_fp8(const void* q, const void* k_new, bool f32,
+                                          const float* weights, bool pow2, uint8_t* cache,
+                                          int64_t num_pages, const int32_t* block_table,
+                                          int64_t bt_row_stride, const int32_t* context_lens,
+                                          int B, int next_n, int H, int64_t max_context_len,
+                                          float* logits, int64_t ld, int clean,
+                                          hipStream_t stream) {
+  if (f32)
+    return launch_paged_fp8_source(F8Raw<true>{q, k_new, weights, pow2 ? 1 : 0}, cache,
+                                   num_pages, block_table, bt_row_stride, context_lens, B, next_n,
+                                   H, max_context_len, logits, ld, clean, stream);
+  return launch_paged_fp8_source(F8Raw<false>{q, k_new, weights, pow2 ? 1 : 0}, cache, num_pages,
+                                 block_table, bt_row_stride, context_lens, B, next_n, H,
+                                 max_context_len, logits, ld, clean, stream);
 }
 
 hipError_t launch_logits_prefill_fp8(const uint8_t* q_values, const float* weights,

@@ -102,6 +102,13 @@ hipError_t launch_logits_paged_fp8(const uint8_t* q_values, const float* weights
                                    const int32_t* context_lens, int B, int next_n, int H,
                                    int64_t max_context_len, float* logits, int64_t ld, int clean,
                                    hipStream_t stream);
+hipError_t launch_logits_paged_insert_fp8(const void* q, const void* k_new, bool f32,
+                                          const float* weights, bool pow2, uint8_t* cache,
+                                          int64_t num_pages, const int32_t* block_table,
+                                          int64_t bt_row_stride, const int32_t* context_lens,
+                                          int B, int next_n, int H, int64_t max_context_len,
+                                          float* logits, int64_t ld, int clean,
+                                          hipStream_t stream);
 hipError_t launch_logits_prefill_fp8(const uint8_t* q_values, const float* weights,
                                      const uint8_t* k_values, const float* k_scales,
                                      const int32_t* ks, const int32_t* ke, int64_t T, int H,

@@ -45,7 +45,7 @@ def test_header_declarations_are_exported(L):
 
 
 def test_version_and_strerror(L):
-    assert L.idx_version() == 106
+    assert L.idx_version() == 107
     for st in range(5):
         assert L.idx_strerror(st)
     assert L.idx_strerror(99) == b"unknown status"
@@ -146,6 +146,30 @@ def test_logits_paged_insert_argument_validation(L):
     assert call(max_len=0) == OK
 
 
+def test_logits_paged_insert_fp8_argument_validation(L):
+    # idx_logits_paged_insert_fp8(q, k_new, dtype, w, scale_fmt, cache, num_pages, page, bt,
+    #                             bt_stride, ctx, B, next_n, H, max_len, logits, ld, clean, stream)
+    def call(q=P, k=P, dtype=0, fmt=0, H=32, next_n=1, max_len=64, bt_stride=1, ld=64, page=64,
+             B=1):
+        return L.idx_logits_paged_insert_fp8(q, k, dtype, P, fmt, P, 4, page, P, bt_stride, P, B,
+                                             next_n, H, max_len, P, ld, 1, None)
+    for dtype in (-1, 2):
+        assert call(dtype=dtype) == ERR_ARG
+    for fmt in (-1, 2):
+        assert call(fmt=fmt) == ERR_ARG
+    for H in (0, 8, 24, 144):
+        assert call(H=H) == ERR_ARG
+    assert call(q=None) == ERR_ARG
+    assert call(k=MIS) == ERR_ARG
+    assert call(next_n=0) == ERR_ARG
+    assert call(next_n=17) == ERR_ARG
+    assert call(max_len=65, ld=65) == ERR_ARG     # block-table stride below the pages needed
+    assert call(ld=63) == ERR_ARG
+    assert call(page=48) == ERR_ARG
+    assert call(B=0) == OK
+    assert call(max_len=0) == OK
+
+
 def test_topk_argument_validation(L):
     for k in (0, -3, 2049):
         assert L.idx_topk(P, 4, 64, None, P, k, P, None) == ERR_ARG
@@ -187,6 +211,8 @@ def test_fails_closed_without_device(L):
     assert L.idx_logits_paged(P, P, P, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 64, 1, None) == ERR_NO_DEVICE
     assert L.idx_logits_paged_insert(P, P, 0, P, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 64, 1,
                                      None) == ERR_NO_DEVICE
+    assert L.idx_logits_paged_insert_fp8(P, P, 0, P, 1, P, 4, 64, P, 1, P, 1, 1, 32, 64, P, 64, 1,
+                                         None) == ERR_NO_DEVICE
 
 
 def test_python_wrapper_raises_on_error(L):
