@@ -55,6 +55,7 @@ constexpr int kWaveHistBins = 2048;
 // (quadratic, so the cutoff is per kernel): the row top-k uses 64, the merge
 // of rank lists -- whose first-level bins are larger -- uses 256.
 constexpr int kFewCand = 256;      // LDS capacity for the ranked keys
+constexpr int kTopkMaxOut = 2048;  // largest k (IDX_TOPK_MAX)
 constexpr int kFewTopk = 64;
 constexpr int kFewMerge = 256;
 
@@ -402,12 +403,25 @@ __device__ __forceinline__ void select_few(Shared<BINS>& s, const uint32_t (&key
   });
   uint32_t total;
   const uint32_t pos = block_scan<NT>(ca, s, parity, total);
+  // With 16 or more keys per thread the row's k outputs are staged in the
+  // histogram's words (no wave reads the histogram past the scan's barrier)
+  // and stored in one coalesced pass: the per-thread positions scatter over
+  // the row, a global store per key slot against an LDS write (prefill-chunk
+  // rows 76.0 -> 57.4 us).  With 8 keys per thread (decode rows) the stores go
+  // out directly: the staging's extra barrier costs more (5.57 -> 5.63 us).
+  constexpr bool kStage = E >= 16;
+  static_assert(!kStage || BINS >= kTopkMaxOut, "the staging area holds a whole output row");
+  uint32_t* stage = s.hist;
+  auto emit = [&](uint32_t o, uint32_t c) __attribute__((always_inline)) {
+    if constexpr (kStage) stage[o] = c;
+    else out[o] = (int32_t)c;
+  };
   per_fill(wfull, [&](auto full) __attribute__((always_inline)) {
     uint32_t p = pos;
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if ((full.value || e < nv) && ((key[e] - kmin) >> shift) > prefix)
-        out[p++] = (int32_t)(kCols ? cols[e] : col0 + (uint32_t)e);
+        emit(p++, kCols ? cols[e] : col0 + (uint32_t)e);
   });
   const uint32_t cnt = s.ccount;
   const uint32_t i = threadIdx.x / kPerCand;
@@ -437,8 +451,12 @@ __device__ __forceinline__ void select_few(Shared<BINS>& s, const uint32_t (&key
     }
   }
   before = group_sum<kPerCand>(before);          // a candidate's threads share a DPP row
-  if (i < cnt && threadIdx.x % kPerCand == kPerCand - 1 && before < need)
-    out[above + before] = (int32_t)ci;
+  if (i < cnt && threadIdx.x % kPerCand == kPerCand - 1 && before < need) emit(above + before, ci);
+  if constexpr (kStage) {
+    __syncthreads();
+    // above + need outputs: the keys above the bin and the bin's first `need`
+    for (uint32_t o = threadIdx.x; o < above + need; o += NT) out[o] = (int32_t)stage[o];
+  }
 }
 
 // Ordered output of register-held candidates (thread t holds consecutive
