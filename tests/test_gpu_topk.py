@@ -114,7 +114,9 @@ def test_topk_deterministic_across_runs():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("rows,n,k", [(600, 3000, 2048), (520, 20000, 2048), (512, 9000, 100)])
+@pytest.mark.parametrize("rows,n,k", [(600, 3000, 2048), (520, 20000, 2048), (512, 9000, 100),
+                                      # 16 keys per thread (outputs staged in LDS), odd k
+                                      (512, 6000, 1), (512, 6000, 7), (512, 6000, 2047)])
 def test_topk_many_rows(rows, n, k):
     # 512 or more rows select the many-rows launch shape (512-thread workgroups)
     rng = np.random.default_rng(rows + n)
