@@ -17,7 +17,9 @@
  *   idx_insert_quantize, idx_logits_paged_insert (and their _rope forms, with
  *                       the query RoPE): a decode step's calls in fewer launches
  *   idx_*_fp8           the FP8 (E4M3) indexer cache the MXFP4 one replaces:
- *                       quantize, insert, gather, dense and paged logits
+ *                       quantize, insert, gather, dense and paged logits,
+ *                       and idx_logits_paged_insert_fp8, its decode step's
+ *                       quantize + insert + paged logits in one launch
  *
  * Sources: P1 = "[Kernel] MXFP4 indexer cache for GLM-5.2 / DSA (glm_moe_dsa)"
  * (vLLM pull request 48558); P2 = "Enable SM86 MXFP4 sparse-indexer cache"
