@@ -523,11 +523,13 @@ __global__ __launch_bounds__(256) void logits_prefill_fp8_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
-  // XCD-aware order (workgroup i runs on XCD i % 8): one XCD's resident
-  // workgroups share a query block, causal work spreads over the XCDs, and
-  // query blocks run last to first (the longest causal rows first)
+  // Workgroup order as in the MXFP4 kernel: key-chunk-major for long inputs (the
+  // resident workgroups share a K chunk in L2), XCD-aware for short ones
   int64_t qb, kc;
-  if (n_qb % 8 == 0) {
+  if (key_chunk == kF8KeyChunk) {
+    kc = n_kc - 1 - (int64_t)blockIdx.x / n_qb;
+    qb = n_qb - 1 - (int64_t)blockIdx.x % n_qb;
+  } else if (n_qb % 8 == 0) {
     const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
     qb = n_qb - 1 - ((j / n_kc) * 8 + x);
     kc = j % n_kc;

@@ -87,8 +87,18 @@ __global__ __launch_bounds__(256) void logits_prefill_kernel(
   const int g = lane >> 4;
   const int n = lane & 15;
 
+  // Workgroup order.  Long inputs (4096-key chunks) go key chunk by key chunk, so
+  // the workgroups resident at one time share one chunk of K, which stays in L2,
+  // while their query blocks stream; the last chunks, which the causal diagonal
+  // leaves uneven, run first.  Short inputs are XCD-aware (workgroup i runs on
+  // XCD i % 8): one XCD's resident workgroups share a query block, causal work
+  // spreads over the XCDs, and query blocks run last to first (the longest
+  // causal rows first).
   int64_t qb, kc;
-  if (n_qb % 8 == 0) {
+  if (key_chunk == kKeyChunk) {
+    kc = n_kc - 1 - (int64_t)blockIdx.x / n_qb;
+    qb = n_qb - 1 - (int64_t)blockIdx.x % n_qb;
+  } else if (n_qb % 8 == 0) {
     const int64_t x = blockIdx.x % 8, j = blockIdx.x / 8;
     qb = n_qb - 1 - ((j / n_kc) * 8 + x);
     kc = j % n_kc;
