@@ -490,32 +490,23 @@ __global__ __launch_bounds__(kWave) void logits_paged_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Dense prefill: 4 waves x RW query rows per workgroup over a chunk of keys,
-// 64 keys per step with the next step's tile in flight, as the MXFP4 kernel
-// (logits_prefill.hip) does; K rows are 128 bytes and each key's scale is
-// applied to its logit after the head sum.
+// Dense prefill: 4 waves x RW query rows per workgroup over a chunk of keys, 64
+// keys per step, as the MXFP4 kernel (logits_prefill.hip) does; K rows are 128
+// bytes and each key's scale is applied to its logit after the head sum.  Unlike
+// the MXFP4 kernel, the K tiles go through LDS once per workgroup: a lane's 32
+// bytes of a key are two 16-byte loads at half a line's width, and with every wave
+// loading each tile itself the vector-memory path, not the matrix core, set the
+// pace (one row per wave instead of two nearly doubled the time).  Staged tiles
+// also free the registers of two tile buffers, so 3 waves fit per SIMD.
 constexpr int kF8KeyChunkSmallS = 512;
 constexpr int kF8KeyChunk = 4096;
 constexpr int64_t kF8SmallS = 16384;
 
-__device__ __forceinline__ void load_f8_tile(F8Tile& t, const uint8_t* __restrict__ kv,
-                                             const float* __restrict__ ksc, int c0, int S, int g,
-                                             int n, int lane) {
-  c0 = __builtin_amdgcn_readfirstlane(c0);
-  const int keys = __builtin_amdgcn_readfirstlane(max(min(S - c0, 64), 0));
-  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(kv + (int64_t)c0 * kF8Row, keys * kF8Row);
-  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(ksc + (int64_t)c0, keys * 4);
-  const uint32_t off = (uint32_t)(kF8Row * n + 32 * g);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    t.v[j][0] = ld16<0>(rv, off + 2048u * j);
-    t.v[j][1] = ld16<0>(rv, off + 2048u * j + 16u);
-  }
-  t.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, 4u * lane, 0, 0));
-}
+constexpr int kF8TileLds = 64 * 128 + 64 * 4;   // one 64-key tile: values, then scales
 
 template <int NH, int RW>
-__global__ __launch_bounds__(256) void logits_prefill_fp8_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+void logits_prefill_fp8_kernel(
     const uint8_t* __restrict__ q_values, const float* __restrict__ weights,
     const uint8_t* __restrict__ k_values, const float* __restrict__ k_scales,
     const int32_t* __restrict__ ks, const int32_t* __restrict__ ke, int64_t T, int S,
@@ -541,7 +532,6 @@ __global__ __launch_bounds__(256) void logits_prefill_fp8_kernel(
   const int c_begin = (int)kc * key_chunk;
   const int c_end = (int)min((int64_t)c_begin + key_chunk, (int64_t)S);
   int lo[RW], hi[RW];
-  int need_lo = c_end, need_hi = c_begin;
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     const int64_t t = t0 + i;
@@ -550,19 +540,28 @@ __global__ __launch_bounds__(256) void logits_prefill_fp8_kernel(
     if (t < T) {
       lo[i] = ks ? max(ks[t], 0) : 0;
       hi[i] = min(ke[t], S);
-      if (lo[i] < hi[i]) {
-        need_lo = min(need_lo, max(lo[i], c_begin));
-        need_hi = max(need_hi, min(hi[i], c_end));
-      }
     }
   }
+  // the window of the whole workgroup: its 4 waves share the K tiles
+  int need_lo = c_end, need_hi = c_begin;
+  for (int r = 0; r < 4 * RW; ++r) {
+    const int64_t t = qb * (4 * RW) + r;
+    if (t >= T) break;
+    const int l = ks ? max(ks[t], 0) : 0, h = min(ke[t], S);
+    if (l < h) {
+      need_lo = min(need_lo, max(l, c_begin));
+      need_hi = max(need_hi, min(h, c_end));
+    }
+  }
+  need_lo = __builtin_amdgcn_readfirstlane(need_lo);
+  need_hi = __builtin_amdgcn_readfirstlane(need_hi);
   float* lrow[RW];
 #pragma unroll
   for (int i = 0; i < RW; ++i) lrow[i] = logits + min(t0 + i, T - 1) * ld;
-  auto store = [&](int i, int c0, float v) {
-    c0 = __builtin_amdgcn_readfirstlane(c0);
+  auto store = [&](int i, int c0, float v, bool live = true) {
+    c0 = __builtin_amdgcn_readfirstlane(max(c0, 0));
     uint32_t off = 4u * lane;
-    if (t0 + i >= T) off = kDropOffset;
+    if (t0 + i >= T || !live) off = kDropOffset;
     if (!(c0 >= lo[i] && c0 + 64 <= hi[i])) {          // a tile that straddles [ks, ke)
       const int col = c0 + lane;
       const bool scored = col >= lo[i] && col < hi[i];
@@ -586,17 +585,84 @@ __global__ __launch_bounds__(256) void logits_prefill_fp8_kernel(
 #pragma unroll
   for (int i = 0; i < RW; ++i) q[i] = load_f8_query<NH>(q_values, weights, min(t0 + i, T - 1), g, n);
 
-  F8Tile kt0, kt1;
-  load_f8_tile(kt0, k_values, k_scales, k_first, S, g, n, lane);
+  // K tiles staged once per workgroup in LDS, two buffers.  A tile's 8 KB of
+  // values are 8 slices of 1 KB, slice 2j + h holding, for lane (g, n), bytes
+  // 32g + 16h .. +15 of key 16j + n (the 16 bytes that lane supplies as half h of
+  // MFMA tile j); wave w copies slices 2w and 2w + 1 with 16-byte buffer-to-LDS
+  // loads and every wave the 64 key scales (identical data).  Keys at or past S
+  // read as zeros.  A tile's results are stored one step later, and one barrier
+  // per step publishes the next tile and frees the current one.
+  __shared__ __attribute__((aligned(16))) uint8_t kb0[kF8TileLds];
+  __shared__ __attribute__((aligned(16))) uint8_t kb1[kF8TileLds];
+  const uint32_t src0 = (uint32_t)((16 * wave + n) * kF8Row + 32 * g);
+  auto dma = [&](uint8_t* kb, int c0) {
+    c0 = __builtin_amdgcn_readfirstlane(c0);
+    const int keys = __builtin_amdgcn_readfirstlane(max(min(S - c0, 64), 0));
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(k_values + (int64_t)c0 * kF8Row, keys * kF8Row);
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(k_scales + (int64_t)c0, keys * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, (__attribute__((address_space(3))) void*)(kb + 2048 * wave), 16, src0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rv, (__attribute__((address_space(3))) void*)(kb + 2048 * wave + 1024), 16, src0 + 16u, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(kb + 8192), 4, 4u * lane, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // the copy stays ahead of the step's stores
+  };
+  // Scores of the 64 keys of an LDS tile for the wave's rows, tile j outermost:
+  // acc[i][j] sums the head groups in order, so the bits equal f8_tile_score's.
+  auto score_lds = [&](const uint8_t* kb, float (&out)[RW]) {
+    constexpr int P = RW * NH;
+    const v4f zero = {0.f, 0.f, 0.f, 0.f};
+    float acc[RW][4];
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 v[2];
+      v[0] = *reinterpret_cast<const uint4*>(kb + 2048 * j + 16 * lane);
+      v[1] = *reinterpret_cast<const uint4*>(kb + 2048 * j + 1024 + 16 * lane);
+      v4f d[3];
+      d[0] = mfma_fp8(q[0].a[0], v, zero);
+      if (P > 1) d[1] = mfma_fp8(q[1 / NH].a[1 % NH], v, zero);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        if (p + 2 < P) d[(p + 2) % 3] = mfma_fp8(q[(p + 2) / NH].a[(p + 2) % NH], v, zero);
+        acc[p / NH][j] = relu_weighted(d[p % 3], q[p / NH].w[p % NH], acc[p / NH][j]);
+      }
+    }
+    const float sc = *reinterpret_cast<const float*>(kb + 8192 + 4 * lane);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) out[i] = reduce_tiles(acc[i]) * sc;
+  };
+  // vmcnt counts loads and stores in issue order: after a step only its RW
+  // stores may still be outstanding, so the wait covers the tile copy alone
+  constexpr int kWaitCopy = (RW & 15) | (0x7 << 4) | (0xF << 8);
+  float res[RW] = {};
+  int prev = -1;
+  auto step_from = [&](const uint8_t* kb, int c0) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) store(i, prev, res[i], prev >= 0);
+    score_lds(kb, res);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) asm volatile("" ::"v"(res[i]));   // done before the barrier
+    prev = c0;
+    __builtin_amdgcn_s_waitcnt(kWaitCopy);
+    asm volatile("s_barrier" ::: "memory");
+  };
+  dma(kb0, k_first);
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("s_barrier" ::: "memory");
   for (int c0 = k_first; c0 < need_hi; c0 += 128) {
-    load_f8_tile(kt1, k_values, k_scales, c0 + 64, S, g, n, lane);
-#pragma unroll
-    for (int i = 0; i < RW; ++i) store(i, c0, f8_tile_score<NH>(kt0, q[i]));
+    dma(kb1, c0 + 64);
+    step_from(kb0, c0);
     if (c0 + 64 >= need_hi) break;
-    load_f8_tile(kt0, k_values, k_scales, c0 + 128, S, g, n, lane);
-#pragma unroll
-    for (int i = 0; i < RW; ++i) store(i, c0 + 64, f8_tile_score<NH>(kt1, q[i]));
+    dma(kb0, c0 + 128);
+    step_from(kb1, c0 + 64);
   }
+#pragma unroll
+  for (int i = 0; i < RW; ++i) store(i, prev, res[i], true);
 }
 
 template <int NH, typename QS>
