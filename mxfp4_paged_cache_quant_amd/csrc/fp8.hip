@@ -291,6 +291,21 @@ __device__ __forceinline__ float encode_block32(const float (&v)[32], bool pow2,
     const float r = 1.0f / s;                      // exact: s is a power of two
 #pragma unroll
     for (int i = 0; i < 32; ++i) y[i] = v[i] * r;
+  } else if (s >= 0x1p-64f) {
+    // x / s correctly rounded without a division per element (Markstein's
+    // theorem: with y = 1/s rounded, q0 = x*y within an ulp and the remainder
+    // e = x - s*q0 exact under an FMA, fma(e, y, q0) is the rounded quotient when
+    // nothing underflows).  For s >= 2^-64 that holds wherever |x/s| >= 2^-11;
+    // smaller quotients round to an E4M3 zero either way, and x's sign bit is
+    // copied so that -0 stays -0.  The host check tests/c/fp8_quotient_check.c
+    // holds the route to the division bit for bit.
+    const float r = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float q0 = v[i] * r;
+      const float q = fmaf(fmaf(-s, q0, v[i]), r, q0);
+      y[i] = __uint_as_float((__float_as_uint(q) & 0x7fffffffu) | (__float_as_uint(v[i]) & 0x80000000u));
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 32; ++i) y[i] = v[i] / s;

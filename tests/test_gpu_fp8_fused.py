@@ -99,3 +99,55 @@ def test_fp8_paged_insert_16x8192_against_oracle():
     check_topk_sets(g, zeros, ke, case["topk"], out, "fp8 one-launch 16x8192")
     check_topk_end_to_end(ref[seqs], bound[seqs], zeros[seqs], ke[seqs], case["topk"], out[seqs],
                           "fp8 one-launch 16x8192", abs_factor=F8)
+
+
+def _extreme_rows(rng, n):
+    """fp32 rows whose scales and elements reach the ends of the in-wave encode:
+    scales on both sides of 2^-64 (reciprocal route / division), at the 2^-126
+    floor and near the fp32 maximum; signed zeros, subnormals, E4M3 rounding ties
+    and log-uniform magnitudes over the whole exponent range."""
+    rows = []
+    for amax in (448 * 2.0 ** -64, np.nextafter(np.float32(448 * 2.0 ** -64), np.float32(0)),
+                 np.float32(1e-39), 2.0 ** -120, 3.0e38, 448.0, 1.0):
+        r = (rng.uniform(-1, 1, 128) * amax).astype(np.float32)
+        r[rng.integers(0, 128)] = np.float32(amax)
+        rows.append(r)
+    # E4M3 ties (nearest-even decides) and tiny quotients at a power-of-two scale
+    s = 2.0 ** -3
+    t = np.array([2.0 ** -10, 3 * 2.0 ** -10, 2.0 ** -11, 2.0 ** -12, 1.0625, 1.1875, 17.0,
+                  232.0, 0.0, 2.0 ** -9, 5 * 2.0 ** -10, 448.0], np.float64)
+    r = np.zeros(128, np.float32)
+    r[:len(t)] = t * s
+    r[len(t):2 * len(t)] = -t * s
+    r[2 * len(t)] = np.float32(-0.0)
+    r[2 * len(t) + 1:2 * len(t) + 5] = np.array([1e-45, -1e-45, 1e-40, -3e-39], np.float32)
+    rows.append(r)
+    while len(rows) < n:
+        mag = np.exp2(rng.uniform(-149, 127, 128))
+        sign = np.where(rng.random(128) < 0.5, -1.0, 1.0)
+        r = (sign * mag).astype(np.float32)
+        r[rng.random(128) < 0.05] = np.float32(-0.0)
+        rows.append(r)
+    out = np.stack(rows[:n])
+    assert np.all(np.isfinite(out))
+    return out
+
+
+@pytest.mark.parametrize("round_scale", [False, True])
+def test_fp8_paged_insert_extreme_rows(round_scale):
+    """New K rows and query rows at the ends of the encode's range: the one-launch
+    step equals the separate calls (cache bytes, logit bits) and its cache equals
+    the oracle's for every token."""
+    rng = np.random.default_rng(4242 + round_scale)
+    lens = [5, 70, 129, 64, 3, 200, 31, 2]
+    case = workloads.decode_case(77, seq_lens=lens, H=32, next_n=2, dtype="f32", width=260)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    new = np.concatenate([starts[b] + lens[b] - 2 + np.arange(2) for b in range(len(lens))])
+    case["k"][new] = _extreme_rows(rng, len(new))
+    R, H = case["q"].shape[:2]
+    case["q"] = _extreme_rows(rng, R * H).reshape(R, H, 128)
+    cache, _ = _step_pair(case, round_scale=round_scale, clean=True)
+    ref_cache = of8.write_rows(np.full((case["num_pages"], 64 * 132), CANARY, np.uint8),
+                               *of8.quantize_rows(exact(case, "k"), round_scale=round_scale),
+                               case["slot_mapping"])
+    assert np.array_equal(host(cache), ref_cache)
