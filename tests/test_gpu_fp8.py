@@ -160,7 +160,9 @@ def test_fp8_paged_logits(H, next_n, lens, clean):
 
 
 @pytest.mark.parametrize("H,T,S,clean", [(32, 200, 700, True), (64, 70, 1300, False),
-                                          (16, 40, 100, True), (128, 30, 300, True)])
+                                          (16, 40, 100, True), (128, 30, 300, True),
+                                          (48, 50, 900, False), (64, 24, 17000, True),
+                                          (32, 20, 20000, False)])
 def test_fp8_prefill_logits_and_paged_bitwise(H, T, S, clean):
     rng = np.random.default_rng(H + T)
     case = workloads.prefill_case(H * 7 + S, T=T, S=S, H=H, dtype="bf16")

@@ -137,6 +137,29 @@ def test_prefill_varlen_ranges_and_clean_false():
     check_logits(host(out1), ref, bound, "varlen clean=1")
 
 
+@pytest.mark.parametrize("H,clean", [(32, True), (64, False)])
+def test_prefill_long_keys_varlen(H, clean):
+    """S above 16384 (4096-key workgroups in key-chunk-major order) with windows
+    that start and end inside chunks, span several chunks or are empty."""
+    rng = np.random.default_rng(H + 5)
+    T, S = 24, 20000
+    ks = rng.integers(0, S, T).astype(np.int32)
+    ke = np.minimum(S, ks + rng.integers(0, 12000, T)).astype(np.int32)
+    ks[:4] = [0, 4095, 8192, 100]
+    ke[:4] = [S, 4097, 8192, 16390]                                          # row 2 empty
+    case = workloads.prefill_case(H * 11 + 3, T=T, S=S, H=H, ks=ks, ke=ke)
+    poison = torch.full((T, S), float("nan"), device="cuda")
+    out, *_ = _prefill_gpu(case, clean=clean, logits=poison)
+    ref, bound = _prefill_oracle(case)
+    g = host(out)
+    if clean:
+        check_logits(g, ref, bound, f"long-key prefill H={H}")
+    else:
+        vis = np.isfinite(ref)
+        assert np.all(np.isnan(g[~vis])), "clean=0 wrote a masked column"
+        check_logits(np.where(vis, g, -np.inf), ref, bound, f"long-key prefill H={H} clean=0")
+
+
 def test_paged_equals_prefill_bitwise_and_page_order_invariant():
     lens = [500]
     a = workloads.decode_case(30, seq_lens=lens, H=32, next_n=4, spare_pages=5)
