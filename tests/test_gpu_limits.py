@@ -1,6 +1,7 @@
 """GPU parity at the size limits of the ABI: the largest decode batch (65535
-sequences, the grid's y extent) and a cache whose pages lie beyond 2 GiB of
-byte offset (64-bit page addressing in insert, gather and paged logits)."""
+sequences, the grid's y extent) and caches whose pages lie beyond 2 GiB of
+byte offset (64-bit page addressing in insert, gather, paged logits and the
+one-launch step), for the MXFP4 and the FP8 cache."""
 
 import numpy as np
 import pytest
@@ -71,3 +72,44 @@ def test_pages_beyond_2gib_offsets():
     ref, bound = olog.paged_mqa_logits(*oracle_q(case), case["w"], ref_pages, case["block_table"],
                                        case["context_lens"], 2, case["width"], with_bound=True)
     check_logits(host(out), ref, bound, "pages beyond 2 GiB")
+
+
+def test_fp8_pages_beyond_2gib_offsets():
+    # 300,000 FP8 pages of 8448 B = 2.5 GB; the sequences' pages are taken from the top
+    from oracle import fp8 as of8
+    from tests.gpu_helpers import split_new_tokens
+    num_pages = 300_000
+    lens = np.array([200, 130], np.int32)
+    case = workloads.decode_case(78, seq_lens=lens, H=32, next_n=2, spare_pages=0, width=200)
+    pages_used = case["num_pages"]
+    high = num_pages - pages_used
+    case_hi = dict(case)
+    case_hi["block_table"] = (case["block_table"] + high).astype(np.int32)
+    case_hi["slot_mapping"] = case["slot_mapping"] + np.int64(high) * 64
+    pre_slots, k_new, new_slots = split_new_tokens(case_hi, case_hi["block_table"])
+    cache = torch.zeros((num_pages, 64 * 132), dtype=torch.uint8, device="cuda")
+    mx.insert_fp8(dev(case["k"]), dev(pre_slots), cache)
+    bt, ctx = dev(case_hi["block_table"]), dev(case["context_lens"])
+    q, w = dev(case["q"]), dev(case["w"])
+    out1 = mx.logits_paged_insert_fp8(q, dev(k_new), w, cache, bt, ctx, 2, case["width"],
+                                      clean=True)                 # writes the new tokens
+    qv, _, wf = mx.quantize_fp8(q, weights=w)
+    out2 = mx.logits_paged_fp8(qv, wf, cache, bt, ctx, 2, case["width"], clean=True)
+    kv, ksc = mx.gather_fp8(cache, bt, ctx, dev(np.array([0, 200], np.int64)), 200, 330)
+    torch.cuda.synchronize()
+    kc, kscale = of8.quantize_rows(exact(case, "k"))
+    ref_pages = of8.write_rows(np.zeros((pages_used, 64 * 132), np.uint8), kc, kscale,
+                               case["slot_mapping"])
+    assert np.array_equal(host(cache[high:]), ref_pages)
+    assert not torch.any(cache[:high].view(-1)[:: 4099]).item()   # sampled untouched low pages
+    assert np.array_equal(host(kv), kc) and np.array_equal(host(ksc), kscale)
+    H = case["H"]
+    qc, qsc = of8.quantize_rows(exact(case, "q"))
+    wref = of8.fold_weights(case["w"].reshape(-1), qsc).reshape(-1, H)
+    ref, bound = of8.paged_mqa_logits(qc.reshape(-1, H, 128), wref, ref_pages, case["block_table"],
+                                      case["context_lens"], 2, case["width"], with_bound=True)
+    from oracle import tolerance
+    for out, what in ((out1, "one-launch"), (out2, "paged")):
+        check_logits(host(out), ref, bound, f"fp8 pages beyond 2 GiB ({what})",
+                     abs_factor=tolerance.ABS_FACTOR_FP8)
+    assert np.array_equal(host(out1).view(np.uint32), host(out2).view(np.uint32))
